@@ -1,0 +1,26 @@
+"""CPU oracle for the single-GPU MoE layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
+package.  The product path (the HIP library and its Python binding) never
+imports it, and this package imports nothing from the product path.
+
+Modules
+-------
+moe_oracle
+    Plain numpy float64 implementation of each step of the layer (router
+    logits, softmax + top-K selection + renormalised gates, per-expert
+    histogram, capacity, exclusive scan, scatter index, SwiGLU expert FFN,
+    gate-weighted combine), vectorised only where a library primitive (a
+    matmul, a stable sort) is a whole step.
+brute
+    Pure-Python loops over every (token, expert) pair for tiny inputs, written
+    independently of ``moe_oracle``; it pins the oracle.
+
+Parity status of each function is listed in the module docstrings; every
+function is pinned by at least one ``-m "not gpu"`` test (worked example,
+brute force, closed form or invariant).  The published performance figures
+of the pages are the only item with "parity unpinned".
+"""
+
+from . import moe_oracle, brute  # noqa: F401
