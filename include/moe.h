@@ -1,0 +1,165 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer forward library.
+ *
+ * The layer, for tokens X[T,d] and E SwiGLU experts of width n:
+ *   1. router logits  l = X W_r (+ b)              (page "Routing-Free 与 OmniMoE", §1.1)
+ *   2. softmax, top-K, gates renormalised over the K selected experts
+ *                                                   (same page §1.1; "AI芯片如何支持MoE架构" §4.3)
+ *   3-5. expert-major metadata: per-expert histogram, capacity cut in token
+ *        order, exclusive scan, scatter index       (SonicMoE article §11; "算子与编译器：MoE 路由
+ *                                                    与稀疏 Kernel" §3-§4; OmniMoE page §2.3)
+ *   6. grouped GEMM over the gathered token rows with a SwiGLU epilogue -> H
+ *   7. second grouped GEMM -> O                     (SonicMoE article §3, §6.2, §6.3)
+ *   8. gate-weighted combine back to token order -> Y  (SonicMoE article §1, §6.1)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every call returns a moe_status; nothing throws across the ABI.  On
+ *   failure moe_last_error() gives a message for the calling thread.
+ * - Device entry points take device pointers owned by the caller and enqueue
+ *   their kernels on `stream` (a hipStream_t passed as void*; NULL = the
+ *   default stream).  They never synchronise, never copy to the host and
+ *   never allocate: buffers and workspaces are the caller's.  Device faults
+ *   therefore surface at the caller's next synchronisation.
+ * - Argument checks happen on the host before anything is enqueued; a failed
+ *   check enqueues nothing.  A failed kernel launch gives MOE_ERR_HIP.
+ * - Layouts are row-major and contiguous.  X, W_r, W_gate, W_up, W_down, H,
+ *   O and Y have the element type desc->dtype (fp32 or bf16); logits, gates
+ *   and bias are fp32 in both cases; ids, counts, offsets and slots are
+ *   int32 (so T*K must stay below 2^31).  Arithmetic accumulates in fp32;
+ *   H, O and Y are rounded to desc->dtype (round to nearest even).
+ * - Every device pointer must be 16-byte aligned (MOE_ERR_ALIGNMENT).
+ * - Supported shapes: 1 <= E <= 256, 1 <= K <= E, d and n multiples of 64
+ *   (MOE_ERR_UNSUPPORTED otherwise), T >= 0 (T = 0 is a successful no-op).
+ * - Identical inputs give bitwise identical outputs; moe_forward gives the
+ *   same bits as the step-wise chain route -> permute -> grouped_ffn ->
+ *   combine.  Calls sharing a workspace must not overlap in time.
+ * - Inputs must be finite; non-finite values give unspecified routing.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* null pointer, bad count, bad flags, non-finite factor */
+  MOE_ERR_UNSUPPORTED = -2,  /* shape outside the supported set */
+  MOE_ERR_ALIGNMENT = -3,    /* a device pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = -4,    /* workspace missing or smaller than moe_workspace_size */
+  MOE_ERR_HIP = -5           /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Problem description (the pages' problem statement: X[T,d], W_r[d,E], K,
+ * capacity factor, W_gate/W_up[E,d,n], W_down[E,n,d]). */
+typedef struct {
+  int64_t T;                /* tokens */
+  int32_t d;                /* model width */
+  int32_t E;                /* experts */
+  int32_t K;                /* experts per token (run-time value, "AI芯片..." §4.3) */
+  int32_t n;                /* expert FFN width */
+  int32_t dtype;            /* moe_dtype of X, weights, H, O, Y */
+  double capacity_factor;   /* <= 0: no cap (C = T); else C = min(T, ceil(cf*T*K/E))
+                               with cf's exact binary value ("算子与编译器..." §4) */
+  uint32_t flags;           /* 0, or MOE_FLAG_TILE_TABLE_READY */
+} moe_desc;
+
+/* desc->flags bit for moe_grouped_gemm_up / moe_grouped_gemm_down /
+ * moe_grouped_ffn: the workspace already holds the row-tile table that a
+ * previous grouped call on the same stream built from the same offsets, so
+ * the call skips rebuilding it (e.g. a down-projection issued right after its
+ * up-projection).  Other entry points reject the bit. */
+#define MOE_FLAG_TILE_TABLE_READY 1u
+
+/* Workspace selectors for moe_workspace_size. */
+enum { MOE_WS_PERMUTE = 0, MOE_WS_GROUPED_FFN = 1, MOE_WS_FORWARD = 2 };
+
+/* ---------------------------------------------------------------- host only
+ * These make no HIP call and can run on a machine without a GPU. */
+
+/* Checks the description (counts, supported shapes, flags, capacity factor). */
+moe_status moe_validate(const moe_desc* desc);
+
+/* Per-expert cap C (see moe_desc.capacity_factor); exact integer arithmetic. */
+moe_status moe_capacity(const moe_desc* desc, int64_t* C_out);
+
+/* Upper bound on kept (token, expert) assignments: min(T*K, E*C).  H and O
+ * need this many rows. */
+moe_status moe_max_rows(const moe_desc* desc, int64_t* rows_out);
+
+/* Bytes of workspace that the entry point `entry` (MOE_WS_*) needs. */
+moe_status moe_workspace_size(const moe_desc* desc, int32_t entry, size_t* bytes);
+
+/* Static description of a status code. */
+const char* moe_status_str(int32_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ---------------------------------------------------------------- device
+ * Steps 1-2 (router GEMM, softmax, top-K, renormalised gates).
+ *   X[T,d] dtype, W_r[d,E] dtype, bias[E] fp32 or NULL,
+ *   logits[T,E] fp32 or NULL (when given, receives the exact scores the
+ *   selection was made on), topk_ids[T,K] int32, topk_gates[T,K] fp32.
+ * ids[t,:] lists the K largest scores best first; equal scores go to the
+ * lower expert id and -0.0 equals +0.0.  gates[t,:] sum to 1. */
+moe_status moe_route(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
+                     float* logits, int32_t* topk_ids, float* topk_gates, void* stream);
+
+/* Steps 3-5 (histogram, capacity cut in token order, exclusive scan, scatter).
+ *   topk_ids[T,K] int32 with distinct ids in [0,E) per token (as moe_route writes;
+ *   other ids are ignored and marked dropped),
+ *   counts[E] kept per expert, offsets[E+1] exclusive scan of counts,
+ *   raw_counts[E] before the cut or NULL,
+ *   perm_token[T*K]: for slot s < offsets[E], the token of expert-major slot s
+ *   (slots ordered by expert, then ascending token); entries past offsets[E]
+ *   are left untouched,
+ *   inv_slot[T*K]: slot of assignment (t,k), or -1 when the cap dropped it.
+ *   ws: MOE_WS_PERMUTE bytes. */
+moe_status moe_permute(const moe_desc* desc, const int32_t* topk_ids, int32_t* counts,
+                       int32_t* offsets, int32_t* raw_counts, int32_t* perm_token,
+                       int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 6: H[s,:] = silu(X[perm_token[s]] W_gate[e]) * (X[perm_token[s]] W_up[e])
+ * for every slot s of expert e (rows gathered from X inside the GEMM; no
+ * gathered copy of X is made).  offsets/perm_token as moe_permute writes them.
+ *   H has moe_max_rows rows of n; ws: MOE_WS_GROUPED_FFN bytes. */
+moe_status moe_grouped_gemm_up(const moe_desc* desc, const void* X, const int32_t* offsets,
+                               const int32_t* perm_token, const void* W_gate, const void* W_up,
+                               void* H, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 7: O[s,:] = H[s,:] W_down[e] for every slot s of expert e.
+ *   O has moe_max_rows rows of d; ws: MOE_WS_GROUPED_FFN bytes. */
+moe_status moe_grouped_gemm_down(const moe_desc* desc, const void* H, const int32_t* offsets,
+                                 const void* W_down, void* O, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* Steps 6-7 in one call (moe_grouped_gemm_up then moe_grouped_gemm_down). */
+moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* offsets,
+                           const int32_t* perm_token, const void* W_gate, const void* W_up,
+                           const void* W_down, void* H, void* O, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Step 8: Y[t,:] = sum over k with inv_slot[t,k] >= 0, in k order, of
+ * topk_gates[t,k] * O[inv_slot[t,k],:], accumulated in fp32; a token whose
+ * K assignments were all dropped gets a zero row.  No atomics. */
+moe_status moe_combine(const moe_desc* desc, const void* O, const float* topk_gates,
+                       const int32_t* inv_slot, void* Y, void* stream);
+
+/* Steps 1-8 in one call; every intermediate lives in ws (MOE_WS_FORWARD bytes). */
+moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
+                       const void* W_gate, const void* W_up, const void* W_down, void* Y,
+                       void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -267,28 +267,37 @@ def forward(X, W_r, W_gate, W_up, W_down, K: int, capacity_factor=0.0,
 
 
 def token_outputs(tokens, X, ids, gates, inv_slot, W_gate, W_up, W_down) -> np.ndarray:
-    """Y rows for the listed tokens only, one token at a time.
+    """Y rows for the listed tokens only.
 
     Y[t] depends on x_t, its selected experts, its gates and which of its
     entries survived the capacity cut; the cut itself comes from ``inv_slot``
-    (computed over all tokens by ``permute``).  Used for sampled checks at
-    sizes where the full H and O would not fit in host memory.
+    (computed over all tokens by ``permute``).  The listed tokens' kept
+    entries are grouped by expert so that each expert's weights are promoted
+    to float64 once; the sum over k then runs in k order per token.  Used for
+    sampled checks at sizes where the full H and O would not fit in memory.
     """
     ids = np.asarray(ids)
     inv_slot = np.asarray(inv_slot)
     g = _f64(gates)
-    rows = []
-    for t in tokens:
-        x = _f64(X[t])[None, :]
-        y = np.zeros(x.shape[1])
-        for k in range(ids.shape[1]):
-            if inv_slot[t, k] < 0:
-                continue
-            e = int(ids[t, k])
-            _, o = expert_ffn(x, W_gate[e], W_up[e], W_down[e])
-            y += g[t, k] * o[0]
-        rows.append(y)
-    return np.array(rows)
+    tokens = [int(t) for t in tokens]
+    K = ids.shape[1]
+    outs = {}                                   # (row, k) -> expert output
+    by_expert = {}
+    for i, t in enumerate(tokens):
+        for k in range(K):
+            if inv_slot[t, k] >= 0:
+                by_expert.setdefault(int(ids[t, k]), []).append((i, k))
+    for e, entries in by_expert.items():
+        a = _f64(X[[tokens[i] for i, _ in entries]])
+        _, o = expert_ffn(a, W_gate[e], W_up[e], W_down[e])
+        for (i, k), row in zip(entries, o):
+            outs[(i, k)] = row
+    Y = np.zeros((len(tokens), np.asarray(X).shape[1]))
+    for i, t in enumerate(tokens):
+        for k in range(K):
+            if (i, k) in outs:
+                Y[i] += g[t, k] * outs[(i, k)]
+    return Y
 
 
 def slot_outputs(slots, X, offsets, perm_token, W_gate, W_up, W_down):

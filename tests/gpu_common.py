@@ -1,0 +1,71 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare it with the oracle at the tolerances the layer is judged by."""
+
+import numpy as np
+import torch
+
+import top_routing_grouped_amd as moe
+from oracle import moe_oracle as mo
+
+# Output tolerance (relative L2): fp32 inputs vs bf16 inputs with fp32 accumulation.
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+LOGIT_TOL = 1e-5      # both dtypes: bf16 x bf16 products are exact in fp32
+GATE_ATOL = 2e-6
+
+
+def f32np(t):
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def intnp(t):
+    return t.detach().cpu().numpy().astype(np.int64)
+
+
+def device_inputs(inp):
+    out = {}
+    for k in ("X", "W_r", "W_gate", "W_up", "W_down", "bias"):
+        v = inp.get(k)
+        out[k] = None if v is None else v.cuda().contiguous()
+    return out
+
+
+def run_stepwise(dev, K, cf):
+    """route -> permute -> grouped_ffn -> combine through the C ABI."""
+    X, W_gate = dev["X"], dev["W_gate"]
+    T, d = X.shape
+    E, _, n = W_gate.shape
+    dtype = "bf16" if X.dtype == torch.bfloat16 else "fp32"
+    desc = moe.make_desc(T, d, E, K, n, dtype, cf)
+    ids, gates, logits = moe.route(X, dev["W_r"], K, bias=dev["bias"], want_logits=True, n=n)
+    meta = moe.permute(desc, ids)
+    H, O = moe.grouped_ffn(desc, X, meta["offsets"], meta["perm_token"], W_gate, dev["W_up"],
+                           dev["W_down"])
+    Y = moe.combine(desc, O, gates, meta["inv_slot"])
+    res = {"desc": desc, "ids": ids, "gates": gates, "logits": logits, "H": H, "O": O, "Y": Y}
+    res.update(meta)
+    return res
+
+
+def check_routing(res, inp, K):
+    """Logits within tolerance of the fp64 definition; ids and gates from the
+    device's own fp32 logits (same decision inputs on both sides)."""
+    L_gpu = f32np(res["logits"]).astype(np.float64)
+    L_ref = mo.router_logits(f32np(inp["X"]), f32np(inp["W_r"]),
+                             None if inp.get("bias") is None else f32np(inp["bias"]))
+    assert mo.rel_l2(L_gpu, L_ref) <= LOGIT_TOL
+    ids_ref = mo.topk_select(L_gpu, K)
+    ids_gpu = intnp(res["ids"])
+    assert np.array_equal(ids_gpu, ids_ref), "top-K ids differ"
+    g_ref = mo.topk_gates(L_gpu, ids_ref)
+    g_gpu = f32np(res["gates"]).astype(np.float64)
+    assert np.max(np.abs(g_gpu - g_ref)) <= GATE_ATOL
+    return L_gpu, ids_ref, g_ref
+
+
+def check_permutation(res, ids, E, C):
+    ref = mo.permute(ids, E, C)
+    for key in ("raw_counts", "counts", "offsets", "inv_slot"):
+        assert np.array_equal(intnp(res[key]), ref[key].astype(np.int64)), key
+    N = int(ref["offsets"][-1])
+    assert np.array_equal(intnp(res["perm_token"])[:N], ref["perm_token"][:N].astype(np.int64))
+    return ref

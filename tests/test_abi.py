@@ -1,0 +1,125 @@
+"""The C-ABI library on the host: it loads, exports every symbol that
+include/moe.h declares, and its host-only logic (validation, capacity,
+workspace sizes, argument errors) behaves as documented.  No compute call is
+made: every device entry point below fails validation (or is a T = 0 no-op)
+before anything is enqueued, so these run without a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_routing_grouped_amd as moe
+from oracle import moe_oracle as mo
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 13
+    lib = moe.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = moe.lib()
+    assert lib.moe_status_str(0) == b"MOE_OK"
+    assert lib.moe_status_str(-4) == b"MOE_ERR_WORKSPACE"
+    assert lib.moe_status_str(7) == b"unknown moe_status"
+
+
+def test_validate_cases():
+    ok = moe.make_desc(16, 128, 8, 2, 256, "bf16")
+    assert moe.moe_validate(ok) == moe.MOE_OK
+    bad = [
+        (moe.make_desc(16, 128, 8, 9, 256), moe.MOE_ERR_INVALID_ARG),          # K > E
+        (moe.make_desc(16, 128, 8, 0, 256), moe.MOE_ERR_INVALID_ARG),          # K = 0
+        (moe.make_desc(-1, 128, 8, 2, 256), moe.MOE_ERR_INVALID_ARG),          # T < 0
+        (moe.make_desc(16, 128, 0, 1, 256), moe.MOE_ERR_INVALID_ARG),          # E = 0
+        (moe.make_desc(16, 128, 300, 2, 256), moe.MOE_ERR_UNSUPPORTED),        # E > 256
+        (moe.make_desc(16, 100, 8, 2, 256), moe.MOE_ERR_UNSUPPORTED),          # d % 64
+        (moe.make_desc(16, 128, 8, 2, 96), moe.MOE_ERR_UNSUPPORTED),           # n % 64
+        (moe.make_desc(16, 128, 8, 2, 256, flags=1), moe.MOE_ERR_INVALID_ARG),  # flag not allowed here
+        (moe.make_desc(16, 128, 8, 2, 256, flags=2), moe.MOE_ERR_INVALID_ARG),  # unknown flag
+        (moe.make_desc(16, 128, 8, 2, 256, capacity_factor=float("nan")), moe.MOE_ERR_INVALID_ARG),
+        (moe.make_desc(16, 128, 8, 2, 256, capacity_factor=float("inf")), moe.MOE_ERR_INVALID_ARG),
+        (moe.make_desc(2 ** 30, 128, 8, 2, 256), moe.MOE_ERR_UNSUPPORTED),     # T*K >= 2^31
+    ]
+    for desc, want in bad:
+        assert moe.moe_validate(desc) == want
+    d = moe.make_desc(16, 128, 8, 2, 256)
+    d.dtype = 7
+    assert moe.moe_validate(d) == moe.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("T,K,E,cf", [
+    (8192, 4, 64, 1.25), (100, 2, 4, 0.0), (100, 2, 4, -1.0), (100, 2, 4, 1e-9),
+    (100, 2, 4, 1e9), (10, 1, 1, 0.25), (10, 1, 1, 0.5), (10, 1, 1, 0.1), (0, 2, 4, 1.0),
+    (16384, 8, 128, 1.0), (12345, 3, 7, 0.3), (777, 5, 200, 2.5), (1, 1, 1, 1e-300),
+    (1000, 8, 256, 3.0 / 7.0), (4096, 2, 8, 1e300),
+])
+def test_capacity_matches_oracle(T, K, E, cf):
+    desc = moe.make_desc(T, 128, E, K, 128, "bf16", cf)
+    assert moe.moe_capacity(desc) == mo.capacity(T, K, E, cf)
+    C = mo.capacity(T, K, E, cf)
+    assert moe.moe_max_rows(desc) == min(T * K, E * C)
+
+
+def test_workspace_sizes_grow_with_problem():
+    small = moe.make_desc(64, 128, 8, 2, 128)
+    big = moe.make_desc(16384, 2048, 128, 8, 768)
+    for entry in (moe.MOE_WS_PERMUTE, moe.MOE_WS_GROUPED_FFN, moe.MOE_WS_FORWARD):
+        a = moe.moe_workspace_size(small, entry)
+        b = moe.moe_workspace_size(big, entry)
+        assert 0 < a < b
+    # forward workspace holds H and O for every kept row
+    rows = moe.moe_max_rows(big)
+    assert moe.moe_workspace_size(big, moe.MOE_WS_FORWARD) >= rows * (768 + 2048) * 2
+    with pytest.raises(moe.MoeError):
+        moe.moe_workspace_size(small, 9)
+
+
+def _raw(name):
+    return getattr(moe.lib(), name)
+
+
+def test_device_entry_points_reject_bad_arguments_without_enqueueing():
+    lib = moe.lib()
+    desc = moe.make_desc(64, 128, 8, 2, 128)
+    p = ctypes.byref(desc)
+    A = ctypes.c_void_p(1 << 20)          # aligned fake pointers: never dereferenced
+    U = ctypes.c_void_p((1 << 20) + 4)    # misaligned
+    # null required pointer
+    assert lib.moe_route(p, None, A, None, None, A, A, None) == moe.MOE_ERR_INVALID_ARG
+    assert b"X is NULL" in lib.moe_last_error()
+    # misaligned pointer
+    assert lib.moe_route(p, U, A, None, None, A, A, None) == moe.MOE_ERR_ALIGNMENT
+    assert lib.moe_combine(p, A, A, A, U, None) == moe.MOE_ERR_ALIGNMENT
+    # missing / short workspace
+    assert lib.moe_permute(p, A, A, A, None, A, A, None, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_forward(p, A, A, None, A, A, A, A, A, 16, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_grouped_ffn(p, A, A, A, A, A, A, A, A, A, 0, None) == moe.MOE_ERR_WORKSPACE
+    # invalid description
+    bad = moe.make_desc(64, 128, 8, 9, 128)
+    assert lib.moe_forward(ctypes.byref(bad), A, A, None, A, A, A, A, A, 1 << 30, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    # T = 0 is a successful no-op (no launch)
+    zero = moe.make_desc(0, 128, 8, 2, 128)
+    ws = moe.moe_workspace_size(zero, moe.MOE_WS_FORWARD)
+    assert lib.moe_forward(ctypes.byref(zero), A, A, None, A, A, A, A, A, ws + 256, None) == moe.MOE_OK
+    assert lib.moe_route(ctypes.byref(zero), A, A, None, None, A, A, None) == moe.MOE_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", "/nonexistent/libmoe_mi355x.so")
+    with pytest.raises(RuntimeError, match="no non-HIP fallback"):
+        moe.lib()

@@ -1,0 +1,193 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer results (ids, counts, offsets, permutation) must match bit for bit,
+with the oracle routing on the device's own fp32 logits; floating outputs
+must meet the relative-L2 tolerance (1e-5 fp32, 2e-2 bf16); gates within
+2e-6.  Small shapes compare every element and are chosen to span several
+tiles with ragged tails (token tiles of 64 and 256, row tiles of 128, column
+tiles of 128/256, partial last column tiles); the full workloads compare
+every routing/permutation entry and a sample of output rows.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import top_routing_grouped_amd as moe
+from oracle import moe_oracle as mo
+from gpu_common import (TOL, check_permutation, check_routing, device_inputs, f32np, intnp,
+                        run_stepwise)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _full_check(inp, K, cf, dtype):
+    dev = device_inputs(inp)
+    res = run_stepwise(dev, K, cf)
+    torch.cuda.synchronize()
+    T, E = inp["X"].shape[0], inp["W_r"].shape[1]
+    L_gpu, ids, gates = check_routing(res, inp, K)
+    C = mo.capacity(T, K, E, cf)
+    ref = check_permutation(res, ids, E, C)
+    N = int(ref["offsets"][-1])
+    X32 = f32np(inp["X"])
+    Wg, Wu, Wd = f32np(inp["W_gate"]), f32np(inp["W_up"]), f32np(inp["W_down"])
+    H_ref, O_ref = mo.grouped_ffn(X32, ref["offsets"], ref["perm_token"], Wg, Wu, Wd)
+    tol = TOL[dtype]
+    if N:
+        assert mo.rel_l2(f32np(res["H"])[:N], H_ref) <= tol
+        assert mo.rel_l2(f32np(res["O"])[:N], O_ref) <= tol
+    Y_ref = mo.combine(O_ref, gates, ref["inv_slot"], d=X32.shape[1])
+    Y_gpu = f32np(res["Y"])
+    assert mo.rel_l2(Y_gpu, Y_ref) <= tol
+    dropped = np.all(ref["inv_slot"] < 0, axis=1)
+    assert np.all(Y_gpu[dropped] == 0.0)
+    # the fused entry point gives the same bits as the step-wise chain
+    Y_fused = moe.forward(dev["X"], dev["W_r"], dev["W_gate"], dev["W_up"], dev["W_down"], K, cf,
+                          bias=dev["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(Y_fused, res["Y"])
+    return res, ref
+
+
+SMALL = [
+    # T,    d,   E,  K,   n,  dtype, cf,   bias
+    (1000, 320, 4, 2, 192, "bf16", 0.0, None),       # partial last column tile in both GEMMs
+    (777, 256, 16, 4, 256, "bf16", 1.0, "zipf"),     # capacity drops under a skewed router
+    (513, 128, 3, 3, 128, "bf16", 0.0, None),        # K = E, E not a multiple of 8
+    (130, 128, 256, 8, 128, "bf16", 0.0, None),      # E = 256
+    (200, 192, 1, 1, 64, "bf16", 0.0, None),         # single expert
+    (300, 128, 64, 6, 256, "bf16", 0.3, "zipf"),     # heavy drops, fully dropped tokens
+    (70, 64, 40, 20, 64, "bf16", 0.0, None),         # K above 16
+    (1, 128, 8, 2, 128, "bf16", 0.0, None),          # one token
+    (256, 128, 8, 2, 256, "fp32", 0.0, None),        # the tiny fp32 layer's shape, other seed
+    (100, 64, 5, 3, 64, "fp32", 0.5, "zipf"),
+]
+
+
+@pytest.mark.parametrize("T,d,E,K,n,dtype,cf,bias", SMALL)
+def test_small_layer_parity(T, d, E, K, n, dtype, cf, bias):
+    print(f"case T={T} d={d} E={E} K={K} n={n} {dtype} cf={cf} bias={bias}", flush=True)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    inp = mi.draw(T, d, E, n, tdt, seed=7, bias=bias)
+    _full_check(inp, K, cf, dtype)
+
+
+def test_zero_router_gives_lowest_ids_and_uniform_gates():
+    inp = mi.draw(300, 128, 16, 128, torch.bfloat16, seed=1)
+    inp["W_r"] = torch.zeros_like(inp["W_r"])
+    res, _ = _full_check(inp, 5, 0.0, "bf16")
+    assert np.all(intnp(res["ids"]) == np.arange(5)[None, :])
+    assert np.all(f32np(res["gates"]) == np.float32(0.2))
+
+
+def test_duplicated_router_columns_tie_to_lower_id():
+    inp = mi.draw(400, 256, 12, 128, torch.bfloat16, seed=2)
+    inp["W_r"][:, 9] = inp["W_r"][:, 2]
+    res, _ = _full_check(inp, 12, 0.0, "bf16")
+    L = f32np(res["logits"])
+    assert np.array_equal(L[:, 2], L[:, 9])
+    ids = intnp(res["ids"])
+    pos2 = np.argmax(ids == 2, axis=1)
+    pos9 = np.argmax(ids == 9, axis=1)
+    assert np.all(pos2 + 1 == pos9)
+
+
+def test_quantised_logits_with_many_exact_ties():
+    g = torch.Generator().manual_seed(3)
+    T, d, E, n = 600, 128, 32, 128
+    inp = mi.draw(T, d, E, n, torch.bfloat16, seed=3)
+    inp["X"] = torch.randint(-1, 2, (T, d), generator=g).to(torch.bfloat16)
+    inp["W_r"] = (torch.randint(-1, 2, (d, E), generator=g).float() / 8).to(torch.bfloat16)
+    res, _ = _full_check(inp, 4, 0.0, "bf16")
+    L = f32np(res["logits"])
+    ties = sum(len(np.unique(row)) < E for row in L)
+    assert ties > T // 2
+
+
+def test_capacity_one_keeps_each_experts_first_token():
+    inp = mi.draw(257, 128, 8, 128, torch.bfloat16, seed=4)
+    cf = 1e-6                                    # C = 1
+    assert mo.capacity(257, 2, 8, cf) == 1
+    _, ref = _full_check(inp, 2, cf, "bf16")
+    assert np.all(ref["counts"] <= 1)
+
+
+@pytest.mark.parametrize("case,cf", [("uncapped", 0.0), ("capped", 1.0)])
+def test_worked_example_on_device(case, cf):
+    with open(os.path.join(GOLDEN, "worked_example_permute.json")) as f:
+        ex = json.load(f)
+    want = ex[case]
+    desc = moe.make_desc(3, 64, ex["E"], 3, 64, "bf16", cf)
+    assert moe.moe_capacity(desc) == want["C"]
+    ids = torch.tensor(ex["ids"], dtype=torch.int32, device="cuda")
+    got = moe.permute(desc, ids)
+    torch.cuda.synchronize()
+    for key in ("raw_counts", "counts", "offsets", "inv_slot"):
+        assert intnp(got[key]).tolist() == want[key], key
+    N = want["offsets"][-1]
+    assert intnp(got["perm_token"])[:N].tolist() == want["perm_token"]
+
+
+def test_repeat_runs_are_bitwise_identical():
+    inp = mi.draw(2000, 256, 32, 256, torch.bfloat16, seed=5)
+    dev = device_inputs(inp)
+    ys = [moe.forward(dev["X"], dev["W_r"], dev["W_gate"], dev["W_up"], dev["W_down"], 4, 1.0)
+          for _ in range(3)]
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+
+
+def test_zero_tokens_is_a_no_op():
+    X = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    W_r = torch.zeros((128, 8), dtype=torch.bfloat16, device="cuda")
+    Wg = torch.zeros((8, 128, 128), dtype=torch.bfloat16, device="cuda")
+    Y = moe.forward(X, W_r, Wg, Wg, Wg.transpose(1, 2).contiguous(), 2)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 128)
+
+
+# ---------------------------------------------------------------- full workloads
+
+def _sampled_full_check(name, n_sample=48):
+    inp = mi.make_inputs(name)
+    w = inp["workload"]
+    print(f"workload {name}: T={w.T} d={w.d} E={w.E} K={w.K} n={w.n}", flush=True)
+    dev = device_inputs(inp)
+    res = run_stepwise(dev, w.K, w.capacity_factor)
+    Y_fused = moe.forward(dev["X"], dev["W_r"], dev["W_gate"], dev["W_up"], dev["W_down"], w.K,
+                          w.capacity_factor, bias=dev["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(Y_fused, res["Y"])
+    L_gpu, ids, gates = check_routing(res, inp, w.K)
+    C = mo.capacity(w.T, w.K, w.E, w.capacity_factor)
+    ref = check_permutation(res, ids, w.E, C)
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(w.T, size=min(w.T, n_sample), replace=False))
+    X32 = f32np(inp["X"])
+    Wg, Wu, Wd = (inp[k].float().numpy() for k in ("W_gate", "W_up", "W_down"))
+    y_ref = mo.token_outputs(toks, X32, ids, gates, ref["inv_slot"], Wg, Wu, Wd)
+    y_gpu = f32np(res["Y"])[toks]
+    assert mo.rel_l2(y_gpu, y_ref) <= TOL[w.dtype]
+    N = int(ref["offsets"][-1])
+    if N:
+        slots = np.sort(rng.choice(N, size=min(N, 16), replace=False))
+        h_ref, o_ref = mo.slot_outputs(slots, X32, ref["offsets"], ref["perm_token"], Wg, Wu, Wd)
+        assert mo.rel_l2(f32np(res["H"])[slots], h_ref) <= TOL[w.dtype]
+        assert mo.rel_l2(f32np(res["O"])[slots], o_ref) <= TOL[w.dtype]
+    return res, ref
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "qwen3_bf16", "skewed_cap_bf16", "mixtral_bf16",
+                                  "granular_bf16", "granular_decode_bf16"])
+def test_workload_full_size(name):
+    res, ref = _sampled_full_check(name)
+    if name == "skewed_cap_bf16":
+        assert int(ref["offsets"][-1]) < 8192 * 4          # the cap drops assignments
+        assert int(np.max(ref["counts"])) == 640

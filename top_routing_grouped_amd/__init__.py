@@ -1,0 +1,269 @@
+"""MI355X (gfx950) MoE layer forward: Python binding over the C ABI of include/moe.h.
+
+Argument marshalling only.  Every step of the layer runs in the HIP kernels of
+``libmoe_mi355x.so``; PyTorch supplies device memory and the stream.  If the
+library has not been built, every call raises (there is no fallback path).
+
+Low-level functions carry the C names (``moe_route``, ``moe_permute``,
+``moe_grouped_gemm_up``, ``moe_grouped_gemm_down``, ``moe_grouped_ffn``,
+``moe_combine``, ``moe_forward`` and the host-only queries) and take torch
+tensors.  ``route``, ``permute``, ``grouped_ffn``, ``combine`` and
+``forward`` allocate the outputs with torch and call them.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_NAME = "libmoe_mi355x.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_ALIGNMENT = -3
+MOE_ERR_WORKSPACE = -4
+MOE_ERR_HIP = -5
+MOE_F32 = 0
+MOE_BF16 = 1
+MOE_WS_PERMUTE = 0
+MOE_WS_GROUPED_FFN = 1
+MOE_WS_FORWARD = 2
+MOE_FLAG_TILE_TABLE_READY = 1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+class MoeDesc(ctypes.Structure):
+    """Mirror of ``moe_desc`` (same field order, natural alignment)."""
+
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("d", ctypes.c_int32),
+        ("E", ctypes.c_int32),
+        ("K", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_double),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+def make_desc(T, d, E, K, n, dtype="bf16", capacity_factor=0.0, flags=0) -> MoeDesc:
+    code = {"bf16": MOE_BF16, "fp32": MOE_F32, MOE_BF16: MOE_BF16, MOE_F32: MOE_F32}[dtype]
+    return MoeDesc(int(T), int(d), int(E), int(K), int(n), code, float(capacity_factor), int(flags))
+
+
+_lib = None
+_VP = ctypes.c_void_p
+_DP = ctypes.POINTER(MoeDesc)
+_SIGNATURES = {
+    "moe_validate": [_DP],
+    "moe_capacity": [_DP, ctypes.POINTER(ctypes.c_int64)],
+    "moe_max_rows": [_DP, ctypes.POINTER(ctypes.c_int64)],
+    "moe_workspace_size": [_DP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
+    "moe_route": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "moe_permute": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "moe_grouped_gemm_up": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "moe_grouped_gemm_down": [_DP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "moe_grouped_ffn": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "moe_combine": [_DP, _VP, _VP, _VP, _VP, _VP],
+    "moe_forward": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m top_routing_grouped_amd.build` "
+                "(there is no non-HIP fallback)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int32
+        handle.moe_status_str.argtypes = [ctypes.c_int32]
+        handle.moe_status_str.restype = ctypes.c_char_p
+        handle.moe_last_error.argtypes = []
+        handle.moe_last_error.restype = ctypes.c_char_p
+        _lib = handle
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        L = lib()
+        detail = (L.moe_last_error() or b"").decode() or L.moe_status_str(status).decode()
+        raise MoeError(status, where, detail)
+
+
+def _p(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+# ---------------------------------------------------------------- host-only queries
+
+def moe_validate(desc: MoeDesc) -> int:
+    return lib().moe_validate(ctypes.byref(desc))
+
+
+def moe_capacity(desc: MoeDesc) -> int:
+    out = ctypes.c_int64(0)
+    _check(lib().moe_capacity(ctypes.byref(desc), ctypes.byref(out)), "moe_capacity")
+    return out.value
+
+
+def moe_max_rows(desc: MoeDesc) -> int:
+    out = ctypes.c_int64(0)
+    _check(lib().moe_max_rows(ctypes.byref(desc), ctypes.byref(out)), "moe_max_rows")
+    return out.value
+
+
+def moe_workspace_size(desc: MoeDesc, entry: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_size(ctypes.byref(desc), int(entry), ctypes.byref(out)),
+           "moe_workspace_size")
+    return out.value
+
+
+# ---------------------------------------------------------------- device entry points
+
+def moe_route(desc, X, W_r, bias, logits, ids, gates, stream=None):
+    _check(lib().moe_route(ctypes.byref(desc), _p(X), _p(W_r), _p(bias), _p(logits), _p(ids),
+                           _p(gates), _stream(stream)), "moe_route")
+
+
+def moe_permute(desc, ids, counts, offsets, raw_counts, perm_token, inv_slot, ws, stream=None):
+    _check(lib().moe_permute(ctypes.byref(desc), _p(ids), _p(counts), _p(offsets), _p(raw_counts),
+                             _p(perm_token), _p(inv_slot), _p(ws), ws.numel() * ws.element_size(),
+                             _stream(stream)), "moe_permute")
+
+
+def moe_grouped_gemm_up(desc, X, offsets, perm_token, W_gate, W_up, H, ws, stream=None):
+    _check(lib().moe_grouped_gemm_up(ctypes.byref(desc), _p(X), _p(offsets), _p(perm_token),
+                                     _p(W_gate), _p(W_up), _p(H), _p(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_grouped_gemm_up")
+
+
+def moe_grouped_gemm_down(desc, H, offsets, W_down, O, ws, stream=None):
+    _check(lib().moe_grouped_gemm_down(ctypes.byref(desc), _p(H), _p(offsets), _p(W_down), _p(O),
+                                       _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_grouped_gemm_down")
+
+
+def moe_grouped_ffn(desc, X, offsets, perm_token, W_gate, W_up, W_down, H, O, ws, stream=None):
+    _check(lib().moe_grouped_ffn(ctypes.byref(desc), _p(X), _p(offsets), _p(perm_token),
+                                 _p(W_gate), _p(W_up), _p(W_down), _p(H), _p(O), _p(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_grouped_ffn")
+
+
+def moe_combine(desc, O, gates, inv_slot, Y, stream=None):
+    _check(lib().moe_combine(ctypes.byref(desc), _p(O), _p(gates), _p(inv_slot), _p(Y),
+                             _stream(stream)), "moe_combine")
+
+
+def moe_forward(desc, X, W_r, bias, W_gate, W_up, W_down, Y, ws, stream=None):
+    _check(lib().moe_forward(ctypes.byref(desc), _p(X), _p(W_r), _p(bias), _p(W_gate), _p(W_up),
+                             _p(W_down), _p(Y), _p(ws), ws.numel() * ws.element_size(),
+                             _stream(stream)), "moe_forward")
+
+
+# ---------------------------------------------------------------- allocating helpers
+
+def _desc_for(X, W_gate, K, capacity_factor):
+    import torch
+    T, d = X.shape
+    E, _, n = W_gate.shape
+    dtype = "bf16" if X.dtype == torch.bfloat16 else "fp32"
+    return make_desc(T, d, E, K, n, dtype, capacity_factor)
+
+
+def workspace(desc: MoeDesc, entry: int, device="cuda"):
+    import torch
+    nbytes = max(16, moe_workspace_size(desc, entry))
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def route(X, W_r, K, bias=None, want_logits=False, n=64):
+    """Steps 1-2.  Returns (ids [T,K] int32, gates [T,K] fp32, logits [T,E] fp32 or None)."""
+    import torch
+    T, d = X.shape
+    E = W_r.shape[1]
+    desc = make_desc(T, d, E, K, n, "bf16" if X.dtype == torch.bfloat16 else "fp32")
+    ids = torch.empty((T, K), dtype=torch.int32, device=X.device)
+    gates = torch.empty((T, K), dtype=torch.float32, device=X.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=X.device) if want_logits else None
+    moe_route(desc, X, W_r, bias, logits, ids, gates)
+    return ids, gates, logits
+
+
+def permute(desc: MoeDesc, ids):
+    """Steps 3-5.  Returns dict(counts, offsets, raw_counts, perm_token, inv_slot)."""
+    import torch
+    dev = ids.device
+    T, K, E = desc.T, desc.K, desc.E
+    out = {
+        "counts": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "raw_counts": torch.empty(E, dtype=torch.int32, device=dev),
+        "perm_token": torch.full((max(1, T * K),), -1, dtype=torch.int32, device=dev),
+        "inv_slot": torch.empty((T, K), dtype=torch.int32, device=dev),
+    }
+    ws = workspace(desc, MOE_WS_PERMUTE, dev)
+    moe_permute(desc, ids, out["counts"], out["offsets"], out["raw_counts"], out["perm_token"],
+                out["inv_slot"], ws)
+    return out
+
+
+def grouped_ffn(desc: MoeDesc, X, offsets, perm_token, W_gate, W_up, W_down):
+    """Steps 6-7.  Returns (H [rows_max, n], O [rows_max, d]); rows >= offsets[E] are unspecified."""
+    import torch
+    rows = max(1, moe_max_rows(desc))
+    H = torch.empty((rows, desc.n), dtype=X.dtype, device=X.device)
+    O = torch.empty((rows, desc.d), dtype=X.dtype, device=X.device)
+    ws = workspace(desc, MOE_WS_GROUPED_FFN, X.device)
+    moe_grouped_ffn(desc, X, offsets, perm_token, W_gate, W_up, W_down, H, O, ws)
+    return H, O
+
+
+def combine(desc: MoeDesc, O, gates, inv_slot):
+    """Step 8.  Returns Y [T, d]."""
+    import torch
+    Y = torch.empty((desc.T, desc.d), dtype=O.dtype, device=O.device)
+    moe_combine(desc, O, gates, inv_slot, Y)
+    return Y
+
+
+def forward(X, W_r, W_gate, W_up, W_down, K, capacity_factor=0.0, bias=None, ws=None):
+    """Steps 1-8 in one library call.  Returns Y [T, d]."""
+    import torch
+    desc = _desc_for(X, W_gate, K, capacity_factor)
+    if ws is None:
+        ws = workspace(desc, MOE_WS_FORWARD, X.device)
+    Y = torch.empty_like(X)
+    moe_forward(desc, X, W_r, bias, W_gate, W_up, W_down, Y, ws)
+    return Y

@@ -1,0 +1,105 @@
+// Step 8 of the layer: gate-weighted combine back to token order.
+//
+// Y[t] = sum over k = 0..K-1 with inv_slot[t,k] >= 0 of gates[t,k] * O[inv_slot[t,k]]
+// (SonicMoE article §1 for the weighted sum, §6.1 for doing the scatter and
+// the sum in one aggregation kernel).  One wave owns one token: it reads the
+// token's K expert rows of O with 16-byte loads (the K loads of a chunk are
+// independent, so they are all in flight together), accumulates in fp32 in k
+// order and writes the row once.  Every output row has exactly one writer,
+// so no atomics are needed and the result is deterministic.
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+using f32x4 = float __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kTokPerBlock = kThreads / 64;
+
+// bf16: 8 elements per 16-byte chunk; KU = k unroll (loads in flight per chunk).
+template <int KU>
+__global__ __launch_bounds__(kThreads) void combine_bf16(const uint16_t* __restrict__ O,
+                                                        const float* __restrict__ gates,
+                                                        const int32_t* __restrict__ inv,
+                                                        uint16_t* __restrict__ Y, int64_t T, int d,
+                                                        int K) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int nchunk = d / 8;
+  const int32_t* tinv = inv + t * K;
+  const float* tg = gates + t * K;
+  for (int c = lane; c < nchunk; c += 64) {
+    float acc[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[v] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += KU) {
+      u32x4 o[KU];
+      float gk[KU];
+      bool ok[KU];
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int k = k0 + u;
+        const int s = (k < K) ? tinv[k] : -1;
+        ok[u] = s >= 0;
+        gk[u] = ok[u] ? tg[k] : 0.f;
+        o[u] = ok[u] ? *reinterpret_cast<const u32x4*>(O + (int64_t)s * d + c * 8)
+                     : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        if (!ok[u]) continue;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc[2 * h] = fmaf(gk[u], dev::bf16_bits_to_f32(o[u][h] & 0xFFFFu), acc[2 * h]);
+          acc[2 * h + 1] = fmaf(gk[u], dev::bf16_bits_to_f32(o[u][h] >> 16), acc[2 * h + 1]);
+        }
+      }
+    }
+    u32x4 out;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) out[h] = dev::pack_bf16x2(acc[2 * h], acc[2 * h + 1]);
+    *reinterpret_cast<u32x4*>(Y + t * (int64_t)d + c * 8) = out;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void combine_f32(const float* __restrict__ O,
+                                                       const float* __restrict__ gates,
+                                                       const int32_t* __restrict__ inv,
+                                                       float* __restrict__ Y, int64_t T, int d,
+                                                       int K) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int nchunk = d / 4;
+  for (int c = lane; c < nchunk; c += 64) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < K; ++k) {
+      const int s = inv[t * K + k];
+      if (s < 0) continue;
+      const float g = gates[t * K + k];
+      const f32x4 o = *reinterpret_cast<const f32x4*>(O + (int64_t)s * d + c * 4);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = fmaf(g, o[v], acc[v]);
+    }
+    *reinterpret_cast<f32x4*>(Y + t * (int64_t)d + c * 4) = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Problem& p, const void* O, const float* gates,
+                          const int32_t* inv_slot, void* Y, hipStream_t s) {
+  const dim3 grid((unsigned)((p.T + kTokPerBlock - 1) / kTokPerBlock));
+  if (p.bf16)
+    hipLaunchKernelGGL(combine_bf16<4>, grid, dim3(kThreads), 0, s, (const uint16_t*)O, gates,
+                       inv_slot, (uint16_t*)Y, p.T, p.d, p.K);
+  else
+    hipLaunchKernelGGL(combine_f32, grid, dim3(kThreads), 0, s, (const float*)O, gates, inv_slot,
+                       (float*)Y, p.T, p.d, p.K);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,348 @@
+// C ABI of the MI355X MoE layer library (declared in include/moe.h).
+//
+// Host side only: argument checks, the capacity rule, workspace carving and
+// the launch order.  Every entry point enqueues on the caller's stream and
+// returns without synchronising; nothing here allocates device memory.
+#include "moe.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "moe_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Exact C = min(T, ceil(cf * T * K / E)) for cf > 0, with cf taken as the
+// exact binary value of the double: cf = m * 2^ex, m a 53-bit integer.
+int64_t exact_capacity(int64_t T, int64_t K, int64_t E, double cf) {
+  if (!(cf > 0.0)) return T;
+  if (T == 0) return 0;
+  int ex = 0;
+  const double f = std::frexp(cf, &ex);            // cf = f * 2^ex, f in [0.5, 1)
+  const int64_t m = (int64_t)std::ldexp(f, 53);    // exact
+  ex -= 53;                                        // cf = m * 2^ex
+  if (ex >= 0) return T;                           // cf >= 2^52: above any cap
+  if (-ex > 100) return 1;                         // 0 < cf*T*K/E < 1
+  const __int128 num = (__int128)m * T * K;
+  const __int128 den = (__int128)E << (-ex);
+  const __int128 c = (num + den - 1) / den;
+  return c < (__int128)T ? (int64_t)c : T;
+}
+
+moe_status check_desc(const moe_desc* d, uint32_t allowed_flags = 0) {
+  if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is NULL");
+  if (d->flags & ~allowed_flags) return fail(MOE_ERR_INVALID_ARG, "desc->flags has a bit this entry point does not accept");
+  if (d->T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0");
+  if (d->E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1");
+  if (d->K < 1 || d->K > d->E) return fail(MOE_ERR_INVALID_ARG, "K must satisfy 1 <= K <= E");
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_F32 or MOE_BF16");
+  if (!std::isfinite(d->capacity_factor))
+    return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite");
+  if (d->E > 256) return fail(MOE_ERR_UNSUPPORTED, "E above 256 is not supported");
+  if (d->d < 64 || d->d % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "d must be a positive multiple of 64");
+  if (d->n < 64 || d->n % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "n must be a positive multiple of 64");
+  if (d->T * (int64_t)d->K >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T*K must stay below 2^31 (int32 slots)");
+  return MOE_OK;
+}
+
+moe::Problem make_problem(const moe_desc* d) {
+  moe::Problem p;
+  p.T = d->T;
+  p.d = d->d;
+  p.E = d->E;
+  p.K = d->K;
+  p.n = d->n;
+  p.bf16 = d->dtype == MOE_BF16;
+  p.C = exact_capacity(d->T, d->K, d->E, d->capacity_factor);
+  const int64_t tk = d->T * (int64_t)d->K;
+  const int64_t ec = (int64_t)d->E * p.C;
+  p.rows_max = tk < ec ? tk : ec;
+  return p;
+}
+
+size_t elem(const moe::Problem& p) { return p.bf16 ? 2 : 4; }
+
+struct PermuteWs {
+  int32_t* blockcnt;
+  int32_t* blockbase;
+  int32_t* raw;
+};
+size_t permute_ws_bytes(const moe::Problem& p) {
+  const size_t nbe = (size_t)moe::permute_blocks(p.T) * p.E * sizeof(int32_t);
+  return align_up(nbe) * 2 + align_up((size_t)p.E * sizeof(int32_t));
+}
+PermuteWs carve_permute(const moe::Problem& p, unsigned char* base) {
+  const size_t nbe = align_up((size_t)moe::permute_blocks(p.T) * p.E * sizeof(int32_t));
+  return {reinterpret_cast<int32_t*>(base), reinterpret_cast<int32_t*>(base + nbe),
+          reinterpret_cast<int32_t*>(base + 2 * nbe)};
+}
+
+struct ForwardWs {
+  int32_t* ids;
+  float* gates;
+  int32_t* inv;
+  int32_t* perm;
+  int32_t* counts;
+  int32_t* offsets;
+  unsigned char* permute;
+  int32_t* table;
+  void* H;
+  void* O;
+  size_t bytes;
+};
+ForwardWs carve_forward(const moe::Problem& p, unsigned char* base) {
+  ForwardWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    unsigned char* ptr = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return ptr;
+  };
+  const size_t tk = (size_t)p.T * p.K;
+  w.ids = reinterpret_cast<int32_t*>(take(tk * 4));
+  w.gates = reinterpret_cast<float*>(take(tk * 4));
+  w.inv = reinterpret_cast<int32_t*>(take(tk * 4));
+  w.perm = reinterpret_cast<int32_t*>(take(tk * 4));
+  w.counts = reinterpret_cast<int32_t*>(take((size_t)p.E * 4));
+  w.offsets = reinterpret_cast<int32_t*>(take((size_t)(p.E + 1) * 4));
+  w.permute = take(permute_ws_bytes(p));
+  w.table = reinterpret_cast<int32_t*>(take(moe::tile_table_bytes(p)));
+  w.H = take((size_t)p.rows_max * p.n * elem(p));
+  w.O = take((size_t)p.rows_max * p.d * elem(p));
+  w.bytes = off;
+  return w;
+}
+
+bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
+
+moe_status check_ptrs(std::initializer_list<std::pair<const void*, const char*>> required,
+                      std::initializer_list<std::pair<const void*, const char*>> optional) {
+  for (auto& pr : required) {
+    if (!pr.first) return fail(MOE_ERR_INVALID_ARG, std::string(pr.second) + " is NULL");
+    if (misaligned(pr.first))
+      return fail(MOE_ERR_ALIGNMENT, std::string(pr.second) + " is not 16-byte aligned");
+  }
+  for (auto& pr : optional)
+    if (pr.first && misaligned(pr.first))
+      return fail(MOE_ERR_ALIGNMENT, std::string(pr.second) + " is not 16-byte aligned");
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define MOE_TRY(expr)                 \
+  do {                                \
+    const moe_status st_ = (expr);    \
+    if (st_ != MOE_OK) return st_;    \
+  } while (0)
+
+// The step sequences shared by the step-wise entry points and moe_forward.
+moe_status run_permute(const moe::Problem& p, const int32_t* ids, int32_t* counts,
+                       int32_t* offsets, int32_t* raw, int32_t* perm, int32_t* inv,
+                       unsigned char* ws, int32_t* table, hipStream_t s) {
+  PermuteWs w = carve_permute(p, ws);
+  MOE_TRY(hip_status(moe::launch_histogram(p, ids, w.blockcnt, s), "histogram launch"));
+  MOE_TRY(hip_status(moe::launch_scan(p, w.blockcnt, w.blockbase, raw ? raw : w.raw, counts,
+                                      offsets, table, s),
+                     "scan launch"));
+  return hip_status(moe::launch_scatter(p, ids, w.blockbase, offsets, perm, inv, s),
+                    "scatter launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_validate(const moe_desc* desc) {
+  g_last_error.clear();
+  return check_desc(desc);
+}
+
+moe_status moe_capacity(const moe_desc* desc, int64_t* C_out) {
+  MOE_TRY(check_desc(desc));
+  if (!C_out) return fail(MOE_ERR_INVALID_ARG, "C_out is NULL");
+  *C_out = make_problem(desc).C;
+  return MOE_OK;
+}
+
+moe_status moe_max_rows(const moe_desc* desc, int64_t* rows_out) {
+  MOE_TRY(check_desc(desc));
+  if (!rows_out) return fail(MOE_ERR_INVALID_ARG, "rows_out is NULL");
+  *rows_out = make_problem(desc).rows_max;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_size(const moe_desc* desc, int32_t entry, size_t* bytes) {
+  MOE_TRY(check_desc(desc));
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  const moe::Problem p = make_problem(desc);
+  switch (entry) {
+    case MOE_WS_PERMUTE:
+      *bytes = permute_ws_bytes(p);
+      return MOE_OK;
+    case MOE_WS_GROUPED_FFN:
+      *bytes = align_up(moe::tile_table_bytes(p));
+      return MOE_OK;
+    case MOE_WS_FORWARD:
+      *bytes = carve_forward(p, nullptr).bytes;
+      return MOE_OK;
+    default:
+      return fail(MOE_ERR_INVALID_ARG, "unknown workspace selector");
+  }
+}
+
+const char* moe_status_str(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_ALIGNMENT: return "MOE_ERR_ALIGNMENT";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "unknown moe_status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_route(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
+                     float* logits, int32_t* topk_ids, float* topk_gates, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc));
+  if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
+  MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {topk_ids, "topk_ids"}, {topk_gates, "topk_gates"}},
+                     {{bias, "bias"}, {logits, "logits"}}));
+  const moe::Problem p = make_problem(desc);
+  return hip_status(moe::launch_route(p, X, W_r, bias, logits, topk_ids, topk_gates,
+                                      (hipStream_t)stream),
+                    "route launch");
+}
+
+moe_status moe_permute(const moe_desc* desc, const int32_t* topk_ids, int32_t* counts,
+                       int32_t* offsets, int32_t* raw_counts, int32_t* perm_token,
+                       int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc));
+  if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
+  MOE_TRY(check_ptrs({{topk_ids, "topk_ids"}, {counts, "counts"}, {offsets, "offsets"},
+                      {perm_token, "perm_token"}, {inv_slot, "inv_slot"}},
+                     {{raw_counts, "raw_counts"}, {ws, "ws"}}));
+  const moe::Problem p = make_problem(desc);
+  if (!ws || ws_bytes < permute_ws_bytes(p))
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_PERMUTE)");
+  return run_permute(p, topk_ids, counts, offsets, raw_counts, perm_token, inv_slot,
+                     static_cast<unsigned char*>(ws), nullptr, (hipStream_t)stream);
+}
+
+moe_status moe_grouped_gemm_up(const moe_desc* desc, const void* X, const int32_t* offsets,
+                               const int32_t* perm_token, const void* W_gate, const void* W_up,
+                               void* H, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc, MOE_FLAG_TILE_TABLE_READY));
+  if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
+  MOE_TRY(check_ptrs({{X, "X"}, {offsets, "offsets"}, {perm_token, "perm_token"},
+                      {W_gate, "W_gate"}, {W_up, "W_up"}, {H, "H"}},
+                     {{ws, "ws"}}));
+  const moe::Problem p = make_problem(desc);
+  if (!ws || ws_bytes < moe::tile_table_bytes(p))
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_GROUPED_FFN)");
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* table = static_cast<int32_t*>(ws);
+  if (!(desc->flags & MOE_FLAG_TILE_TABLE_READY))
+    MOE_TRY(hip_status(moe::launch_tile_table(p, offsets, table, s), "tile table launch"));
+  return hip_status(moe::launch_gemm_up(p, X, perm_token, table, W_gate, W_up, H, s),
+                    "grouped GEMM (up) launch");
+}
+
+moe_status moe_grouped_gemm_down(const moe_desc* desc, const void* H, const int32_t* offsets,
+                                 const void* W_down, void* O, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc, MOE_FLAG_TILE_TABLE_READY));
+  if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
+  MOE_TRY(check_ptrs({{H, "H"}, {offsets, "offsets"}, {W_down, "W_down"}, {O, "O"}}, {{ws, "ws"}}));
+  const moe::Problem p = make_problem(desc);
+  if (!ws || ws_bytes < moe::tile_table_bytes(p))
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_GROUPED_FFN)");
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* table = static_cast<int32_t*>(ws);
+  if (!(desc->flags & MOE_FLAG_TILE_TABLE_READY))
+    MOE_TRY(hip_status(moe::launch_tile_table(p, offsets, table, s), "tile table launch"));
+  return hip_status(moe::launch_gemm_down(p, H, table, W_down, O, s), "grouped GEMM (down) launch");
+}
+
+moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* offsets,
+                           const int32_t* perm_token, const void* W_gate, const void* W_up,
+                           const void* W_down, void* H, void* O, void* ws, size_t ws_bytes,
+                           void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc, MOE_FLAG_TILE_TABLE_READY));
+  if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
+  MOE_TRY(check_ptrs({{X, "X"}, {offsets, "offsets"}, {perm_token, "perm_token"},
+                      {W_gate, "W_gate"}, {W_up, "W_up"}, {W_down, "W_down"}, {H, "H"}, {O, "O"}},
+                     {{ws, "ws"}}));
+  const moe::Problem p = make_problem(desc);
+  if (!ws || ws_bytes < moe::tile_table_bytes(p))
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_GROUPED_FFN)");
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* table = static_cast<int32_t*>(ws);
+  if (!(desc->flags & MOE_FLAG_TILE_TABLE_READY))
+    MOE_TRY(hip_status(moe::launch_tile_table(p, offsets, table, s), "tile table launch"));
+  MOE_TRY(hip_status(moe::launch_gemm_up(p, X, perm_token, table, W_gate, W_up, H, s),
+                     "grouped GEMM (up) launch"));
+  return hip_status(moe::launch_gemm_down(p, H, table, W_down, O, s), "grouped GEMM (down) launch");
+}
+
+moe_status moe_combine(const moe_desc* desc, const void* O, const float* topk_gates,
+                       const int32_t* inv_slot, void* Y, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc));
+  if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
+  MOE_TRY(check_ptrs({{O, "O"}, {topk_gates, "topk_gates"}, {inv_slot, "inv_slot"}, {Y, "Y"}}, {}));
+  const moe::Problem p = make_problem(desc);
+  return hip_status(moe::launch_combine(p, O, topk_gates, inv_slot, Y, (hipStream_t)stream),
+                    "combine launch");
+}
+
+moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
+                       const void* W_gate, const void* W_up, const void* W_down, void* Y,
+                       void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc));
+  if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
+  MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {W_gate, "W_gate"}, {W_up, "W_up"},
+                      {W_down, "W_down"}, {Y, "Y"}},
+                     {{bias, "bias"}, {ws, "ws"}}));
+  const moe::Problem p = make_problem(desc);
+  const ForwardWs size_only = carve_forward(p, nullptr);
+  if (!ws || ws_bytes < size_only.bytes)
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_FORWARD)");
+  hipStream_t s = (hipStream_t)stream;
+  ForwardWs w = carve_forward(p, static_cast<unsigned char*>(ws));
+  MOE_TRY(hip_status(moe::launch_route(p, X, W_r, bias, nullptr, w.ids, w.gates, s), "route launch"));
+  MOE_TRY(run_permute(p, w.ids, w.counts, w.offsets, nullptr, w.perm, w.inv, w.permute, w.table, s));
+  MOE_TRY(hip_status(moe::launch_gemm_up(p, X, w.perm, w.table, W_gate, W_up, w.H, s),
+                     "grouped GEMM (up) launch"));
+  MOE_TRY(hip_status(moe::launch_gemm_down(p, w.H, w.table, W_down, w.O, s),
+                     "grouped GEMM (down) launch"));
+  return hip_status(moe::launch_combine(p, w.O, w.gates, w.inv, Y, s), "combine launch");
+}
+
+}  // extern "C"
