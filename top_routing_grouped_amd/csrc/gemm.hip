@@ -8,7 +8,7 @@
 // and applies SwiGLU while the products are still in the accumulators (§6.3).
 //
 // bf16 kernel (gfx950, one 256-thread workgroup per tile, 1 per CU):
-// * Tile = 128 expert-major rows x 256 accumulator columns (up: 128 W_gate
+// * Tile = 256 expert-major rows x 256 accumulator columns (up: 128 W_gate
 //   columns + the same 128 W_up columns, so each lane holds matching gate and
 //   up values and SwiGLU is register-local; down: 256 W_down columns).
 //   Row tiles come from a device-built table (expert, row range), so experts
@@ -16,10 +16,15 @@
 //   surplus workgroups exit at once.
 // * Loads go global -> LDS with global_load_lds_dwordx4 (no VGPR staging).
 //   Each lane supplies its own global address, which is what makes the row
-//   gather free: a lane simply points at row perm_token[s] of X.  Three LDS
-//   stages of 48 KB keep two k-steps in flight.
+//   gather free: a lane simply points at row perm_token[s] of X.  Four LDS
+//   stages of 32 KB (k depth 32) keep three k-steps in flight.
+// * Each wave owns a 128 x 128 sub-tile (256 fp32 accumulators per lane):
+//   the LDS bytes read per MFMA flop fall with the sub-tile's perimeter /
+//   area, so the big sub-tile keeps LDS bandwidth below the MFMA rate.
+//   Fragments are read one 16-deep sub-step ahead of the MFMAs that use them,
+//   and 32-row blocks past an expert's last row skip their MFMAs.
 // * LDS layouts are XOR-swizzled at 16-byte granularity so both fragment
-//   reads are bank-conflict free: token rows (128 B) use slot c^((r>>1)&7);
+//   reads are bank-conflict free: token rows (64 B) use slot c^((r>>2)&3);
 //   weight rows (512 B, natural [k][n] order) use slot q^(4*(k&3)) and are
 //   read with ds_read_b64_tr_b16, which hands each lane 4 consecutive k of
 //   one column -- the MFMA operand layout -- so weights are never transposed.
@@ -38,16 +43,41 @@ using i16x4 = short __attribute__((ext_vector_type(4)));
 using f32x16 = float __attribute__((ext_vector_type(16)));
 using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
 
-constexpr int BM = kGemmBM;      // 128 rows (tokens) per tile
 constexpr int BN = 256;          // accumulator columns per tile
-constexpr int BK = 64;           // k per stage
-constexpr int kStages = 3;
-constexpr int kThreads = 256;
-constexpr int kAStage = BM * BK * 2;        // 16 KB
-constexpr int kBStage = BK * BN * 2;        // 32 KB
-constexpr int kStageBytes = kAStage + kBStage;
-constexpr int kAInstr = kAStage / 1024 / 4; // DMA instructions per wave per stage (4)
-constexpr int kBInstr = kBStage / 1024 / 4; // (8)
+
+// Tile geometry: a WGM x WGN grid of waves, each owning WTB 32-row token
+// blocks x WCB 32-column blocks; NST LDS stages of depth BK (32 or 64).
+template <int WGM, int WGN, int WTB, int WCB, int NST, int BK>
+struct Geo {
+  static constexpr int kWaves = WGM * WGN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int BM = WGM * WTB * 32;
+  static_assert(WGN * WCB * 32 == BN, "waves must cover the 256 accumulator columns");
+  static constexpr int kAStage = BM * BK * 2;
+  static constexpr int kBStage = BK * BN * 2;
+  static constexpr int kStageBytes = kAStage + kBStage;
+  static constexpr int kAInstr = kAStage / 1024 / kWaves;   // copy instructions per wave per stage
+  static constexpr int kBInstr = kBStage / 1024 / kWaves;
+  static_assert(kAInstr * 1024 * kWaves == kAStage && kBInstr * 1024 * kWaves == kBStage, "copy split");
+  static constexpr int kInstr = kAInstr + kBInstr;
+  static constexpr int kLds = NST * kStageBytes;
+  // token tile rows hold BK/8 16-byte chunks; XOR swizzle slot = c ^ ((r >> kSh) & (kCpr-1))
+  static constexpr int kCpr = BK / 8;
+  static constexpr int kSh = (BK == 32) ? 2 : 1;
+  static_assert(BK == 32 || BK == 64, "stage depth");
+};
+// Production geometry: 256 x 256 tiles, 8 waves (2 per SIMD) in a 2 x 4 grid,
+// each wave 128 tokens x 64 columns (128 fp32 accumulators per lane).  The
+// wave tile is tall (more token rows than weight columns) because weight
+// fragments come through the transpose reads, whose LDS throughput is well
+// below that of the 16-byte token-fragment reads.
+constexpr int kWGM = 2, kWGN = 4, kWTB = 4, kWCB = 2;
+// Two 64-deep stages of 64 KB: 64-deep stages make every gathered token-row
+// chunk a whole 128-byte line.  The copy rate is bounded by the requests an
+// L1 keeps in flight, so full-line requests move more bytes per request.
+constexpr int kNST = 2, kBK = 64;
+using ProdGeo = Geo<kWGM, kWGN, kWTB, kWCB, kNST, kBK>;
+static_assert(ProdGeo::BM == kGemmBM, "tile table rows must match the kernel tile");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -61,21 +91,41 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // so clobbering it is safe; silence the generic reserved-register warning.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, const void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_ptr_t)lds);
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(g), "s"(m0)
+               : "v"(g), "s"(lds_addr)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// s_waitcnt lgkmcnt(0) as a builtin (gfx9 encoding: vmcnt and expcnt left at
+// their maxima), so the compiler's own wait tracking sees it.
+constexpr int kWaitLds = 0xC07F;
+
+// Wait until at most `pending` stages (INSTR copy instructions each) of this
+// wave are still in flight.
+template <int INSTR>
+__device__ __forceinline__ void wait_copies(int pending) {
+  if (pending >= 4) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * INSTR) : "memory");
+  else if (pending == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * INSTR) : "memory");
+  else if (pending == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * INSTR) : "memory");
+  else if (pending == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(INSTR) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return __fdividef(g, 1.0f + __expf(-g)) * u;
 }
 
-template <bool UP>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(
+template <int WTB, int WCB>
+struct Frags {
+  bf16x8 a[WTB];   // token fragments (MFMA B operand), one per 32-row block
+  bf16x8 b[WCB];   // weight fragments (MFMA A operand), one per 32-column block
+};
+
+template <bool UP, int WGM, int WGN, int WTB, int WCB, int NST, int BK>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_bf16(
     const uint16_t* __restrict__ A,       // up: X [T][Kd]; down: H [rows][Kd]
     const int32_t* __restrict__ perm,     // up: expert-major slot -> token
     const int32_t* __restrict__ table,    // tile table
@@ -83,12 +133,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(
     const uint16_t* __restrict__ B1,      // up: W_up
     uint16_t* __restrict__ C,             // up: H [rows][N]; down: O [rows][N]
     int64_t T, int Kd, int N, int NT) {
+  using G = Geo<WGM, WGN, WTB, WCB, NST, BK>;
+  constexpr int kCpr = G::kCpr, kSh = G::kSh, kRowsPerCopy = 64 / kCpr;
+  constexpr int KS = BK / 16;              // 16-deep MFMA sub-steps per stage
+  constexpr int BM = G::BM, kAStage = G::kAStage, kStageBytes = G::kStageBytes;
+  constexpr int kAInstr = G::kAInstr, kBInstr = G::kBInstr, kInstr = G::kInstr;
+  constexpr int kStages = NST;
+  constexpr int kHalf = WCB / 2;           // up: gate blocks (then as many up blocks)
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int wm = w / WGN, wn = w - (w / WGN) * WGN;
+  const uint32_t lds_base = (uint32_t)(size_t)(lds_ptr_t)smem;
 
   // ---- tile decode (XCD-aware: consecutive tile ids on one XCD)
   const int total = table[0] * NT;
@@ -102,14 +160,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(
   const int e = ent[0], row0 = ent[1];
   const int nrows = ent[2] - row0;
   const int ncol0 = nt * (UP ? BN / 2 : BN);   // first output column of the tile
+  // 32-row token blocks of this wave that hold any valid row (uniform per wave)
+  int ntb = (nrows - wm * (WTB * 32) + 31) / 32;
+  ntb = ntb < 0 ? 0 : (ntb > WTB ? WTB : ntb);
 
-  // ---- DMA source addresses
-  // token tile: instruction i of wave w fills rows (4w+i)*8 + lane/8, slot lane%8
+  // ---- copy source addresses
+  // token tile (2*BK-byte rows): copy instruction j = kAInstr*w + i fills rows
+  // kRowsPerCopy*j + lane/kCpr, slot lane%kCpr holding k chunk
+  // slot^((row>>kSh)&(kCpr-1)).
   const uint16_t* asrc[kAInstr];
 #pragma unroll
   for (int i = 0; i < kAInstr; ++i) {
-    const int r = (w * kAInstr + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int r = (w * kAInstr + i) * kRowsPerCopy + (lane / kCpr);
+    const int c = (lane % kCpr) ^ ((r >> kSh) & (kCpr - 1));
     const int rr = r < nrows ? r : nrows - 1;
     int64_t row;
     if (UP) {
@@ -121,8 +184,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(
     }
     asrc[i] = A + row * (int64_t)Kd + c * 8;
   }
-  // weight tile: instruction i fills rows 2*(8w+i) + lane/32, slot lane%32;
-  // slot -> column chunk depends on the row's k&3 = (2i + lane/32) & 3.
+  // weight tile (512 B rows, natural [k][n]): copy instruction j = kBInstr*w + i
+  // fills rows 2j + lane/32, slot lane%32 holding column chunk slot^(4*(k&3));
+  // k&3 = (2j + lane/32)&3 depends on the parity of j only.
   const uint16_t* bsrc[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
@@ -141,130 +205,151 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(
     bsrc[par] = base + (int64_t)e * Kd * N + (int64_t)(lane >> 5) * N + col;
   }
 
-  auto issue_stage = [&](int kt, int buf) {
-    unsigned char* As = smem + buf * kStageBytes;
-    unsigned char* Bs = As + kAStage;
+  auto issue_stage = [&](int kt) {
+    const uint32_t As = lds_base + (uint32_t)((kt % kStages) * kStageBytes);
+    const uint32_t Bs = As + kAStage;
 #pragma unroll
     for (int i = 0; i < kAInstr; ++i) dma16(asrc[i] + kt * BK, As + (w * kAInstr + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < kBInstr; ++i)
-      dma16(bsrc[i & 1] + (int64_t)(kt * BK + 2 * (w * kBInstr + i)) * N,
-            Bs + (w * kBInstr + i) * 1024);
+    for (int i = 0; i < kBInstr; ++i) {
+      const int jb = w * kBInstr + i;
+      dma16(bsrc[jb & 1] + (int64_t)(kt * BK + 2 * jb) * N, Bs + jb * 1024);
+    }
   };
 
   // ---- fragment geometry
-  // token fragment (MFMA B operand): lane -> token row wm*64 + tb*32 + lane%32, k chunk ks*2 + lane/32
-  int a_off[2][4];
+  // token fragment: lane -> token row wm*32*WTB + tb*32 + lane%32, k chunk 2*ks + lane/32
+  int a_off[WTB][KS];
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
+  for (int tb = 0; tb < WTB; ++tb)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int r = wm * 64 + tb * 32 + (lane & 31);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int r = wm * (WTB * 32) + tb * 32 + (lane & 31);
       const int c = ks * 2 + (lane >> 5);
-      a_off[tb][ks] = r * 128 + ((c ^ ((r >> 1) & 7)) * 16);
+      a_off[tb][ks] = r * (2 * BK) + ((c ^ ((r >> kSh) & (kCpr - 1))) * 16);
     }
-  // weight fragment (MFMA A operand) via transpose loads: group g = lane/16,
-  // lane s in group -> row ks*16 + 8*(g/2) + s/4 (+4), column n0 + 16*(g%2) + 4*(s%4)
+  // weight fragment via transpose loads: group g = lane/16, lane s in group ->
+  // row 16*ks + 8*(g/2) + s/4 (+4 for the second half), column 16*(g%2) + 4*(s%4)
   const int g = lane >> 4, s16 = lane & 15;
   const int tr_row = 8 * (g >> 1) + (s16 >> 2);
-  int b_off[4][2];   // [cb][half of k group], byte offset within the stage's weight tile (ks = 0)
+  int b_off[WCB][2];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int cb = 0; cb < WCB; ++cb) {
     int colbase;
-    if (UP) colbase = (cb < 2) ? (wn * 64 + cb * 32) : (128 + wn * 64 + (cb - 2) * 32);
-    else colbase = wn * 128 + cb * 32;
+    if (UP) colbase = (cb < kHalf) ? (wn * kHalf * 32 + cb * 32) : (BN / 2 + wn * kHalf * 32 + (cb - kHalf) * 32);
+    else colbase = wn * WCB * 32 + cb * 32;
     const int n = colbase + 16 * (g & 1) + 4 * (s16 & 3);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int k = tr_row + 4 * h;
       const int q = n >> 3;
-      b_off[cb][h] = k * 512 + ((q ^ (4 * (k & 3))) * 16) + ((n >> 2) & 1) * 8;
+      b_off[cb][h] = kAStage + k * 512 + ((q ^ (4 * (k & 3))) * 16) + ((n >> 2) & 1) * 8;
     }
   }
 
-  f32x16 acc[4][2];
+  auto read_frags = [&](Frags<WTB, WCB>& f, int kt, int ks) {
+    const unsigned char* S = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+    for (int tb = 0; tb < WTB; ++tb)
+      f.a[tb] = *reinterpret_cast<const bf16x8*>(S + a_off[tb][ks]);
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int cb = 0; cb < WCB; ++cb) {
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(S + b_off[cb][0] + ks * 16 * 512));
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(S + b_off[cb][1] + ks * 16 * 512));
+      f.b[cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+
+  f32x16 acc[WCB][WTB];
+#pragma unroll
+  for (int cb = 0; cb < WCB; ++cb)
+#pragma unroll
+    for (int tb = 0; tb < WTB; ++tb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[cb][tb][v] = 0.f;
 
-  const int KT = Kd / BK;
-  issue_stage(0, 0);
-  if (KT > 1) issue_stage(1, 1);
-  if (KT > 1)
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  auto mma = [&](const Frags<WTB, WCB>& f) {
+#pragma unroll
+    for (int tb = 0; tb < WTB; ++tb)
+      if (tb < ntb) {
+#pragma unroll
+        for (int cb = 0; cb < WCB; ++cb)
+          acc[cb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[cb], f.a[tb], acc[cb][tb], 0, 0, 0);
+      }
+  };
+
+  // ---- main loop: stage kt+NST-1 copies in flight while stage kt is
+  // multiplied; fragments are read one 16-deep sub-step ahead of the MFMAs.
+  // Order inside an iteration (pinned with sched_barrier): wait for the
+  // fragments already in flight, issue the next fragment reads, then the
+  // MFMAs on the landed fragments, so LDS reads overlap the matrix work.
+  const int KT = Kd / BK;   // the host requires Kd % 64 == 0
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < KT) issue_stage(s);
+  wait_copies<kInstr>((KT - 1 < kStages - 2) ? KT - 1 : kStages - 2);
   asm volatile("s_barrier" ::: "memory");
 
-  int buf = 0;
+  Frags<WTB, WCB> cur, nxt;
+  read_frags(cur, 0, 0);
   for (int kt = 0; kt < KT; ++kt) {
-    const unsigned char* As = smem + buf * kStageBytes;
-    const unsigned char* Bs = As + kAStage;
-    bf16x8 af[4][2], bfr[4][4];
+    if (kt + kStages - 1 < KT) issue_stage(kt + kStages - 1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-        af[ks][tb] = *reinterpret_cast<const bf16x8*>(As + a_off[tb][ks]);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        // ks advances 16 rows of the weight tile (8 KB); row&3 is unchanged
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(Bs + b_off[cb][0] + ks * 16 * 512));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(Bs + b_off[cb][1] + ks * 16 * 512));
-        bfr[ks][cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int ks = 0; ks < KS; ks += 2) {
+      __builtin_amdgcn_s_waitcnt(kWaitLds);            // cur landed
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(nxt, kt, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(cur);
+      __builtin_amdgcn_sched_barrier(0);
+      // nxt landed (and, on the last sub-step, every read of stage kt is
+      // done).  Waiting here, on both paths of the branch below, keeps the
+      // compiler from merging the pending reads of the two paths.
+      __builtin_amdgcn_s_waitcnt(kWaitLds);
+      if (ks + 2 < KS) {
+        read_frags(cur, kt, ks + 2);
+      } else if (kt + 1 < KT) {
+        // stage kt+1 must have landed (own copies), then publish it to all
+        // waves; the barrier also tells every wave that stage kt is free.
+        const int last = (kt + kStages - 1 < KT) ? kt + kStages - 1 : KT - 1;
+        wait_copies<kInstr>(last - (kt + 1));
+        asm volatile("s_barrier" ::: "memory");
+        read_frags(cur, kt + 1, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      mma(nxt);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 2 < KT) {
-      int nb = buf + 2;
-      if (nb >= kStages) nb -= kStages;
-      issue_stage(kt + 2, nb);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-          acc[cb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks][cb], af[ks][tb], acc[cb][tb], 0, 0, 0);
-    if (kt + 2 < KT)
-      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    buf = (buf + 1 == kStages) ? 0 : buf + 1;
   }
 
   // ---- epilogue: lane holds, for token column lane%32 of block tb, output
   // columns 8*(v/4) + 4*(lane/32) + v%4 of block cb (v = accumulator index).
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int rloc = wm * 64 + tb * 32 + (lane & 31);
+  for (int tb = 0; tb < WTB; ++tb) {
+    const int rloc = wm * (WTB * 32) + tb * 32 + (lane & 31);
     if (rloc >= nrows) continue;
     uint16_t* crow = C + (int64_t)(row0 + rloc) * N;
     if (UP) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < kHalf; ++cb)
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
-          const int col = ncol0 + wn * 64 + cb * 32 + 8 * v4 + 4 * (lane >> 5);
+          const int col = ncol0 + wn * kHalf * 32 + cb * 32 + 8 * v4 + 4 * (lane >> 5);
           if (col >= N) continue;
           float h[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = silu_mul(acc[cb][tb][4 * v4 + r], acc[cb + 2][tb][4 * v4 + r]);
+          for (int r = 0; r < 4; ++r) h[r] = silu_mul(acc[cb][tb][4 * v4 + r], acc[cb + kHalf][tb][4 * v4 + r]);
           u32x2 pk = {dev::pack_bf16x2(h[0], h[1]), dev::pack_bf16x2(h[2], h[3])};
           *reinterpret_cast<u32x2*>(crow + col) = pk;
         }
     } else {
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < WCB; ++cb)
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
-          const int col = ncol0 + wn * 128 + cb * 32 + 8 * v4 + 4 * (lane >> 5);
+          const int col = ncol0 + wn * WCB * 32 + cb * 32 + 8 * v4 + 4 * (lane >> 5);
           if (col >= N) continue;
           u32x2 pk = {dev::pack_bf16x2(acc[cb][tb][4 * v4], acc[cb][tb][4 * v4 + 1]),
                       dev::pack_bf16x2(acc[cb][tb][4 * v4 + 2], acc[cb][tb][4 * v4 + 3])};
@@ -274,19 +359,35 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(
   }
 }
 
+template <bool UP>
+hipError_t launch_bf16(const uint16_t* A, const int32_t* perm, const int32_t* table,
+                       const uint16_t* B0, const uint16_t* B1, uint16_t* C, int64_t T, int Kd,
+                       int N, int64_t mtiles, hipStream_t s) {
+  const int NT = (N + (UP ? BN / 2 : BN) - 1) / (UP ? BN / 2 : BN);
+  auto* kern = grouped_gemm_bf16<UP, kWGM, kWGN, kWTB, kWCB, kNST, kBK>;
+  hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, ProdGeo::kLds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(mtiles * NT)), dim3(ProdGeo::kThreads),
+                     (size_t)ProdGeo::kLds, s, A, perm, table, B0, B1, C, T, Kd, N, NT);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- fp32 (plain FMA)
 // 32-row x 64-column tiles, LDS-tiled over k; only for the fp32 element type.
+constexpr int kF32Rows = 32;
+constexpr int kF32Sub = kGemmBM / kF32Rows;   // sub-tiles per table tile
 template <bool UP>
 __global__ __launch_bounds__(256) void grouped_gemm_f32(
     const float* __restrict__ A, const int32_t* __restrict__ perm, const int32_t* __restrict__ table,
     const float* __restrict__ B0, const float* __restrict__ B1, float* __restrict__ C, int64_t T,
     int Kd, int N, int NT) {
-  constexpr int TM = 32, TN = 64, TK = 16;
+  constexpr int TM = kF32Rows, TN = 64, TK = 16;
   __shared__ float As[TM][TK + 1];
   __shared__ float Bg[TK][TN];
   __shared__ float Bu[TK][TN];
   // each 128-row table tile is covered by BM/TM sub-tiles of TM rows
-  constexpr int kSub = BM / TM;
+  constexpr int kSub = kF32Sub;
   const int total = table[0] * kSub * NT;
   const int bid = blockIdx.x;
   if (bid >= total) return;
@@ -354,43 +455,27 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
 hipError_t launch_gemm_up(const Problem& p, const void* X, const int32_t* perm,
                           const int32_t* table, const void* W_gate, const void* W_up, void* H,
                           hipStream_t s) {
-  const int64_t mtiles = max_row_tiles(p, BM);
-  if (p.bf16) {
-    const int NT = (p.n + BN / 2 - 1) / (BN / 2);
-    const size_t smem = (size_t)kStages * kStageBytes;
-    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_bf16<true>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3((unsigned)(mtiles * NT)), dim3(kThreads), smem,
-                       s, (const uint16_t*)X, perm, table, (const uint16_t*)W_gate,
-                       (const uint16_t*)W_up, (uint16_t*)H, p.T, p.d, p.n, NT);
-  } else {
-    const int NT = (p.n + 63) / 64;
-    hipLaunchKernelGGL(grouped_gemm_f32<true>, dim3((unsigned)(mtiles * 4 * NT)), dim3(256), 0, s,
-                       (const float*)X, perm, table, (const float*)W_gate, (const float*)W_up,
-                       (float*)H, p.T, p.d, p.n, NT);
-  }
+  const int64_t mtiles = max_row_tiles(p, kGemmBM);
+  if (p.bf16)
+    return launch_bf16<true>((const uint16_t*)X, perm, table, (const uint16_t*)W_gate,
+                             (const uint16_t*)W_up, (uint16_t*)H, p.T, p.d, p.n, mtiles, s);
+  const int NT = (p.n + 63) / 64;
+  hipLaunchKernelGGL(grouped_gemm_f32<true>, dim3((unsigned)(mtiles * kF32Sub * NT)), dim3(256), 0, s,
+                     (const float*)X, perm, table, (const float*)W_gate, (const float*)W_up,
+                     (float*)H, p.T, p.d, p.n, NT);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const Problem& p, const void* H, const int32_t* table,
                             const void* W_down, void* O, hipStream_t s) {
-  const int64_t mtiles = max_row_tiles(p, BM);
-  if (p.bf16) {
-    const int NT = (p.d + BN - 1) / BN;
-    const size_t smem = (size_t)kStages * kStageBytes;
-    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_bf16<false>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3((unsigned)(mtiles * NT)), dim3(kThreads),
-                       smem, s, (const uint16_t*)H, nullptr, table, (const uint16_t*)W_down,
-                       nullptr, (uint16_t*)O, p.T, p.n, p.d, NT);
-  } else {
-    const int NT = (p.d + 63) / 64;
-    hipLaunchKernelGGL(grouped_gemm_f32<false>, dim3((unsigned)(mtiles * 4 * NT)), dim3(256), 0, s,
-                       (const float*)H, nullptr, table, (const float*)W_down, nullptr, (float*)O,
-                       p.T, p.n, p.d, NT);
-  }
+  const int64_t mtiles = max_row_tiles(p, kGemmBM);
+  if (p.bf16)
+    return launch_bf16<false>((const uint16_t*)H, nullptr, table, (const uint16_t*)W_down,
+                              nullptr, (uint16_t*)O, p.T, p.n, p.d, mtiles, s);
+  const int NT = (p.d + 63) / 64;
+  hipLaunchKernelGGL(grouped_gemm_f32<false>, dim3((unsigned)(mtiles * kF32Sub * NT)), dim3(256), 0, s,
+                     (const float*)H, nullptr, table, (const float*)W_down, nullptr, (float*)O,
+                     p.T, p.n, p.d, NT);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ constexpr int kPermuteBlock = 256;
 
 // Tile rows of the grouped GEMMs (shared by both GEMMs so one tile table
 // serves both).
-constexpr int kGemmBM = 128;
+constexpr int kGemmBM = 256;
 
 inline int64_t permute_blocks(int64_t T) { return (T + kPermuteBlock - 1) / kPermuteBlock; }
 

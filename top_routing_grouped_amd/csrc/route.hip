@@ -28,7 +28,6 @@ using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 constexpr int kTok = 64;       // tokens per workgroup
 constexpr int kBK = 64;        // k per stage
 constexpr int kThreads = 256;
-constexpr int kPF = 4;         // X stages in flight per wave
 
 // ---------------------------------------------------------------- selection helpers
 __device__ __forceinline__ int sort_key(float f) {
@@ -153,12 +152,16 @@ __device__ void route_tail(float* L, int S, int64_t t0, int64_t T, int E, int K,
 
 // ---------------------------------------------------------------- bf16 router (MFMA)
 // NBW: 16-column blocks per wave; the padded expert range is 32*NBW.
+// The widest expert range (NBW = 8) needs the whole register file: one
+// workgroup per CU; narrower ones fit two.
 template <int NBW, bool VEC>
-__global__ __launch_bounds__(kThreads, 2) void route_bf16_kernel(
+__global__ __launch_bounds__(kThreads, (NBW >= 8) ? 1 : 2) void route_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
     int d, int E, int K) {
   constexpr int Epad = 32 * NBW;
+  // X stages held in registers (prefetch depth); fewer when the weight tile is wide
+  constexpr int kPF = (NBW >= 8) ? 4 : 6;
   constexpr int R = Epad + 16;            // bf16 elements per LDS weight row (padded)
   constexpr int S = Epad + 16;            // floats per LDS score row
   constexpr int kStageElems = kBK * R;
@@ -183,10 +186,11 @@ __global__ __launch_bounds__(kThreads, 2) void route_bf16_kernel(
     arow[rb] = X + t * (int64_t)d + 8 * (lane >> 4);
   }
 
-  // Weight tile staging: NBW chunks of 8 bf16 per thread per stage.
+  // Weight tile staging: NBW chunks of 8 bf16 per thread per stage, two
+  // stages in registers (loaded two k-steps ahead) plus two in LDS.
   constexpr int kChunksPerRow = Epad / 8;
-  uint16_t breg[NBW][8];
-  auto load_b = [&](int kt) {
+  uint16_t breg[2][NBW][8];
+  auto load_b = [&](int slot, int kt) {
 #pragma unroll
     for (int c = 0; c < NBW; ++c) {
       const int idx = tid + kThreads * c;
@@ -198,16 +202,16 @@ __global__ __launch_bounds__(kThreads, 2) void route_bf16_kernel(
         if (col < E) v = *reinterpret_cast<const u32x4*>(src);
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          breg[c][2 * h] = (uint16_t)(v[h] & 0xFFFF);
-          breg[c][2 * h + 1] = (uint16_t)(v[h] >> 16);
+          breg[slot][c][2 * h] = (uint16_t)(v[h] & 0xFFFF);
+          breg[slot][c][2 * h + 1] = (uint16_t)(v[h] >> 16);
         }
       } else {
 #pragma unroll
-        for (int h = 0; h < 8; ++h) breg[c][h] = (col + h < E) ? src[h] : (uint16_t)0;
+        for (int h = 0; h < 8; ++h) breg[slot][c][h] = (col + h < E) ? src[h] : (uint16_t)0;
       }
     }
   };
-  auto store_b = [&](int buf) {
+  auto store_b = [&](int slot, int buf) {
 #pragma unroll
     for (int c = 0; c < NBW; ++c) {
       const int idx = tid + kThreads * c;
@@ -215,7 +219,8 @@ __global__ __launch_bounds__(kThreads, 2) void route_bf16_kernel(
       const int col = (idx % kChunksPerRow) * 8;
       u32x4 v;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) v[h] = (uint32_t)breg[c][2 * h] | ((uint32_t)breg[c][2 * h + 1] << 16);
+      for (int h = 0; h < 4; ++h)
+        v[h] = (uint32_t)breg[slot][c][2 * h] | ((uint32_t)breg[slot][c][2 * h + 1] << 16);
       *reinterpret_cast<u32x4*>(Bs + buf * kStageElems + row * R + col) = v;
     }
   };
@@ -240,11 +245,12 @@ __global__ __launch_bounds__(kThreads, 2) void route_bf16_kernel(
   const int trow = 8 * g + (s4 >> 2);
   const int tcol = wn * 16 * NBW + 4 * (s4 & 3);
 
-  load_b(0);
+  load_b(0, 0);
+  if (KT > 1) load_b(1, 1);
 #pragma unroll
   for (int s = 0; s < kPF - 1; ++s)
     if (s < KT) load_a(s, s);
-  store_b(0);
+  store_b(0, 0);
   __syncthreads();
 
   for (int kt0 = 0; kt0 < KT; kt0 += kPF) {
@@ -253,8 +259,9 @@ __global__ __launch_bounds__(kThreads, 2) void route_bf16_kernel(
       const int kt = kt0 + u;
       if (kt < KT) {
         // weights first: vmcnt retires in issue order, so the wait before
-        // store_b then leaves the deeper X prefetch in flight.
-        if (kt + 1 < KT) load_b(kt + 1);
+        // store_b then leaves the deeper X prefetch in flight.  kt0 is a
+        // multiple of kPF (even), so kt%2 == u%2 at compile time.
+        if (kt + 2 < KT) load_b(u % 2, kt + 2);
         if (kt + kPF - 1 < KT) load_a((u + kPF - 1) % kPF, kt + kPF - 1);
         const uint16_t* Bt = Bs + (kt & 1) * kStageElems;
 #pragma unroll
@@ -273,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_bf16_kernel(
               acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][ks][rb], b, acc[rb][nb], 0, 0, 0);
           }
         }
-        if (kt + 1 < KT) store_b((kt + 1) & 1);
+        if (kt + 1 < KT) store_b((u + 1) % 2, (kt + 1) & 1);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
     }
