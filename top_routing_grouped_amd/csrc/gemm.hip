@@ -7,7 +7,7 @@
 // the GEMM's operand load instead of building a gathered T*K*d copy (§6.2),
 // and applies SwiGLU while the products are still in the accumulators (§6.3).
 //
-// bf16 kernel (gfx950, one 256-thread workgroup per tile, 1 per CU):
+// bf16 kernel (gfx950, one 512-thread workgroup per tile, 1 per CU):
 // * Tile = 256 expert-major rows x 256 accumulator columns (up: 128 W_gate
 //   columns + the same 128 W_up columns, so each lane holds matching gate and
 //   up values and SwiGLU is register-local; down: 256 W_down columns).
@@ -16,21 +16,25 @@
 //   surplus workgroups exit at once.
 // * Loads go global -> LDS with global_load_lds_dwordx4 (no VGPR staging).
 //   Each lane supplies its own global address, which is what makes the row
-//   gather free: a lane simply points at row perm_token[s] of X.  Four LDS
-//   stages of 32 KB (k depth 32) keep three k-steps in flight.
-// * Each wave owns a 128 x 128 sub-tile (256 fp32 accumulators per lane):
-//   the LDS bytes read per MFMA flop fall with the sub-tile's perimeter /
-//   area, so the big sub-tile keeps LDS bandwidth below the MFMA rate.
-//   Fragments are read one 16-deep sub-step ahead of the MFMAs that use them,
-//   and 32-row blocks past an expert's last row skip their MFMAs.
+//   gather free: a lane simply points at row perm_token[s] of X.  Two LDS
+//   stages of 64 KB (k depth 64, so every gathered row chunk is a whole
+//   128-byte line) keep the next k-step loading while this one multiplies.
+// * 8 waves (2 per SIMD) in a 2 x 4 grid; each wave owns 128 token rows x 64
+//   accumulator columns (128 fp32 accumulators per lane).  Fragments are read
+//   one 16-deep sub-step ahead of the MFMAs that use them, and 32-row blocks
+//   past an expert's last row skip their MFMAs.
 // * LDS layouts are XOR-swizzled at 16-byte granularity so both fragment
-//   reads are bank-conflict free: token rows (64 B) use slot c^((r>>2)&3);
+//   reads are bank-conflict free: token rows (128 B) use slot c^((r>>1)&7);
 //   weight rows (512 B, natural [k][n] order) use slot q^(4*(k&3)) and are
 //   read with ds_read_b64_tr_b16, which hands each lane 4 consecutive k of
 //   one column -- the MFMA operand layout -- so weights are never transposed.
 // * The MFMA computes the transposed tile (weights as the A operand, tokens
-//   as B), so each lane ends with 4 consecutive output columns of one row and
-//   stores 8 bytes at a time.
+//   as B), so each lane ends with 4 consecutive output columns of one row.
+// * Epilogue: the finished tile is written into the (now idle) stage buffers
+//   as a row-major bf16 tile and stored as whole rows with 16-byte lanes;
+//   storing straight from the accumulators would write 16-byte pieces of 32
+//   different rows per instruction, which made the store phase cost about a
+//   third of the down-projection's time.
 // * Workgroup ids are remapped so that consecutive tiles (same expert, same
 //   token rows) run on the same XCD and share its L2.
 #include "moe_internal.hpp"
@@ -44,6 +48,7 @@ using f32x16 = float __attribute__((ext_vector_type(16)));
 using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
 
 constexpr int BN = 256;          // accumulator columns per tile
+constexpr int kColBlock = 8;     // column tiles per block of an expert's tile order
 
 // Tile geometry: a WGM x WGN grid of waves, each owning WTB 32-row token
 // blocks x WCB 32-column blocks; NST LDS stages of depth BK (32 or 64).
@@ -148,16 +153,34 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_bf16(
   const int wm = w / WGN, wn = w - (w / WGN) * WGN;
   const uint32_t lds_base = (uint32_t)(size_t)(lds_ptr_t)smem;
 
-  // ---- tile decode (XCD-aware: consecutive tile ids on one XCD)
+  // ---- tile decode.  Workgroups are dispatched to the 8 XCDs round robin
+  // (workgroup b runs on XCD b%8); ids are remapped so that each XCD takes a
+  // contiguous range of tiles (same expert, same token rows close together)
+  // and the tiles running at once on an XCD share operands in its L2.
   const int total = table[0] * NT;
   const int bid = blockIdx.x;
   if (bid >= total) return;
   const int q8 = total >> 3, r8 = total & 7;
   const int xcd = bid & 7, j = bid >> 3;
   const int L = xcd * q8 + (xcd < r8 ? xcd : r8) + j;
-  const int mt = L / NT, nt = L - mt * NT;
+  // Within an expert (c row tiles x NT column tiles, ids [first*NT,
+  // (first+c)*NT)), tiles run in blocks of kColBlock columns: block by block,
+  // row tile by row tile, column by column.  The c*kColBlock tiles of a block
+  // are consecutive ids, so they run together on one XCD and share both the
+  // token rows (across columns) and the weight slices (across row tiles).
+  const int m0 = L / NT;
+  const uint32_t head = (uint32_t)table[4 * (m0 + 1)];
+  const int first = table[4 * (m0 + 1) + 3];
+  const int c = tile_expert_tiles(head);
+  const int local = L - first * NT;
+  const int blk = local / (c * kColBlock);
+  const int inb = local - blk * (c * kColBlock);
+  const int bw = (NT - blk * kColBlock < kColBlock) ? NT - blk * kColBlock : kColBlock;
+  const int mt = first + inb / bw;
+  const int nt = blk * kColBlock + (inb - (inb / bw) * bw);
+  if (mt >= table[0]) return;   // only with a table cut at its capacity (inconsistent offsets)
   const int32_t* ent = table + 4 * (mt + 1);
-  const int e = ent[0], row0 = ent[1];
+  const int e = tile_expert((uint32_t)ent[0]), row0 = ent[1];
   const int nrows = ent[2] - row0;
   const int ncol0 = nt * (UP ? BN / 2 : BN);   // first output column of the tile
   // 32-row token blocks of this wave that hold any valid row (uniform per wave)
@@ -324,37 +347,47 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_bf16(
     }
   }
 
-  // ---- epilogue: lane holds, for token column lane%32 of block tb, output
-  // columns 8*(v/4) + 4*(lane/32) + v%4 of block cb (v = accumulator index).
+  // ---- epilogue: the tile goes through LDS so that global stores are whole
+  // rows.  A lane holds, for token row lane%32 of block tb, output columns
+  // 8*(v/4) + 4*(lane/32) + v%4 of block cb (v = accumulator index); it writes
+  // them as 8-byte pieces into a row-major bf16 tile whose 16-byte chunks are
+  // XOR-swizzled by row, then every thread stores 16-byte chunks of whole rows.
+  constexpr int OW = UP ? BN / 2 : BN;        // output columns per tile
+  constexpr int kRowBytes = OW * 2;
+  constexpr int kChunks = kRowBytes / 16;
+  static_assert(BM * kRowBytes <= G::kLds, "output tile must fit the stage buffers");
+  asm volatile("s_barrier" ::: "memory");     // every wave is done reading the last stage
 #pragma unroll
   for (int tb = 0; tb < WTB; ++tb) {
     const int rloc = wm * (WTB * 32) + tb * 32 + (lane & 31);
-    if (rloc >= nrows) continue;
-    uint16_t* crow = C + (int64_t)(row0 + rloc) * N;
-    if (UP) {
+    unsigned char* srow = smem + rloc * kRowBytes;
 #pragma unroll
-      for (int cb = 0; cb < kHalf; ++cb)
+    for (int cb = 0; cb < (UP ? kHalf : WCB); ++cb)
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const int col = ncol0 + wn * kHalf * 32 + cb * 32 + 8 * v4 + 4 * (lane >> 5);
-          if (col >= N) continue;
-          float h[4];
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int col = wn * (UP ? kHalf : WCB) * 32 + cb * 32 + 8 * v4 + 4 * (lane >> 5);
+        float h[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = silu_mul(acc[cb][tb][4 * v4 + r], acc[cb + kHalf][tb][4 * v4 + r]);
-          u32x2 pk = {dev::pack_bf16x2(h[0], h[1]), dev::pack_bf16x2(h[2], h[3])};
-          *reinterpret_cast<u32x2*>(crow + col) = pk;
-        }
-    } else {
+        for (int r = 0; r < 4; ++r)
+          h[r] = UP ? silu_mul(acc[cb][tb][4 * v4 + r], acc[cb + kHalf][tb][4 * v4 + r])
+                    : acc[cb][tb][4 * v4 + r];
+        const u32x2 pk = {dev::pack_bf16x2(h[0], h[1]), dev::pack_bf16x2(h[2], h[3])};
+        const int chunk = (col >> 3) ^ (rloc & (kChunks - 1));
+        *reinterpret_cast<u32x2*>(srow + chunk * 16 + ((col >> 2) & 1) * 8) = pk;
+      }
+  }
+  __syncthreads();
+  constexpr int kIters = BM * kChunks / G::kThreads;
+  static_assert(kIters * G::kThreads == BM * kChunks, "store split");
 #pragma unroll
-      for (int cb = 0; cb < WCB; ++cb)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const int col = ncol0 + wn * WCB * 32 + cb * 32 + 8 * v4 + 4 * (lane >> 5);
-          if (col >= N) continue;
-          u32x2 pk = {dev::pack_bf16x2(acc[cb][tb][4 * v4], acc[cb][tb][4 * v4 + 1]),
-                      dev::pack_bf16x2(acc[cb][tb][4 * v4 + 2], acc[cb][tb][4 * v4 + 3])};
-          *reinterpret_cast<u32x2*>(crow + col) = pk;
-        }
+  for (int i = 0; i < kIters; ++i) {
+    const int idx = tid + i * G::kThreads;
+    const int rloc = idx / kChunks, c = idx - (idx / kChunks) * kChunks;
+    const int col = ncol0 + c * 8;
+    if (rloc < nrows && col < N) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(
+          smem + rloc * kRowBytes + ((c ^ (rloc & (kChunks - 1))) * 16));
+      *reinterpret_cast<bf16x8*>(C + (int64_t)(row0 + rloc) * N + col) = v;
     }
   }
 }
@@ -395,7 +428,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
   const int rem = bid - mt * (kSub * NT);
   const int sub = rem / NT, nt = rem - (rem / NT) * NT;
   const int32_t* ent = table + 4 * (mt + 1);
-  const int e = ent[0], row0 = ent[1] + sub * TM;
+  const int e = tile_expert((uint32_t)ent[0]), row0 = ent[1] + sub * TM;
   const int nrows = (ent[2] - row0 < TM) ? ent[2] - row0 : TM;
   if (nrows <= 0) return;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;

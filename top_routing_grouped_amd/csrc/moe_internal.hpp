@@ -35,7 +35,12 @@ inline int64_t max_row_tiles(const Problem& p, int bm) {
 }
 
 // Tile table layout: int4 header {count, 0, 0, 0}, then one int4 per row
-// tile {expert, row_begin, row_end, 0}.
+// tile {expert | tiles_of_expert << 8, row_begin, row_end, first_tile_of_expert}.
+// An expert's row tiles are consecutive entries.  The packed word is read as
+// uint32: expert < 256 and tiles_of_expert <= 2^23 (T*K < 2^31).
+__host__ __device__ inline int tile_expert(uint32_t w) { return (int)(w & 255u); }
+__host__ __device__ inline int tile_expert_tiles(uint32_t w) { return (int)(w >> 8); }
+
 inline size_t tile_table_bytes(const Problem& p) {
   return (size_t)(max_row_tiles(p, kGemmBM) + 1) * 4 * sizeof(int32_t);
 }

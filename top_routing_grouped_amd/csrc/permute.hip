@@ -74,10 +74,10 @@ __device__ void write_tiles(int e, int off, int cnt, int start, int64_t max_tile
     int32_t* ent = table + 4 * (idx + 1);
     const int rb = off + i * kGemmBM;
     const int re = (rb + kGemmBM < off + cnt) ? rb + kGemmBM : off + cnt;
-    ent[0] = e;
+    ent[0] = (int32_t)((uint32_t)e | ((uint32_t)nt << 8));
     ent[1] = rb;
     ent[2] = re;
-    ent[3] = 0;
+    ent[3] = start;
   }
 }
 
