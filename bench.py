@@ -2,24 +2,35 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = one pass of the whole hot path over one batch (route -> permute
--> grouped GEMM up -> grouped GEMM down -> combine) on synthetic seeded
-inputs already resident in HBM.  The timed region runs K steps through the
-C ABI's step-wise entry points with HIP events between the stages on the
-stream the kernels run on (the same kernels moe_forward launches); the fused
-moe_forward is timed as well.  Prints one JSON line.
+One step = one pass of the whole hot path over one batch: moe_forward (route
+-> permute -> grouped GEMM up -> grouped GEMM down -> combine) on seeded
+synthetic inputs already resident in HBM.  Before every timed step a 1 GiB
+scratch buffer is rewritten so that neither L2 nor the 256 MB MALL holds the
+inputs (cold cache); each step is bracketed by HIP events on the stream the
+kernels run on, and `value` = T / median step time.  The same K steps are
+then run through the step-wise entry points with events between the stages
+(per-stage medians, same kernels), and both are repeated without the flush
+(warm, labelled as such).  Prints one JSON line.
 
 Extra modes (used for profiler runs):
     --calib-copy BYTES   only run a plain device-to-device copy of BYTES
                          (the reference kernel for scaling HBM counters).
+    --pmc-summary FETCH_DIR WRITE_DIR CALIB_FETCH_DIR CALIB_WRITE_DIR
+                         turn four rocprofv3 --pmc runs into the traffic
+                         summary under profiles/ (no GPU needed).
     --no-cpu-baseline    skip the oracle timing on the host cores.
+    --warm               skip the cache flush (profiling runs).
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -31,6 +42,10 @@ PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "MoE-layer fwd tokens/s; grouped-GEMM MFMA util; permute/combine HBM GB/s"
 DEFAULT_WORKLOAD = "qwen3_bf16"
+FLUSH_BYTES = 1 << 30
+GEMM_SOURCES = ("top_routing_grouped_amd/csrc/gemm.hip", "top_routing_grouped_amd/csrc/moe_internal.hpp")
+TRAFFIC_FILE = "profiles/gemm_up_traffic_{workload}.json"
+UP_KERNEL = "grouped_gemm_bf16<true"
 
 
 def parse():
@@ -43,9 +58,75 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens for the oracle timing (0 = pick automatically)")
     ap.add_argument("--calib-copy", type=int, default=0)
+    ap.add_argument("--pmc-summary", nargs=4, default=None)
+    ap.add_argument("--warm", action="store_true")
     return ap.parse_args()
 
 
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+# ---------------------------------------------------------------- counters
+def _pmc_per_dispatch(directory: str, counter: str, name_has: str | None):
+    """{dispatch: (kernel name, summed counter value)} from rocprofv3 CSVs."""
+    out = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                if name_has and name_has not in r["Kernel_Name"]:
+                    continue
+                key = (path, r["Dispatch_Id"])
+                name, v = out.get(key, (r["Kernel_Name"], 0.0))
+                out[key] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def pmc_summary(fetch_dir, write_dir, calib_fetch_dir, calib_write_dir, workload):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the up GEMM, scaled by
+    what the same counters read for a plain copy of known size."""
+    cf = _pmc_per_dispatch(calib_fetch_dir, "FETCH_SIZE", None)
+    cw = _pmc_per_dispatch(calib_write_dir, "WRITE_SIZE", None)
+    # the calibration run copies FLUSH_BYTES (--calib-copy 1073741824): the
+    # copy is the dispatch that fetches the most and writes the most
+    copy_fetch = max(v for _, v in cf.values()) * 1024.0
+    copy_write = max(v for _, v in cw.values()) * 1024.0
+    f_scale = FLUSH_BYTES / copy_fetch
+    w_scale = FLUSH_BYTES / copy_write
+    fu = [v for _, v in _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", UP_KERNEL).values()]
+    wu = [v for _, v in _pmc_per_dispatch(write_dir, "WRITE_SIZE", UP_KERNEL).values()]
+    fetch = statistics.mean(fu) * 1024.0 * f_scale
+    write = statistics.mean(wu) * 1024.0 * w_scale
+    rec = {"workload": workload, "kernel": "grouped_gemm_bf16<up>", "dispatches": [len(fu), len(wu)],
+           "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+           "traffic_bytes_per_launch": fetch + write,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "raw_fetch_kib_mean": statistics.mean(fu), "raw_write_kib_mean": statistics.mean(wu),
+           "gemm_source_sha256": gemm_source_hash()}
+    out = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload))
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def load_traffic(workload: str):
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("gemm_source_sha256") != gemm_source_hash():
+        return None                       # kernel changed since the counters were taken
+    return rec["traffic_bytes_per_launch"]
+
+
+# ---------------------------------------------------------------- helpers
 def calib_copy(nbytes: int) -> None:
     import torch
     n = nbytes // 4
@@ -57,33 +138,68 @@ def calib_copy(nbytes: int) -> None:
     print(json.dumps({"calib_copy_bytes": n * 4, "read_bytes": n * 4, "write_bytes": n * 4}))
 
 
-def cpu_baseline(inp, w, sample_tokens: int):
-    """Time the oracle (as it stands) on the first `sample_tokens` tokens."""
-    import numpy as np
-    from oracle import moe_oracle as mo
+def sha256_tensor(t) -> str:
+    import torch
+    v = t.detach().contiguous()
+    if v.dtype == torch.bfloat16:
+        v = v.view(torch.int16)
+    return hashlib.sha256(v.numpy().tobytes()).hexdigest()
+
+
+def blas_info():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            return infos[0].get("internal_api", "blas"), max(i.get("num_threads", 1) for i in infos)
     except Exception:  # noqa: BLE001 - informational only
-        threads = len(os.sched_getaffinity(0))
+        pass
+    return "unknown", len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(inp, w, sample_tokens: int):
+    """Time the oracle (as it stands) per stage on the first `sample_tokens`
+    tokens of the workload, all experts' weights."""
+    import numpy as np
+    from oracle import moe_oracle as mo
+    vendor, threads = blas_info()
     Ts = min(w.T, sample_tokens)
     X = inp["X"][:Ts].float().numpy()
     W_r = inp["W_r"].float().numpy()
     Wg, Wu, Wd = (inp[k].float().numpy() for k in ("W_gate", "W_up", "W_down"))
     bias = None if inp["bias"] is None else inp["bias"].numpy()
-    t0 = time.perf_counter()
-    out = mo.forward(X, W_r, Wg, Wu, Wd, w.K, w.capacity_factor, bias=bias)
-    dt = time.perf_counter() - t0
-    assert np.all(np.isfinite(out["Y"]))
+    t = [time.perf_counter()]
+    r = mo.route(X, W_r, w.K, bias=bias)
+    t.append(time.perf_counter())
+    meta = mo.permute(r["ids"], w.E, mo.capacity(Ts, w.K, w.E, w.capacity_factor))
+    t.append(time.perf_counter())
+    H, O = mo.grouped_ffn(X, meta["offsets"], meta["perm_token"], Wg, Wu, Wd)
+    t.append(time.perf_counter())
+    Y = mo.combine(O, r["gates"], meta["inv_slot"], d=X.shape[1])
+    t.append(time.perf_counter())
+    dt = t[-1] - t[0]
+    assert np.all(np.isfinite(Y))
     return {"value": Ts / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle forward (numpy fp64) on the first {Ts} of {w.T} tokens of "
-                      f"{w.name}, all {w.E} experts' weights; {dt:.2f} s wall",
-            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+            "sample": f"oracle forward (numpy fp64, BLAS {vendor}) on the first {Ts} of {w.T} "
+                      f"tokens of {w.name}, all {w.E} experts' weights; {dt:.2f} s wall",
+            "seconds": dt,
+            "stage_seconds": {"route": t[1] - t[0], "permute": t[2] - t[1],
+                              "grouped_ffn": t[3] - t[2], "combine": t[4] - t[3]},
+            "blas": vendor, "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def pct(xs, q):
+    s = sorted(xs)
+    i = min(len(s) - 1, max(0, int(round(q * (len(s) - 1)))))
+    return s[i]
+
+
+# ---------------------------------------------------------------- main
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the layer would shard as described in DESIGN.md, but no multi-GPU path exists)",
@@ -100,6 +216,8 @@ def main():
     torch.cuda.set_device(0)
     inp = mi.make_inputs(args.workload)
     w = inp["workload"]
+    hashes = {k: sha256_tensor(inp[k]) for k in ("X", "W_r", "W_gate", "W_up", "W_down", "bias")
+              if inp[k] is not None}
     dev = {k: (None if inp[k] is None else inp[k].cuda())
            for k in ("X", "W_r", "W_gate", "W_up", "W_down", "bias")}
     T, d, E, K, n = w.T, w.d, w.E, w.K, w.n
@@ -121,77 +239,99 @@ def main():
     ws_p = moe.workspace(desc, moe.MOE_WS_PERMUTE)
     ws_f = moe.workspace(desc, moe.MOE_WS_GROUPED_FFN)
     ws_fwd = moe.workspace(desc, moe.MOE_WS_FORWARD)
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev: ev[0].record(stream)
-        moe.moe_route(desc, dev["X"], dev["W_r"], dev["bias"], None, ids, gates)
-        if ev: ev[1].record(stream)
-        moe.moe_permute(desc, ids, counts, offsets, None, perm, inv, ws_p)
-        if ev: ev[2].record(stream)
-        moe.moe_grouped_gemm_up(desc, dev["X"], offsets, perm, dev["W_gate"], dev["W_up"], H, ws_f)
-        if ev: ev[3].record(stream)
-        moe.moe_grouped_gemm_down(desc_ready, H, offsets, dev["W_down"], O, ws_f)
-        if ev: ev[4].record(stream)
-        moe.moe_combine(desc, O, gates, inv, Y)
-        if ev: ev[5].record(stream)
-
-    for _ in range(args.warmup):
-        step()
+    def fused():
         moe.moe_forward(desc, dev["X"], dev["W_r"], dev["bias"], dev["W_gate"], dev["W_up"],
                         dev["W_down"], Y, ws_fwd)
+
+    def stepwise(ev):
+        ev[0].record(stream)
+        moe.moe_route(desc, dev["X"], dev["W_r"], dev["bias"], None, ids, gates)
+        ev[1].record(stream)
+        moe.moe_permute(desc, ids, counts, offsets, None, perm, inv, ws_p)
+        ev[2].record(stream)
+        moe.moe_grouped_gemm_up(desc, dev["X"], offsets, perm, dev["W_gate"], dev["W_up"], H, ws_f)
+        ev[3].record(stream)
+        moe.moe_grouped_gemm_down(desc_ready, H, offsets, dev["W_down"], O, ws_f)
+        ev[4].record(stream)
+        moe.moe_combine(desc, O, gates, inv, Y)
+        ev[5].record(stream)
+
+    def flush(i):
+        scratch.fill_(float(i))
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    for i in range(args.warmup):
+        stepwise([ev() for _ in range(6)])
+        fused()
     torch.cuda.synchronize()
     N = int(offsets[E].item())            # kept (token, expert) rows: fixed by the inputs
     active = int((counts > 0).sum().item())
 
-    # ---- timed region: K steps, events between stages
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    def run_fused(cold: bool):
+        evs = [(ev(), ev()) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            if cold:
+                flush(i)
+            evs[i][0].record(stream)
+            fused()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+    def run_stepwise(cold: bool):
+        evs = [[ev() for _ in range(6)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            if cold:
+                flush(i)
+            stepwise(evs[i])
+        torch.cuda.synchronize()
+        return [[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in evs]
+
+    cold = not args.warm
+    # ---- timed region: K fused steps
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    fused_ms = run_fused(cold)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    stage_ms = [0.0] * 5
-    total_ms = 0.0
-    for ev in evs:
-        for j in range(5):
-            stage_ms[j] += ev[j].elapsed_time(ev[j + 1])
-        total_ms += ev[0].elapsed_time(ev[5])
-    stage_ms = [x / args.steps for x in stage_ms]
-    ms_per_step = total_ms / args.steps
+    stage_ms = run_stepwise(cold)
+    warm_fused_ms = run_fused(False)
+    warm_stage_ms = run_stepwise(False)
 
-    # ---- fused entry point, same work
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    f0.record(stream)
-    for _ in range(args.steps):
-        moe.moe_forward(desc, dev["X"], dev["W_r"], dev["bias"], dev["W_gate"], dev["W_up"],
-                        dev["W_down"], Y, ws_fwd)
-    f1.record(stream)
-    torch.cuda.synchronize()
-    fused_ms = f0.elapsed_time(f1) / args.steps
+    med = statistics.median(fused_ms)
+    names = ["route", "permute", "gemm_up", "gemm_down", "combine"]
+    stage_med = {nm: statistics.median(x[j] for x in stage_ms) for j, nm in enumerate(names)}
+    stage_mean = {nm: statistics.mean(x[j] for x in stage_ms) for j, nm in enumerate(names)}
+    warm_stage_med = {nm: statistics.median(x[j] for x in warm_stage_ms) for j, nm in enumerate(names)}
 
     # ---- algorithmic work (no padding, no pre-gather, active experts only)
-    t_route, t_perm, t_up, t_down, t_comb = (x * 1e-3 for x in stage_ms)
+    t_route, t_perm, t_up, t_down, t_comb = (stage_med[k] * 1e-3 for k in names)
     route_bytes = T * d * s + d * E * s + T * K * 8
     perm_bytes = T * K * 4 + N * 4 + T * K * 4 + 2 * E * 4
     comb_bytes = N * d * s + T * K * 8 + T * d * s
     up_flops = 4.0 * N * d * n
     down_flops = 2.0 * N * n * d
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    up_tflops = up_flops / t_up / 1e12
+    t_up_mean = stage_mean["gemm_up"] * 1e-3
+    up_tflops = up_flops / t_up_mean / 1e12
     mfma_util = (up_flops + down_flops) / (t_up + t_down) / 1e12 / peak
-    value = T / (ms_per_step * 1e-3)
+    traffic = load_traffic(w.name) if w.dtype == "bf16" else None
 
     rec = {
         "metric": METRIC,
-        "value": value,
+        "value": T / (med * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": med,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -199,24 +339,33 @@ def main():
         "data": "synthetic: seeded torch.randn, weights N(0, 1/fan_in), see moe_inputs.py",
         "config": {"workload": w.name, "T": T, "d": d, "E": E, "K": K, "n": n,
                    "capacity_factor": w.capacity_factor, "kept_rows": N, "active_experts": active,
-                   "G": d / n, "rho": K / E, "eta": N / max(1, active)},
-        "fused_forward_ms": fused_ms,
-        "fused_tokens_per_s": T / (fused_ms * 1e-3),
+                   "G": d / n, "rho": K / E, "eta": N / max(1, active),
+                   "cache": "cold (1 GiB rewritten before every timed step)" if cold else "warm"},
+        "step_ms": {"median": med, "mean": statistics.mean(fused_ms), "p10": pct(fused_ms, 0.1),
+                    "p90": pct(fused_ms, 0.9)},
+        "warm": {"value": T / (statistics.median(warm_fused_ms) * 1e-3),
+                 "ms_per_step": statistics.median(warm_fused_ms),
+                 "stage_us": {k: v * 1e3 for k, v in warm_stage_med.items()}},
         "wall_s_timed_region": wall,
-        "stage_us": {"route": stage_ms[0] * 1e3, "permute": stage_ms[1] * 1e3,
-                     "gemm_up": stage_ms[2] * 1e3, "gemm_down": stage_ms[3] * 1e3,
-                     "combine": stage_ms[4] * 1e3},
+        "stage_us": {k: v * 1e3 for k, v in stage_med.items()},
+        "stepwise_ms_per_step": sum(stage_med.values()),
         "grouped_gemm_mfma_util": mfma_util,
         "gemm_up_tflops": up_tflops,
         "gemm_down_tflops": down_flops / t_down / 1e12,
         "route_GBps": route_bytes / t_route / 1e9,
         "permute_GBps": perm_bytes / t_perm / 1e9,
+        "route_permute_GBps": (route_bytes + perm_bytes) / (t_route + t_perm) / 1e9,
         "combine_GBps": comb_bytes / t_comb / 1e9,
+        "hbm_frac": {"route": route_bytes / t_route / 1e9 / PEAK_HBM_GBPS,
+                     "combine": comb_bytes / t_comb / 1e9 / PEAK_HBM_GBPS},
         "roofline": {"bound": "mfma", "achieved": up_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": up_tflops / peak, "traffic": None,
+                     "frac": up_tflops / peak, "traffic": traffic,
                      "kernel": "grouped_gemm_bf16<up> (gather + SwiGLU)",
                      "per_unit": "4*d*n flops per kept (token, expert) row",
-                     "units_per_launch": N},
+                     "units_per_launch": N,
+                     "timing": "mean of the cold step-wise up-stage events (includes the "
+                               "4 us tile-table kernel launched by the same call)"},
+        "input_sha256": hashes,
     }
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_tokens or min(T, 16384)
