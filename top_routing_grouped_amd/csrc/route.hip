@@ -6,15 +6,18 @@
 // over the selected experts.
 //
 // One workgroup = 64 tokens, 4 waves in a 2x2 grid over (32 tokens) x (half of
-// the padded expert range).  X rows stream from HBM straight into registers
-// in the MFMA A-operand layout (16 B per lane, 4 stages in flight); the
-// W_r[k0:k0+64, :] tile is staged in LDS in its natural [k][e] layout and
-// read with the gfx950 transpose load (ds_read_b64_tr_b16), so the weights
-// need no transpose in memory.  The 64 x E fp32 scores land in LDS, then
-// each 16-lane DPP row selects the top K of one token per pass (4 tokens per
-// row, interleaved for ILP) on order-preserving int32 keys: integer max / min
-// reductions need no NaN canonicalisation, and folding -0.0 into +0.0 before
-// keying makes the two zeros tie (then the lower id wins, as the oracle rules).
+// the padded expert range), 16x16x32 bf16 MFMA.  For E % 8 == 0 the X tile
+// (64 tokens x 64 k) and the W_r tile (64 k x E, natural [k][e] layout) of
+// each k-step go global -> LDS with global_load_lds_dwordx4 through 3-4
+// stages whose completion is counted with explicit vmcnt waits; the W_r tile
+// is read with the gfx950 transpose load (ds_read_b64_tr_b16), so the weights
+// need no transpose in memory, and both tiles are XOR-swizzled so that every
+// fragment read is bank-conflict free.  (Other E use a register-staged
+// variant.)  The 64 x E fp32 scores (+ bias) land in LDS, then each 16-lane
+// DPP row selects the top K of 4 tokens at once on order-preserving int32
+// keys: integer max / min reductions need no NaN canonicalisation, and
+// folding -0.0 into +0.0 before keying makes the two zeros tie (then the
+// lower id wins, as the oracle rules).
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -37,9 +40,11 @@ __device__ __forceinline__ int sort_key(float f) {
 __device__ __forceinline__ float key_value(int k) {
   return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
 }
+// Every lane of these patterns reads a valid lane of its row, so bound_ctrl
+// changes nothing and lets the compiler fold the move into the max/min/add.
 template <int CTRL>
 __device__ __forceinline__ int dpp(int x) {
-  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
 }
 // Butterfly over one 16-lane DPP row; every lane of the row ends with the result.
 __device__ __forceinline__ int row_max16(int x) {
@@ -70,8 +75,8 @@ __device__ __forceinline__ float row_sum16(float x) {
 // Round results go to ids (global) and, as values, back into the token's own
 // LDS row (no longer read) for the gate pass.
 template <int V>
-__device__ void topk_from_lds(float* L, int S, int64_t t0, int64_t T, int E, int K,
-                              int32_t* __restrict__ ids, float* __restrict__ gates) {
+__device__ __forceinline__ void topk_from_lds(float* L, int S, int64_t t0, int64_t T, int E, int K,
+                                              int32_t* __restrict__ ids, float* __restrict__ gates) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int q = lane >> 4;
@@ -86,23 +91,46 @@ __device__ void topk_from_lds(float* L, int S, int64_t t0, int64_t T, int E, int
   }
   int top[4];
   for (int k = 0; k < K; ++k) {
+    // the four tokens of a row are independent chains: keep them in one
+    // branch-free block so their DPP steps interleave
+    int m[4], cand[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      int m = key[r][0];
+      m[r] = key[r][0];
 #pragma unroll
-      for (int j = 1; j < V; ++j) m = max(m, key[r][j]);
-      m = row_max16(m);
-      int cand = 0x7FFFFFFF;
+      for (int j = 1; j < V; ++j) m[r] = max(m[r], key[r][j]);
+    }
 #pragma unroll
-      for (int j = V - 1; j >= 0; --j) cand = (key[r][j] == m) ? (i + 16 * j) : cand;
-      cand = row_min16(cand);
+    for (int r = 0; r < 4; ++r) m[r] = row_max16(m[r]);
+    // Candidate = lowest expert id whose key equals the row maximum, and the
+    // winner's key is retired.  Written with plain integer arithmetic (no
+    // compare masks), so the four chains need no scalar mask registers.
 #pragma unroll
-      for (int j = 0; j < V; ++j) key[r][j] = (i + 16 * j == cand) ? kRetired : key[r][j];
-      if (k == 0) top[r] = m;
-      const int tl = 16 * w + 4 * q + r;
-      if (i == 0) {
-        L[tl * S + k] = key_value(m);
-        if (t0 + tl < T) ids[(t0 + tl) * K + k] = cand;
+    for (int r = 0; r < 4; ++r) {
+      cand[r] = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const uint32_t ne = min((uint32_t)(key[r][j] ^ m[r]), 1u);   // 0 iff equal
+        cand[r] = min(cand[r], (int)((uint32_t)(i + 16 * j) | (ne << 30)));
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cand[r] = row_min16(cand[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const uint32_t keep = 0u - min((uint32_t)((i + 16 * j) ^ cand[r]), 1u);  // 0 iff winner
+        key[r][j] = (int)(((uint32_t)key[r][j] & keep) | ((uint32_t)kRetired & ~keep));
+      }
+      if (k == 0) top[r] = m[r];
+    }
+    if (i == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tl = 16 * w + 4 * q + r;
+        L[tl * S + k] = key_value(m[r]);
+        if (t0 + tl < T) ids[(t0 + tl) * K + k] = cand[r];
       }
     }
   }
@@ -125,21 +153,24 @@ __device__ void topk_from_lds(float* L, int S, int64_t t0, int64_t T, int E, int
 }
 
 // Shared tail: bias, optional export, selection.
-template <int V>
-__device__ void route_tail(float* L, int S, int64_t t0, int64_t T, int E, int K, int Epad,
+// PREPPED: the caller already added the bias and wrote -inf into the padding.
+template <int V, bool PREPPED = false>
+__device__ __forceinline__ void route_tail(float* L, int S, int64_t t0, int64_t T, int E, int K, int Epad,
                            const float* __restrict__ bias, float* __restrict__ logits,
                            int32_t* __restrict__ ids, float* __restrict__ gates) {
-  for (int idx = threadIdx.x; idx < kTok * Epad; idx += kThreads) {
-    const int r = idx / Epad, e = idx - (idx / Epad) * Epad;
-    float v = L[r * S + e];
-    if (e < E) {
-      if (bias) v += bias[e];
-    } else {
-      v = -__builtin_inff();
+  if (!PREPPED) {
+    for (int idx = threadIdx.x; idx < kTok * Epad; idx += kThreads) {
+      const int r = idx / Epad, e = idx - (idx / Epad) * Epad;
+      float v = L[r * S + e];
+      if (e < E) {
+        if (bias) v += bias[e];
+      } else {
+        v = -__builtin_inff();
+      }
+      L[r * S + e] = v;
     }
-    L[r * S + e] = v;
+    __syncthreads();
   }
-  __syncthreads();
   if (logits) {
     for (int idx = threadIdx.x; idx < kTok * E; idx += kThreads) {
       const int r = idx / E, e = idx - (idx / E) * E;
@@ -301,6 +332,202 @@ __global__ __launch_bounds__(kThreads, (NBW >= 8) ? 1 : 2) void route_bf16_kerne
   route_tail<2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates);
 }
 
+// ---------------------------------------------------------------- bf16 router, staged copies
+// For E % 8 == 0 (W_r rows are whole 16-byte chunks).  The X tile (64 tokens
+// x 64 k, 128-byte rows) and the W_r tile (64 k x Epad, natural [k][e]
+// layout) of each k-step go global -> LDS with global_load_lds_dwordx4;
+// NST stages keep NST-1 k-steps of copies in flight, and the copies are
+// counted with explicit vmcnt waits so no load ever waits on a later one.
+// Both tiles are XOR-swizzled at 16-byte granularity so that the X fragment
+// reads (ds_read_b128) and the W_r transpose reads are bank-conflict free.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16(const void* g, uint32_t lds_addr) {
+  // M0 = LDS destination base (+16 per lane); s_nop covers the M0 -> LDS-DMA
+  // hazard.  M0 is written only here in this kernel.
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// XOR applied to the 16-byte chunk index of W_r tile row r (CPR chunks per
+// row) so that a 16x16x32 transpose read touches every bank equally.
+template <int CPR>
+__device__ __forceinline__ int wr_swizzle(int r) {
+  if (CPR >= 16) return 2 * ((r & 3) + 4 * ((r >> 3) & 1));
+  if (CPR == 8) return 2 * (((r >> 1) & 1) + 2 * ((r >> 3) & 1));
+  return 2 * ((r >> 3) & 1);
+}
+
+template <int NBW>
+struct RouteGeo {
+  static constexpr int Epad = 32 * NBW;
+  static constexpr int NST = (NBW >= 8) ? 3 : 4;     // LDS stages (X tile + W_r tile each)
+  static constexpr int kX = kTok * kBK * 2;          // X tile bytes (8 KB)
+  static constexpr int kW = kBK * Epad * 2;          // W_r tile bytes
+  static constexpr int kStage = kX + kW;
+  static constexpr int S = Epad + 16;                // floats per score row
+  static constexpr int kLds = (NST * kStage > kTok * S * 4) ? NST * kStage : kTok * S * 4;
+  static constexpr int kXInstr = kX / 1024 / 4;      // copies per wave per tile (4 waves)
+  static constexpr int kWInstr = kW / 1024 / 4;
+  static constexpr int kInstr = kXInstr + kWInstr;
+  static constexpr int CPR = Epad / 8;               // 16-byte chunks per W_r tile row
+  static constexpr int kWRows = 64 / CPR;            // W_r rows per copy instruction
+};
+
+// Wait until at most `pending` stages (INSTR copies each) of this wave are in flight.
+template <int INSTR>
+__device__ __forceinline__ void wait_stages(int pending) {
+  if (pending >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * INSTR) : "memory");
+  else if (pending == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(INSTR) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int NBW>
+__global__ __launch_bounds__(kThreads, 1) void route_staged_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
+    float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
+    int d, int E, int K) {
+  using G = RouteGeo<NBW>;
+  constexpr int Epad = G::Epad, NST = G::NST, CPR = G::CPR;
+  constexpr int XI = G::kXInstr, WI = G::kWInstr;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  float* L = reinterpret_cast<float*>(smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const int64_t t0 = (int64_t)blockIdx.x * kTok;
+  const int KT = d / kBK;
+  const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)smem;
+
+  // X copies: instruction j = XI*w + i fills tile rows 8j + lane/8, slot
+  // lane%8 holding k chunk slot ^ ((row >> 1) & 7).  Rows past T repeat row T-1.
+  const uint16_t* xsrc[XI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int r = (w * XI + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    int64_t t = t0 + r;
+    if (t > T - 1) t = T - 1;
+    xsrc[i] = X + t * (int64_t)d + c * 8;
+  }
+  // W_r copies: instruction j = WI*w + i fills tile rows kWRows*j + lane/CPR,
+  // slot lane%CPR holding column chunk slot ^ wr_swizzle(row).  Chunks past E
+  // (padding) read chunk 0 of the same row: in bounds, and their scores are
+  // replaced by -inf before selection.
+  const uint16_t* wsrc[WI];
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int r = (w * WI + i) * G::kWRows + lane / CPR;
+    int c = (lane % CPR) ^ wr_swizzle<CPR>(r);
+    if (c * 8 >= E) c = 0;
+    wsrc[i] = Wr + (int64_t)r * E + c * 8;
+  }
+  // Every workgroup reads all of W_r; starting each one at a different
+  // k-step (rotated by its position among the workgroups of its XCD) spreads
+  // the reads of any moment over all of W_r instead of one 64-row tile.  The
+  // sum over k is then taken in a rotated but fixed order per token position.
+  const int rot = (int)((blockIdx.x >> 3) % (unsigned)KT);
+  auto issue = [&](int kt) {
+    const uint32_t base = lds_base + (uint32_t)((kt % NST) * G::kStage);
+    int kk = kt + rot;
+    if (kk >= KT) kk -= KT;
+#pragma unroll
+    for (int i = 0; i < XI; ++i) copy16(xsrc[i] + kk * kBK, base + (w * XI + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+      copy16(wsrc[i] + (int64_t)kk * kBK * E, base + G::kX + (w * WI + i) * 1024);
+  };
+
+  // fragment offsets.  X (16x16x32 A operand): lane -> token row lane%16,
+  // k chunk 4*ks + lane/16.  W_r (B operand, transpose read): lane group
+  // g = lane/16, s = lane%16 -> tile row 32*ks + 8g + s/4 (+4 for the upper
+  // half), column 16*nb + 4*(s%4) of this wave's expert range.
+  int xo[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r = wm * 32 + rb * 16 + (lane & 15);
+      const int c = 4 * ks + (lane >> 4);
+      xo[rb][ks] = r * 128 + ((c ^ ((r >> 1) & 7)) * 16);
+    }
+  const int g = lane >> 4, s4 = lane & 15;
+  int wo[NBW][2][2];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 32 * ks + 8 * g + (s4 >> 2) + 4 * h;
+        const int col = wn * 16 * NBW + nb * 16 + 4 * (s4 & 3);
+        wo[nb][ks][h] = G::kX + r * (Epad * 2) + (((col >> 3) ^ wr_swizzle<CPR>(r)) * 16) + (col & 7) * 2;
+      }
+
+  f32x4 acc[2][NBW];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < KT) issue(st);
+  for (int kt = 0; kt < KT; ++kt) {
+    // stage kt landed (own copies), then published to all waves; the barrier
+    // also tells every wave that stage kt-1 (the buffer refilled below) is free
+    const int issued = (kt + NST - 2 < KT - 1) ? kt + NST - 2 : KT - 1;
+    wait_stages<G::kInstr>(issued - kt);
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + NST - 1 < KT) issue(kt + NST - 1);
+    const unsigned char* S = smem + (kt % NST) * G::kStage;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 a[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) a[rb] = *reinterpret_cast<const bf16x8*>(S + xo[rb][ks]);
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(S + wo[nb][ks][0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(S + wo[nb][ks][1]));
+        const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b, acc[rb][nb], 0, 0, 0);
+      }
+    }
+  }
+
+  // scores (+ bias; -inf in the padding columns) -> LDS, reusing the stage
+  // buffers once every wave is done reading them
+  float bcol[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int col = wn * 16 * NBW + nb * 16 + (lane & 15);
+    bcol[nb] = (col < E) ? (bias ? bias[col] : 0.f) : -__builtin_inff();
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * 32 + rb * 16 + 4 * (lane >> 4) + r;
+        const int col = wn * 16 * NBW + nb * 16 + (lane & 15);
+        L[row * G::S + col] = (col < E) ? acc[rb][nb][r] + bcol[nb] : bcol[nb];
+      }
+  __syncthreads();
+  route_tail<2 * NBW, true>(L, G::S, t0, T, E, K, Epad, bias, logits, ids, gates);
+}
+
 // ---------------------------------------------------------------- fp32 router (plain FMA)
 template <int NBW>
 __global__ __launch_bounds__(kThreads) void route_f32_kernel(
@@ -329,11 +556,16 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
                             float* logits, int32_t* ids, float* gates, hipStream_t s) {
   const dim3 grid((unsigned)((p.T + kTok - 1) / kTok));
   if (p.bf16) {
-    if (p.E % 8 == 0)
-      hipLaunchKernelGGL((route_bf16_kernel<NBW, true>), grid, dim3(kThreads), 0, s,
+    if (p.E % 8 == 0) {
+      auto* kern = route_staged_kernel<NBW>;
+      const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 RouteGeo<NBW>::kLds);
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL(kern, grid, dim3(kThreads), (size_t)RouteGeo<NBW>::kLds, s,
                          (const uint16_t*)X, (const uint16_t*)W_r, bias, logits, ids, gates, p.T,
                          p.d, p.E, p.K);
-    else
+    } else
       hipLaunchKernelGGL((route_bf16_kernel<NBW, false>), grid, dim3(kThreads), 0, s,
                          (const uint16_t*)X, (const uint16_t*)W_r, bias, logits, ids, gates, p.T,
                          p.d, p.E, p.K);
