@@ -18,50 +18,90 @@ using f32x4 = float __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kTokPerBlock = kThreads / 64;
 
-// bf16: 8 elements per 16-byte chunk; KU = k unroll (loads in flight per chunk).
-template <int KU>
+// bf16, 8 elements per 16-byte chunk.  The token index is wave-uniform; each
+// group of 8 slots and gates is read with one vector load and broadcast with
+// readlane, so they live in scalar registers.  A lane owns CB chunks of the row
+// (64 lanes x CB x 16 bytes = 2048 bf16 with CB = 4) and issues the loads of
+// all of them for 8 experts at once -- one memory round trip per token row
+// block -- then accumulates in k order.  Dropped assignments point their
+// load at a kept row of the same token (no extra HBM traffic) and are left
+// out of the sum by a select, so the load sequence has no branches.
+template <int CB>
 __global__ __launch_bounds__(kThreads) void combine_bf16(const uint16_t* __restrict__ O,
                                                         const float* __restrict__ gates,
                                                         const int32_t* __restrict__ inv,
                                                         uint16_t* __restrict__ Y, int64_t T, int d,
                                                         int K) {
+  constexpr int KG = 8;                       // experts per load group
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  const int64_t t = (int64_t)__builtin_amdgcn_readfirstlane(
+      (int)(blockIdx.x * kTokPerBlock + (threadIdx.x >> 6)));
   if (t >= T) return;
   const int nchunk = d / 8;
   const int32_t* tinv = inv + t * K;
   const float* tg = gates + t * K;
-  for (int c = lane; c < nchunk; c += 64) {
-    float acc[8];
+  for (int c0 = 0; c0 < nchunk; c0 += 64 * CB) {
+    int fallback = 0;                         // a kept row of this token (row 0 if none yet)
+    float acc[CB][8];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) acc[v] = 0.f;
-    for (int k0 = 0; k0 < K; k0 += KU) {
-      u32x4 o[KU];
-      float gk[KU];
-      bool ok[KU];
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int u = 0; u < KU; ++u) {
-        const int k = k0 + u;
-        const int s = (k < K) ? tinv[k] : -1;
-        ok[u] = s >= 0;
-        gk[u] = ok[u] ? tg[k] : 0.f;
-        o[u] = ok[u] ? *reinterpret_cast<const u32x4*>(O + (int64_t)s * d + c * 8)
-                     : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int v = 0; v < 8; ++v) acc[cb][v] = 0.f;
+    int cc[CB];
 #pragma unroll
-      for (int u = 0; u < KU; ++u) {
-        if (!ok[u]) continue;
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = c0 + 64 * cb + lane;
+      cc[cb] = (c < nchunk) ? c : 0;
+    }
+    for (int k0 = 0; k0 < K; k0 += KG) {
+      int sl[KG];
+      float gk[KG];
+      bool ok[KG];
+      {
+        // lane u (mod KG) loads entry k0+u (clamped), then every value is
+        // broadcast: one memory round trip for the group's metadata
+        const int kk = (k0 + (lane & (KG - 1)) < K) ? k0 + (lane & (KG - 1)) : K - 1;
+        const int ms = tinv[kk];
+        const float mg = tg[kk];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          acc[2 * h] = fmaf(gk[u], dev::bf16_bits_to_f32(o[u][h] & 0xFFFFu), acc[2 * h]);
-          acc[2 * h + 1] = fmaf(gk[u], dev::bf16_bits_to_f32(o[u][h] >> 16), acc[2 * h + 1]);
+        for (int u = 0; u < KG; ++u) {
+          sl[u] = __builtin_amdgcn_readlane(ms, u);
+          gk[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mg), u));
+          ok[u] = (k0 + u < K) && sl[u] >= 0;
         }
       }
-    }
-    u32x4 out;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) out[h] = dev::pack_bf16x2(acc[2 * h], acc[2 * h + 1]);
-    *reinterpret_cast<u32x4*>(Y + t * (int64_t)d + c * 8) = out;
+      for (int u = KG - 1; u >= 0; --u) fallback = ok[u] ? sl[u] : fallback;
+#pragma unroll
+      for (int u = 0; u < KG; ++u) sl[u] = ok[u] ? sl[u] : fallback;
+      u32x4 o[KG][CB];
+#pragma unroll
+      for (int u = 0; u < KG; ++u)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          o[u][cb] = *reinterpret_cast<const u32x4*>(O + (int64_t)sl[u] * d + cc[cb] * 8);
+#pragma unroll
+      for (int u = 0; u < KG; ++u)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const float lo = fmaf(gk[u], dev::bf16_bits_to_f32(o[u][cb][h] & 0xFFFFu), acc[cb][2 * h]);
+            const float hi = fmaf(gk[u], dev::bf16_bits_to_f32(o[u][cb][h] >> 16), acc[cb][2 * h + 1]);
+            acc[cb][2 * h] = ok[u] ? lo : acc[cb][2 * h];
+            acc[cb][2 * h + 1] = ok[u] ? hi : acc[cb][2 * h + 1];
+          }
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = c0 + 64 * cb + lane;
+      if (c < nchunk) {
+        u32x4 out;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) out[h] = dev::pack_bf16x2(acc[cb][2 * h], acc[cb][2 * h + 1]);
+        *reinterpret_cast<u32x4*>(Y + t * (int64_t)d + c * 8) = out;
+      }
+    }
   }
 }
 
