@@ -32,8 +32,9 @@
  * - Supported shapes: 1 <= E <= 256, 1 <= K <= E, d and n multiples of 64
  *   (MOE_ERR_UNSUPPORTED otherwise), T >= 0 (T = 0 is a successful no-op).
  * - Identical inputs give bitwise identical outputs; moe_forward gives the
- *   same bits as the step-wise chain route -> permute -> grouped_ffn ->
- *   combine.  Calls sharing a workspace must not overlap in time.
+ *   same bits as the step-wise chain route_ws -> permute -> grouped_ffn ->
+ *   combine with the same flags.  Calls sharing a workspace must not overlap
+ *   in time.
  * - Inputs must be finite; non-finite values give unspecified routing.
  */
 #ifndef MOE_MI355X_H
@@ -78,13 +79,28 @@ typedef struct {
  * up-projection).  Other entry points reject the bit. */
 #define MOE_FLAG_TILE_TABLE_READY 1u
 
+/* desc->flags bits for moe_grouped_gemm_up / moe_grouped_gemm_down /
+ * moe_grouped_ffn / moe_forward (bf16 only; at most one of the two): which
+ * grouped-GEMM kernels run.  By default a batch that averages at most 64 rows
+ * per expert (T*K <= 64*E, e.g. decode) runs the weight-streaming kernels --
+ * one workgroup per expert and column block, reading each active expert's
+ * weights once per 64 rows -- and larger batches run the 256x256-tiled
+ * kernels.  Both give results within the documented tolerance of each other
+ * (they round the same fp32 sums; summation order differs).  The skinny
+ * kernels need no tile table: MOE_FLAG_TILE_TABLE_READY is then ignored. */
+#define MOE_FLAG_GEMM_TILED 2u
+#define MOE_FLAG_GEMM_SKINNY 4u
+
 /* Workspace selectors for moe_workspace_size. */
-enum { MOE_WS_PERMUTE = 0, MOE_WS_GROUPED_FFN = 1, MOE_WS_FORWARD = 2 };
+enum { MOE_WS_PERMUTE = 0, MOE_WS_GROUPED_FFN = 1, MOE_WS_FORWARD = 2, MOE_WS_ROUTE = 3 };
 
 /* ---------------------------------------------------------------- host only
  * These make no HIP call and can run on a machine without a GPU. */
 
-/* Checks the description (counts, supported shapes, flags, capacity factor). */
+/* Checks the description (counts, supported shapes, capacity factor, and that
+ * flags holds only defined bits, not both GEMM-path bits).  Each device entry
+ * point further rejects the bits it does not take.  The host-only queries
+ * below ignore the flags. */
 moe_status moe_validate(const moe_desc* desc);
 
 /* Per-expert cap C (see moe_desc.capacity_factor); exact integer arithmetic. */
@@ -112,6 +128,17 @@ const char* moe_last_error(void);
  * lower expert id and -0.0 equals +0.0.  gates[t,:] sum to 1. */
 moe_status moe_route(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
                      float* logits, int32_t* topk_ids, float* topk_gates, void* stream);
+
+/* moe_route with a workspace (MOE_WS_ROUTE bytes; may be 0, then ws may be
+ * NULL).  For batches whose 64-token blocks cannot fill the GPU (bf16, E a
+ * multiple of 8) the router's k range is split over several workgroups per
+ * block, whose fp32 partial scores go to ws and are summed in a fixed order
+ * by a second kernel, then selected as in moe_route.  The scores may differ
+ * from moe_route's in the last bits (another summation order); ids and gates
+ * always follow the scores this call computed (and exports). */
+moe_status moe_route_ws(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
+                        float* logits, int32_t* topk_ids, float* topk_gates, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* Steps 3-5 (histogram, capacity cut in token order, exclusive scan, scatter).
  *   topk_ids[T,K] int32 with distinct ids in [0,E) per token (as moe_route writes;

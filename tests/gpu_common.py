@@ -29,7 +29,11 @@ def device_inputs(inp):
     return out
 
 
-def run_stepwise(dev, K, cf):
+# grouped-GEMM kernel choice for a test: the library's own choice, or forced
+GEMM_PATHS = {"auto": 0, "tiled": moe.MOE_FLAG_GEMM_TILED, "skinny": moe.MOE_FLAG_GEMM_SKINNY}
+
+
+def run_stepwise(dev, K, cf, gemm_flags=0):
     """route -> permute -> grouped_ffn -> combine through the C ABI."""
     X, W_gate = dev["X"], dev["W_gate"]
     T, d = X.shape
@@ -38,7 +42,8 @@ def run_stepwise(dev, K, cf):
     desc = moe.make_desc(T, d, E, K, n, dtype, cf)
     ids, gates, logits = moe.route(X, dev["W_r"], K, bias=dev["bias"], want_logits=True, n=n)
     meta = moe.permute(desc, ids)
-    H, O = moe.grouped_ffn(desc, X, meta["offsets"], meta["perm_token"], W_gate, dev["W_up"],
+    ffn_desc = moe.make_desc(T, d, E, K, n, dtype, cf, flags=gemm_flags)
+    H, O = moe.grouped_ffn(ffn_desc, X, meta["offsets"], meta["perm_token"], W_gate, dev["W_up"],
                            dev["W_down"])
     Y = moe.combine(desc, O, gates, meta["inv_slot"])
     res = {"desc": desc, "ids": ids, "gates": gates, "logits": logits, "H": H, "O": O, "Y": Y}

@@ -23,7 +23,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     lib = moe.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -47,14 +47,16 @@ def test_validate_cases():
         (moe.make_desc(16, 128, 300, 2, 256), moe.MOE_ERR_UNSUPPORTED),        # E > 256
         (moe.make_desc(16, 100, 8, 2, 256), moe.MOE_ERR_UNSUPPORTED),          # d % 64
         (moe.make_desc(16, 128, 8, 2, 96), moe.MOE_ERR_UNSUPPORTED),           # n % 64
-        (moe.make_desc(16, 128, 8, 2, 256, flags=1), moe.MOE_ERR_INVALID_ARG),  # flag not allowed here
-        (moe.make_desc(16, 128, 8, 2, 256, flags=2), moe.MOE_ERR_INVALID_ARG),  # unknown flag
+        (moe.make_desc(16, 128, 8, 2, 256, flags=6), moe.MOE_ERR_INVALID_ARG),  # both GEMM paths
+        (moe.make_desc(16, 128, 8, 2, 256, flags=8), moe.MOE_ERR_INVALID_ARG),  # undefined bit
         (moe.make_desc(16, 128, 8, 2, 256, capacity_factor=float("nan")), moe.MOE_ERR_INVALID_ARG),
         (moe.make_desc(16, 128, 8, 2, 256, capacity_factor=float("inf")), moe.MOE_ERR_INVALID_ARG),
         (moe.make_desc(2 ** 30, 128, 8, 2, 256), moe.MOE_ERR_UNSUPPORTED),     # T*K >= 2^31
     ]
     for desc, want in bad:
         assert moe.moe_validate(desc) == want
+    for f in (1, 2, 4, 5):                                    # defined bits are valid
+        assert moe.moe_validate(moe.make_desc(16, 128, 8, 2, 256, flags=f)) == moe.MOE_OK
     d = moe.make_desc(16, 128, 8, 2, 256)
     d.dtype = 7
     assert moe.moe_validate(d) == moe.MOE_ERR_INVALID_ARG
@@ -116,6 +118,47 @@ def test_device_entry_points_reject_bad_arguments_without_enqueueing():
     ws = moe.moe_workspace_size(zero, moe.MOE_WS_FORWARD)
     assert lib.moe_forward(ctypes.byref(zero), A, A, None, A, A, A, A, A, ws + 256, None) == moe.MOE_OK
     assert lib.moe_route(ctypes.byref(zero), A, A, None, None, A, A, None) == moe.MOE_OK
+
+
+def test_route_workspace_only_for_small_batches():
+    # a decode-sized batch splits the router's k range (partials in the workspace)
+    small = moe.make_desc(64, 4096, 256, 8, 512)
+    assert moe.moe_workspace_size(small, moe.MOE_WS_ROUTE) >= 64 * 256 * 4 * 2
+    # a batch that fills the GPU with 64-token blocks needs none
+    big = moe.make_desc(16384, 2048, 128, 8, 768)
+    assert moe.moe_workspace_size(big, moe.MOE_WS_ROUTE) == 0
+    # fp32 and E not a multiple of 8 never split
+    assert moe.moe_workspace_size(moe.make_desc(64, 4096, 256, 8, 512, "fp32"), moe.MOE_WS_ROUTE) == 0
+    assert moe.moe_workspace_size(moe.make_desc(64, 4096, 250, 8, 512), moe.MOE_WS_ROUTE) == 0
+    # the forward workspace holds the partials too
+    assert moe.moe_workspace_size(small, moe.MOE_WS_FORWARD) > moe.moe_workspace_size(small, moe.MOE_WS_ROUTE)
+    lib = moe.lib()
+    A = ctypes.c_void_p(1 << 20)
+    assert lib.moe_route_ws(ctypes.byref(small), A, A, None, None, A, A, None, 0, None) == \
+        moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route_ws(ctypes.byref(moe.make_desc(0, 4096, 256, 8, 512)), A, A, None, None, A, A,
+                            None, 0, None) == moe.MOE_OK
+
+
+def test_gemm_path_flags_are_checked_per_entry_point():
+    lib = moe.lib()
+    A = ctypes.c_void_p(1 << 20)
+    T0 = lambda flags: moe.make_desc(0, 128, 8, 2, 128, flags=flags)   # T = 0: checks only
+    both = moe.MOE_FLAG_GEMM_TILED | moe.MOE_FLAG_GEMM_SKINNY
+    for f in (moe.MOE_FLAG_GEMM_TILED, moe.MOE_FLAG_GEMM_SKINNY,
+              moe.MOE_FLAG_GEMM_SKINNY | moe.MOE_FLAG_TILE_TABLE_READY):
+        assert lib.moe_grouped_ffn(ctypes.byref(T0(f)), A, A, A, A, A, A, A, A, A, 1 << 20, None) == moe.MOE_OK
+    assert lib.moe_grouped_ffn(ctypes.byref(T0(both)), A, A, A, A, A, A, A, A, A, 1 << 20, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert b"exclusive" in lib.moe_last_error()
+    ws = moe.moe_workspace_size(T0(0), moe.MOE_WS_FORWARD) + 256
+    assert lib.moe_forward(ctypes.byref(T0(moe.MOE_FLAG_GEMM_SKINNY)), A, A, None, A, A, A, A, A, ws,
+                           None) == moe.MOE_OK
+    # the tile-table bit belongs to the grouped entry points only; route takes no flags
+    assert lib.moe_forward(ctypes.byref(T0(moe.MOE_FLAG_TILE_TABLE_READY)), A, A, None, A, A, A, A,
+                           A, ws, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(T0(moe.MOE_FLAG_GEMM_TILED)), A, A, None, None, A, A, None) == \
+        moe.MOE_ERR_INVALID_ARG
 
 
 def test_missing_library_fails_loudly(monkeypatch):

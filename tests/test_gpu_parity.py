@@ -19,17 +19,17 @@ import torch
 import moe_inputs as mi
 import top_routing_grouped_amd as moe
 from oracle import moe_oracle as mo
-from gpu_common import (TOL, check_permutation, check_routing, device_inputs, f32np, intnp,
-                        run_stepwise)
+from gpu_common import (GEMM_PATHS, TOL, check_permutation, check_routing, device_inputs, f32np,
+                        intnp, run_stepwise)
 
 pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _full_check(inp, K, cf, dtype):
+def _full_check(inp, K, cf, dtype, gemm_flags=0):
     dev = device_inputs(inp)
-    res = run_stepwise(dev, K, cf)
+    res = run_stepwise(dev, K, cf, gemm_flags)
     torch.cuda.synchronize()
     T, E = inp["X"].shape[0], inp["W_r"].shape[1]
     L_gpu, ids, gates = check_routing(res, inp, K)
@@ -50,7 +50,7 @@ def _full_check(inp, K, cf, dtype):
     assert np.all(Y_gpu[dropped] == 0.0)
     # the fused entry point gives the same bits as the step-wise chain
     Y_fused = moe.forward(dev["X"], dev["W_r"], dev["W_gate"], dev["W_up"], dev["W_down"], K, cf,
-                          bias=dev["bias"])
+                          bias=dev["bias"], flags=gemm_flags)
     torch.cuda.synchronize()
     assert torch.equal(Y_fused, res["Y"])
     return res, ref
@@ -77,6 +77,49 @@ def test_small_layer_parity(T, d, E, K, n, dtype, cf, bias):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     inp = mi.draw(T, d, E, n, tdt, seed=7, bias=bias)
     _full_check(inp, K, cf, dtype)
+
+
+# Both grouped-GEMM kernels on every bf16 shape above, whichever the library
+# would pick: the weight-streaming one (passes of 64 rows, 128-column blocks,
+# partial last block in the down projection) and the 256x256-tiled one.
+@pytest.mark.parametrize("path", ["tiled", "skinny"])
+@pytest.mark.parametrize("T,d,E,K,n,dtype,cf,bias", [c for c in SMALL if c[5] == "bf16"])
+def test_small_layer_parity_each_gemm_path(T, d, E, K, n, dtype, cf, bias, path):
+    print(f"case T={T} d={d} E={E} K={K} n={n} {dtype} cf={cf} bias={bias} path={path}",
+          flush=True)
+    inp = mi.draw(T, d, E, n, torch.bfloat16, seed=11, bias=bias)
+    _full_check(inp, K, cf, dtype, GEMM_PATHS[path])
+
+
+@pytest.mark.parametrize("T,d,E,K", [(64, 4096, 256, 8), (100, 512, 64, 6), (700, 1024, 16, 2),
+                                     (3, 256, 128, 8)])
+def test_route_with_and_without_k_split(T, d, E, K):
+    """moe_route_ws splits the k range over workgroups for small batches;
+    moe_route never does.  Both: logits within tolerance of fp64, ids and
+    gates exactly those of the device's own logits."""
+    print(f"case route split T={T} d={d} E={E} K={K}", flush=True)
+    inp = mi.draw(T, d, E, 64, torch.bfloat16, seed=3, bias="zipf")
+    dev = device_inputs(inp)
+    desc = moe.make_desc(T, d, E, K, 64, "bf16")
+    assert moe.moe_workspace_size(desc, moe.MOE_WS_ROUTE) > 0      # these shapes split
+    for split in (True, False):
+        ids, gates, logits = moe.route(dev["X"], dev["W_r"], K, bias=dev["bias"], want_logits=True,
+                                       split=split)
+        torch.cuda.synchronize()
+        check_routing({"ids": ids, "gates": gates, "logits": logits}, inp, K)
+
+
+def test_gemm_paths_agree_on_skewed_decode():
+    """Decode-sized batch with one expert taking most rows (several 64-row
+    passes in the weight-streaming kernel): both kernels against the oracle
+    and against each other."""
+    print("case decode skew T=160 d=256 E=64 K=2 n=192", flush=True)
+    inp = mi.draw(160, 256, 64, 192, torch.bfloat16, seed=5, bias="zipf")
+    res_t, ref = _full_check(inp, 2, 0.0, "bf16", GEMM_PATHS["tiled"])
+    res_s, _ = _full_check(inp, 2, 0.0, "bf16", GEMM_PATHS["skinny"])
+    assert int(np.max(ref["counts"])) > 128          # more than two passes for that expert
+    N = int(ref["offsets"][-1])
+    assert mo.rel_l2(f32np(res_s["O"])[:N], f32np(res_t["O"])[:N]) <= TOL["bf16"]
 
 
 def test_zero_router_gives_lowest_ids_and_uniform_gates():

@@ -30,7 +30,10 @@ MOE_BF16 = 1
 MOE_WS_PERMUTE = 0
 MOE_WS_GROUPED_FFN = 1
 MOE_WS_FORWARD = 2
+MOE_WS_ROUTE = 3
 MOE_FLAG_TILE_TABLE_READY = 1
+MOE_FLAG_GEMM_TILED = 2
+MOE_FLAG_GEMM_SKINNY = 4
 
 
 class MoeError(RuntimeError):
@@ -68,6 +71,7 @@ _SIGNATURES = {
     "moe_max_rows": [_DP, ctypes.POINTER(ctypes.c_int64)],
     "moe_workspace_size": [_DP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
     "moe_route": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "moe_route_ws": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "moe_permute": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "moe_grouped_gemm_up": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "moe_grouped_gemm_down": [_DP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
@@ -155,6 +159,12 @@ def moe_route(desc, X, W_r, bias, logits, ids, gates, stream=None):
                            _p(gates), _stream(stream)), "moe_route")
 
 
+def moe_route_ws(desc, X, W_r, bias, logits, ids, gates, ws, stream=None):
+    _check(lib().moe_route_ws(ctypes.byref(desc), _p(X), _p(W_r), _p(bias), _p(logits), _p(ids),
+                              _p(gates), _p(ws), ws.numel() * ws.element_size(),
+                              _stream(stream)), "moe_route_ws")
+
+
 def moe_permute(desc, ids, counts, offsets, raw_counts, perm_token, inv_slot, ws, stream=None):
     _check(lib().moe_permute(ctypes.byref(desc), _p(ids), _p(counts), _p(offsets), _p(raw_counts),
                              _p(perm_token), _p(inv_slot), _p(ws), ws.numel() * ws.element_size(),
@@ -208,8 +218,10 @@ def workspace(desc: MoeDesc, entry: int, device="cuda"):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def route(X, W_r, K, bias=None, want_logits=False, n=64):
-    """Steps 1-2.  Returns (ids [T,K] int32, gates [T,K] fp32, logits [T,E] fp32 or None)."""
+def route(X, W_r, K, bias=None, want_logits=False, n=64, split=True):
+    """Steps 1-2.  Returns (ids [T,K] int32, gates [T,K] fp32, logits [T,E] fp32 or None).
+    split=True goes through moe_route_ws (k split for small batches, as
+    moe_forward does); split=False through moe_route."""
     import torch
     T, d = X.shape
     E = W_r.shape[1]
@@ -217,7 +229,10 @@ def route(X, W_r, K, bias=None, want_logits=False, n=64):
     ids = torch.empty((T, K), dtype=torch.int32, device=X.device)
     gates = torch.empty((T, K), dtype=torch.float32, device=X.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=X.device) if want_logits else None
-    moe_route(desc, X, W_r, bias, logits, ids, gates)
+    if split:
+        moe_route_ws(desc, X, W_r, bias, logits, ids, gates, workspace(desc, MOE_WS_ROUTE, X.device))
+    else:
+        moe_route(desc, X, W_r, bias, logits, ids, gates)
     return ids, gates, logits
 
 
@@ -258,10 +273,12 @@ def combine(desc: MoeDesc, O, gates, inv_slot):
     return Y
 
 
-def forward(X, W_r, W_gate, W_up, W_down, K, capacity_factor=0.0, bias=None, ws=None):
-    """Steps 1-8 in one library call.  Returns Y [T, d]."""
+def forward(X, W_r, W_gate, W_up, W_down, K, capacity_factor=0.0, bias=None, ws=None, flags=0):
+    """Steps 1-8 in one library call.  Returns Y [T, d].  `flags` may pick the
+    grouped-GEMM kernels (MOE_FLAG_GEMM_TILED / MOE_FLAG_GEMM_SKINNY)."""
     import torch
     desc = _desc_for(X, W_gate, K, capacity_factor)
+    desc.flags = int(flags)
     if ws is None:
         ws = workspace(desc, MOE_WS_FORWARD, X.device)
     Y = torch.empty_like(X)

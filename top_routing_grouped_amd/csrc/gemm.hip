@@ -89,24 +89,6 @@ static_assert(ProdGeo::BM == kGemmBM, "tile table rows must match the kernel til
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// 16-byte global -> LDS copy per lane; LDS destination = M0 + 16*lane.
-// Issued through asm so the compiler does not treat every later LDS read as
-// aliasing the copy (it would wait for all copies in flight, which would
-// collapse the stage pipeline); completion is awaited explicitly with
-// s_waitcnt vmcnt before the barrier that publishes a stage.  The asm has no
-// register outputs; the s_nop covers the M0-write -> LDS-DMA hazard.
-// M0 is written only here in these kernels (no other instruction reads it),
-// so clobbering it is safe; silence the generic reserved-register warning.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_addr)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
 // s_waitcnt lgkmcnt(0) as a builtin (gfx9 encoding: vmcnt and expcnt left at
 // their maxima), so the compiler's own wait tracking sees it.
 constexpr int kWaitLds = 0xC07F;
@@ -236,11 +218,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_bf16(
     const uint32_t As = lds_base + (uint32_t)((kt % kStages) * kStageBytes);
     const uint32_t Bs = As + kAStage;
 #pragma unroll
-    for (int i = 0; i < kAInstr; ++i) dma16(asrc[i] + kt * BK, As + (w * kAInstr + i) * 1024);
+    for (int i = 0; i < kAInstr; ++i) dev::lds_copy16(asrc[i] + kt * BK, As + (w * kAInstr + i) * 1024);
 #pragma unroll
     for (int i = 0; i < kBInstr; ++i) {
       const int jb = w * kBInstr + i;
-      dma16(bsrc[jb & 1] + (int64_t)(kt * BK + 2 * jb) * N, Bs + jb * 1024);
+      dev::lds_copy16(bsrc[jb & 1] + (int64_t)(kt * BK + 2 * jb) * N, Bs + jb * 1024);
     }
   };
 

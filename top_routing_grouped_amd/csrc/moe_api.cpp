@@ -44,6 +44,8 @@ int64_t exact_capacity(int64_t T, int64_t K, int64_t E, double cf) {
 moe_status check_desc(const moe_desc* d, uint32_t allowed_flags = 0) {
   if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is NULL");
   if (d->flags & ~allowed_flags) return fail(MOE_ERR_INVALID_ARG, "desc->flags has a bit this entry point does not accept");
+  if ((d->flags & MOE_FLAG_GEMM_TILED) && (d->flags & MOE_FLAG_GEMM_SKINNY))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_FLAG_GEMM_TILED and MOE_FLAG_GEMM_SKINNY are exclusive");
   if (d->T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0");
   if (d->E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1");
   if (d->K < 1 || d->K > d->E) return fail(MOE_ERR_INVALID_ARG, "K must satisfy 1 <= K <= E");
@@ -57,6 +59,13 @@ moe_status check_desc(const moe_desc* d, uint32_t allowed_flags = 0) {
   if (d->T * (int64_t)d->K >= ((int64_t)1 << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*K must stay below 2^31 (int32 slots)");
   return MOE_OK;
+}
+
+constexpr uint32_t kGemmFlags = MOE_FLAG_TILE_TABLE_READY | MOE_FLAG_GEMM_TILED | MOE_FLAG_GEMM_SKINNY;
+constexpr uint32_t kAllFlags = kGemmFlags;   // every defined bit (host-only queries accept them all)
+
+bool skinny(const moe::Problem& p, const moe_desc* d) {
+  return moe::use_skinny(p, d->flags, MOE_FLAG_GEMM_TILED, MOE_FLAG_GEMM_SKINNY);
 }
 
 moe::Problem make_problem(const moe_desc* d) {
@@ -92,6 +101,7 @@ PermuteWs carve_permute(const moe::Problem& p, unsigned char* base) {
 }
 
 struct ForwardWs {
+  float* route_partial;
   int32_t* ids;
   float* gates;
   int32_t* inv;
@@ -113,6 +123,8 @@ ForwardWs carve_forward(const moe::Problem& p, unsigned char* base) {
     return ptr;
   };
   const size_t tk = (size_t)p.T * p.K;
+  const size_t rp = moe::route_partial_bytes(p);
+  w.route_partial = rp ? reinterpret_cast<float*>(take(rp)) : nullptr;
   w.ids = reinterpret_cast<int32_t*>(take(tk * 4));
   w.gates = reinterpret_cast<float*>(take(tk * 4));
   w.inv = reinterpret_cast<int32_t*>(take(tk * 4));
@@ -172,25 +184,25 @@ extern "C" {
 
 moe_status moe_validate(const moe_desc* desc) {
   g_last_error.clear();
-  return check_desc(desc);
+  return check_desc(desc, kAllFlags);
 }
 
 moe_status moe_capacity(const moe_desc* desc, int64_t* C_out) {
-  MOE_TRY(check_desc(desc));
+  MOE_TRY(check_desc(desc, kAllFlags));
   if (!C_out) return fail(MOE_ERR_INVALID_ARG, "C_out is NULL");
   *C_out = make_problem(desc).C;
   return MOE_OK;
 }
 
 moe_status moe_max_rows(const moe_desc* desc, int64_t* rows_out) {
-  MOE_TRY(check_desc(desc));
+  MOE_TRY(check_desc(desc, kAllFlags));
   if (!rows_out) return fail(MOE_ERR_INVALID_ARG, "rows_out is NULL");
   *rows_out = make_problem(desc).rows_max;
   return MOE_OK;
 }
 
 moe_status moe_workspace_size(const moe_desc* desc, int32_t entry, size_t* bytes) {
-  MOE_TRY(check_desc(desc));
+  MOE_TRY(check_desc(desc, kAllFlags));
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
   const moe::Problem p = make_problem(desc);
   switch (entry) {
@@ -202,6 +214,9 @@ moe_status moe_workspace_size(const moe_desc* desc, int32_t entry, size_t* bytes
       return MOE_OK;
     case MOE_WS_FORWARD:
       *bytes = carve_forward(p, nullptr).bytes;
+      return MOE_OK;
+    case MOE_WS_ROUTE:
+      *bytes = align_up(moe::route_partial_bytes(p));
       return MOE_OK;
     default:
       return fail(MOE_ERR_INVALID_ARG, "unknown workspace selector");
@@ -230,7 +245,25 @@ moe_status moe_route(const moe_desc* desc, const void* X, const void* W_r, const
   MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {topk_ids, "topk_ids"}, {topk_gates, "topk_gates"}},
                      {{bias, "bias"}, {logits, "logits"}}));
   const moe::Problem p = make_problem(desc);
+  return hip_status(moe::launch_route(p, X, W_r, bias, logits, topk_ids, topk_gates, nullptr,
+                                      (hipStream_t)stream),
+                    "route launch");
+}
+
+moe_status moe_route_ws(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
+                        float* logits, int32_t* topk_ids, float* topk_gates, void* ws,
+                        size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc));
+  if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
+  MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {topk_ids, "topk_ids"}, {topk_gates, "topk_gates"}},
+                     {{bias, "bias"}, {logits, "logits"}, {ws, "ws"}}));
+  const moe::Problem p = make_problem(desc);
+  const size_t need = moe::route_partial_bytes(p);
+  if (need && (!ws || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_ROUTE)");
   return hip_status(moe::launch_route(p, X, W_r, bias, logits, topk_ids, topk_gates,
+                                      need ? static_cast<float*>(ws) : nullptr,
                                       (hipStream_t)stream),
                     "route launch");
 }
@@ -255,7 +288,7 @@ moe_status moe_grouped_gemm_up(const moe_desc* desc, const void* X, const int32_
                                const int32_t* perm_token, const void* W_gate, const void* W_up,
                                void* H, void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  MOE_TRY(check_desc(desc, MOE_FLAG_TILE_TABLE_READY));
+  MOE_TRY(check_desc(desc, kGemmFlags));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
   MOE_TRY(check_ptrs({{X, "X"}, {offsets, "offsets"}, {perm_token, "perm_token"},
                       {W_gate, "W_gate"}, {W_up, "W_up"}, {H, "H"}},
@@ -264,6 +297,9 @@ moe_status moe_grouped_gemm_up(const moe_desc* desc, const void* X, const int32_
   if (!ws || ws_bytes < moe::tile_table_bytes(p))
     return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_GROUPED_FFN)");
   hipStream_t s = (hipStream_t)stream;
+  if (skinny(p, desc))
+    return hip_status(moe::launch_gemm_up_skinny(p, X, perm_token, offsets, W_gate, W_up, H, s),
+                      "grouped GEMM (up, weight-streaming) launch");
   int32_t* table = static_cast<int32_t*>(ws);
   if (!(desc->flags & MOE_FLAG_TILE_TABLE_READY))
     MOE_TRY(hip_status(moe::launch_tile_table(p, offsets, table, s), "tile table launch"));
@@ -275,13 +311,16 @@ moe_status moe_grouped_gemm_down(const moe_desc* desc, const void* H, const int3
                                  const void* W_down, void* O, void* ws, size_t ws_bytes,
                                  void* stream) {
   g_last_error.clear();
-  MOE_TRY(check_desc(desc, MOE_FLAG_TILE_TABLE_READY));
+  MOE_TRY(check_desc(desc, kGemmFlags));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
   MOE_TRY(check_ptrs({{H, "H"}, {offsets, "offsets"}, {W_down, "W_down"}, {O, "O"}}, {{ws, "ws"}}));
   const moe::Problem p = make_problem(desc);
   if (!ws || ws_bytes < moe::tile_table_bytes(p))
     return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_GROUPED_FFN)");
   hipStream_t s = (hipStream_t)stream;
+  if (skinny(p, desc))
+    return hip_status(moe::launch_gemm_down_skinny(p, H, offsets, W_down, O, s),
+                      "grouped GEMM (down, weight-streaming) launch");
   int32_t* table = static_cast<int32_t*>(ws);
   if (!(desc->flags & MOE_FLAG_TILE_TABLE_READY))
     MOE_TRY(hip_status(moe::launch_tile_table(p, offsets, table, s), "tile table launch"));
@@ -293,7 +332,7 @@ moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* o
                            const void* W_down, void* H, void* O, void* ws, size_t ws_bytes,
                            void* stream) {
   g_last_error.clear();
-  MOE_TRY(check_desc(desc, MOE_FLAG_TILE_TABLE_READY));
+  MOE_TRY(check_desc(desc, kGemmFlags));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
   MOE_TRY(check_ptrs({{X, "X"}, {offsets, "offsets"}, {perm_token, "perm_token"},
                       {W_gate, "W_gate"}, {W_up, "W_up"}, {W_down, "W_down"}, {H, "H"}, {O, "O"}},
@@ -302,6 +341,12 @@ moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* o
   if (!ws || ws_bytes < moe::tile_table_bytes(p))
     return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_GROUPED_FFN)");
   hipStream_t s = (hipStream_t)stream;
+  if (skinny(p, desc)) {
+    MOE_TRY(hip_status(moe::launch_gemm_up_skinny(p, X, perm_token, offsets, W_gate, W_up, H, s),
+                       "grouped GEMM (up, weight-streaming) launch"));
+    return hip_status(moe::launch_gemm_down_skinny(p, H, offsets, W_down, O, s),
+                      "grouped GEMM (down, weight-streaming) launch");
+  }
   int32_t* table = static_cast<int32_t*>(ws);
   if (!(desc->flags & MOE_FLAG_TILE_TABLE_READY))
     MOE_TRY(hip_status(moe::launch_tile_table(p, offsets, table, s), "tile table launch"));
@@ -325,7 +370,7 @@ moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, con
                        const void* W_gate, const void* W_up, const void* W_down, void* Y,
                        void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  MOE_TRY(check_desc(desc));
+  MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_GEMM_SKINNY));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
   MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {W_gate, "W_gate"}, {W_up, "W_up"},
                       {W_down, "W_down"}, {Y, "Y"}},
@@ -336,12 +381,20 @@ moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, con
     return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_FORWARD)");
   hipStream_t s = (hipStream_t)stream;
   ForwardWs w = carve_forward(p, static_cast<unsigned char*>(ws));
-  MOE_TRY(hip_status(moe::launch_route(p, X, W_r, bias, nullptr, w.ids, w.gates, s), "route launch"));
+  MOE_TRY(hip_status(moe::launch_route(p, X, W_r, bias, nullptr, w.ids, w.gates, w.route_partial, s),
+                     "route launch"));
   MOE_TRY(run_permute(p, w.ids, w.counts, w.offsets, nullptr, w.perm, w.inv, w.permute, w.table, s));
-  MOE_TRY(hip_status(moe::launch_gemm_up(p, X, w.perm, w.table, W_gate, W_up, w.H, s),
-                     "grouped GEMM (up) launch"));
-  MOE_TRY(hip_status(moe::launch_gemm_down(p, w.H, w.table, W_down, w.O, s),
-                     "grouped GEMM (down) launch"));
+  if (skinny(p, desc)) {
+    MOE_TRY(hip_status(moe::launch_gemm_up_skinny(p, X, w.perm, w.offsets, W_gate, W_up, w.H, s),
+                       "grouped GEMM (up, weight-streaming) launch"));
+    MOE_TRY(hip_status(moe::launch_gemm_down_skinny(p, w.H, w.offsets, W_down, w.O, s),
+                       "grouped GEMM (down, weight-streaming) launch"));
+  } else {
+    MOE_TRY(hip_status(moe::launch_gemm_up(p, X, w.perm, w.table, W_gate, W_up, w.H, s),
+                       "grouped GEMM (up) launch"));
+    MOE_TRY(hip_status(moe::launch_gemm_down(p, w.H, w.table, W_down, w.O, s),
+                       "grouped GEMM (down) launch"));
+  }
   return hip_status(moe::launch_combine(p, w.O, w.gates, w.inv, Y, s), "combine launch");
 }
 

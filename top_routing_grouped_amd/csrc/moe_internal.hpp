@@ -46,8 +46,34 @@ inline size_t tile_table_bytes(const Problem& p) {
 }
 
 // ---------------------------------------------------------------- launchers
+// 16-column blocks per router wave: the padded expert range is 32*route_nbw.
+inline int route_nbw(int E) {
+  const int n = (E + 31) / 32;
+  return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8;
+}
+
+// Router k split for small batches (bf16, E % 8 == 0): up to 16 workgroups
+// per 64-token block so that the blocks fill the chip, at least two 64-deep
+// k-steps each.  1 = no split.
+inline int route_ksplit(const Problem& p) {
+  if (!p.bf16 || p.E % 8 != 0) return 1;
+  const int64_t blocks = (p.T + 63) / 64;
+  const int64_t kt = p.d / 64;
+  int64_t k = 256 / (blocks > 0 ? blocks : 1);
+  if (k > 16) k = 16;
+  if (k > kt / 2) k = kt / 2;
+  return k > 1 ? (int)k : 1;
+}
+// Bytes of the router's split-k partial scores (0 when there is no split).
+inline size_t route_partial_bytes(const Problem& p) {
+  const int ks = route_ksplit(p);
+  if (ks <= 1) return 0;
+  return (size_t)ks * (size_t)p.T * (size_t)(32 * route_nbw(p.E)) * sizeof(float);
+}
+
+// partial: route_partial_bytes(p) of workspace, or NULL (no k split).
 hipError_t launch_route(const Problem& p, const void* X, const void* W_r, const float* bias,
-                        float* logits, int32_t* ids, float* gates, hipStream_t s);
+                        float* logits, int32_t* ids, float* gates, float* partial, hipStream_t s);
 
 hipError_t launch_histogram(const Problem& p, const int32_t* ids, int32_t* blockcnt,
                             hipStream_t s);
@@ -66,6 +92,25 @@ hipError_t launch_gemm_up(const Problem& p, const void* X, const int32_t* perm,
                           hipStream_t s);
 hipError_t launch_gemm_down(const Problem& p, const void* H, const int32_t* table,
                             const void* W_down, void* O, hipStream_t s);
+
+// Weight-streaming grouped GEMMs for few rows per expert (one workgroup per
+// expert and column block; no tile table).
+hipError_t launch_gemm_up_skinny(const Problem& p, const void* X, const int32_t* perm,
+                                 const int32_t* offsets, const void* W_gate, const void* W_up,
+                                 void* H, hipStream_t s);
+hipError_t launch_gemm_down_skinny(const Problem& p, const void* H, const int32_t* offsets,
+                                   const void* W_down, void* O, hipStream_t s);
+
+// Which grouped-GEMM kernels a bf16 problem runs: the tiled ones, or the
+// weight-streaming ones when the batch averages at most kSkinnyRows rows per
+// expert (T*K <= kSkinnyRows*E), unless a flag forces one of them.
+constexpr int64_t kSkinnyRows = 64;
+inline bool use_skinny(const Problem& p, uint32_t flags, uint32_t tiled_flag, uint32_t skinny_flag) {
+  if (!p.bf16) return false;
+  if (flags & tiled_flag) return false;
+  if (flags & skinny_flag) return true;
+  return p.T * (int64_t)p.K <= kSkinnyRows * p.E;
+}
 
 hipError_t launch_combine(const Problem& p, const void* O, const float* gates,
                           const int32_t* inv_slot, void* Y, hipStream_t s);
@@ -93,6 +138,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // fence would also wait for in-flight global->LDS prefetches).  The memory
 // clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// 16-byte global -> LDS copy per lane; LDS destination = M0 + 16*lane, so a
+// wave fills 1 KB at lds_addr (wave-uniform).  Issued through asm so the
+// compiler does not treat later LDS reads as aliasing the copy (it would wait
+// for every copy in flight); completion is awaited with explicit s_waitcnt
+// vmcnt.  The asm has no register outputs; s_nop covers the M0-write ->
+// LDS-DMA hazard.  M0 is written only by these copies in the kernels that
+// use them, so clobbering it is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 }  // namespace dev
 }  // namespace moe

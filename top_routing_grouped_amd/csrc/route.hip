@@ -340,17 +340,6 @@ __global__ __launch_bounds__(kThreads, (NBW >= 8) ? 1 : 2) void route_bf16_kerne
 // counted with explicit vmcnt waits so no load ever waits on a later one.
 // Both tiles are XOR-swizzled at 16-byte granularity so that the X fragment
 // reads (ds_read_b128) and the W_r transpose reads are bank-conflict free.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16(const void* g, uint32_t lds_addr) {
-  // M0 = LDS destination base (+16 per lane); s_nop covers the M0 -> LDS-DMA
-  // hazard.  M0 is written only here in this kernel.
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_addr)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // XOR applied to the 16-byte chunk index of W_r tile row r (CPR chunks per
 // row) so that a 16x16x32 transpose read touches every bank equally.
@@ -385,11 +374,15 @@ __device__ __forceinline__ void wait_stages(int pending) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// With ksplit > 1 the k range is split over gridDim.y workgroups per token
+// block (for batches too small to fill the chip): each writes its raw fp32
+// partial scores to partial[ks][T][Epad]; route_sum_kernel and
+// route_select_kernel finish.
 template <int NBW>
 __global__ __launch_bounds__(kThreads, 1) void route_staged_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
-    int d, int E, int K) {
+    int d, int E, int K, int ksplit, float* __restrict__ partial) {
   using G = RouteGeo<NBW>;
   constexpr int Epad = G::Epad, NST = G::NST, CPR = G::CPR;
   constexpr int XI = G::kXInstr, WI = G::kWInstr;
@@ -401,7 +394,9 @@ __global__ __launch_bounds__(kThreads, 1) void route_staged_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
   const int64_t t0 = (int64_t)blockIdx.x * kTok;
-  const int KT = d / kBK;
+  const int KT_all = d / kBK;
+  const int kt0 = (int)(((int64_t)blockIdx.y * KT_all) / ksplit);   // this workgroup's k-steps
+  const int KT = (int)(((int64_t)(blockIdx.y + 1) * KT_all) / ksplit) - kt0;
   const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)smem;
 
   // X copies: instruction j = XI*w + i fills tile rows 8j + lane/8, slot
@@ -431,16 +426,17 @@ __global__ __launch_bounds__(kThreads, 1) void route_staged_kernel(
   // k-step (rotated by its position among the workgroups of its XCD) spreads
   // the reads of any moment over all of W_r instead of one 64-row tile.  The
   // sum over k is then taken in a rotated but fixed order per token position.
-  const int rot = (int)((blockIdx.x >> 3) % (unsigned)KT);
+  const int rot = (ksplit > 1) ? 0 : (int)((blockIdx.x >> 3) % (unsigned)KT);
   auto issue = [&](int kt) {
     const uint32_t base = lds_base + (uint32_t)((kt % NST) * G::kStage);
     int kk = kt + rot;
     if (kk >= KT) kk -= KT;
+    kk += kt0;
 #pragma unroll
-    for (int i = 0; i < XI; ++i) copy16(xsrc[i] + kk * kBK, base + (w * XI + i) * 1024);
+    for (int i = 0; i < XI; ++i) dev::lds_copy16(xsrc[i] + kk * kBK, base + (w * XI + i) * 1024);
 #pragma unroll
     for (int i = 0; i < WI; ++i)
-      copy16(wsrc[i] + (int64_t)kk * kBK * E, base + G::kX + (w * WI + i) * 1024);
+      dev::lds_copy16(wsrc[i] + (int64_t)kk * kBK * E, base + G::kX + (w * WI + i) * 1024);
   };
 
   // fragment offsets.  X (16x16x32 A operand): lane -> token row lane%16,
@@ -505,6 +501,20 @@ __global__ __launch_bounds__(kThreads, 1) void route_staged_kernel(
     }
   }
 
+  if (ksplit > 1) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t t = t0 + wm * 32 + rb * 16 + 4 * (lane >> 4) + r;
+          const int col = wn * 16 * NBW + nb * 16 + (lane & 15);
+          if (t < T) partial[((int64_t)blockIdx.y * T + t) * Epad + col] = acc[rb][nb][r];
+        }
+    return;
+  }
+
   // scores (+ bias; -inf in the padding columns) -> LDS, reusing the stage
   // buffers once every wave is done reading them
   float bcol[NBW];
@@ -526,6 +536,50 @@ __global__ __launch_bounds__(kThreads, 1) void route_staged_kernel(
       }
   __syncthreads();
   route_tail<2 * NBW, true>(L, G::S, t0, T, E, K, Epad, bias, logits, ids, gates);
+}
+
+// Split-k finish, part 1: partial[0] = sum over ks of partial[ks], in ks
+// order (a fixed order: the result does not depend on which workgroup of the
+// router finished first).  One float4 of scores per thread, spread over as
+// many workgroups as the T x Epad scores need.
+__global__ __launch_bounds__(kThreads) void route_sum_kernel(float* __restrict__ partial,
+                                                             int ksplit, int64_t n4) {
+  using f4 = float __attribute__((ext_vector_type(4)));
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n4) return;
+  f4* P = reinterpret_cast<f4*>(partial);
+  f4 v = P[i];
+  int ks = 1;
+  for (; ks + 4 <= ksplit; ks += 4) {        // four loads in flight, summed in order
+    const f4 a = P[(int64_t)ks * n4 + i], b = P[(int64_t)(ks + 1) * n4 + i];
+    const f4 c = P[(int64_t)(ks + 2) * n4 + i], d = P[(int64_t)(ks + 3) * n4 + i];
+    v += a;
+    v += b;
+    v += c;
+    v += d;
+  }
+  for (; ks < ksplit; ++ks) v += P[(int64_t)ks * n4 + i];
+  P[i] = v;
+}
+
+// Split-k finish, part 2: the summed scores of 64 tokens, plus bias (-inf in
+// the padding), then the same selection tail as the unsplit router.
+template <int NBW>
+__global__ __launch_bounds__(kThreads) void route_select_kernel(
+    const float* __restrict__ scores, const float* __restrict__ bias, float* __restrict__ logits,
+    int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T, int E, int K) {
+  constexpr int Epad = 32 * NBW, S = Epad + 16;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float* L = reinterpret_cast<float*>(smem);
+  const int64_t t0 = (int64_t)blockIdx.x * kTok;
+  for (int idx = threadIdx.x; idx < kTok * Epad; idx += kThreads) {
+    const int r = idx / Epad, e = idx - (idx / Epad) * Epad;
+    const int64_t t = (t0 + r < T) ? t0 + r : T - 1;
+    const float v = scores[t * Epad + e];
+    L[r * S + e] = (e < E) ? (bias ? v + bias[e] : v) : -__builtin_inff();
+  }
+  __syncthreads();
+  route_tail<2 * NBW, true>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates);
 }
 
 // ---------------------------------------------------------------- fp32 router (plain FMA)
@@ -553,18 +607,36 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
 
 template <int NBW>
 hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, const float* bias,
-                            float* logits, int32_t* ids, float* gates, hipStream_t s) {
+                            float* logits, int32_t* ids, float* gates, float* partial,
+                            hipStream_t s) {
   const dim3 grid((unsigned)((p.T + kTok - 1) / kTok));
   if (p.bf16) {
     if (p.E % 8 == 0) {
+      const int ksplit = partial ? route_ksplit(p) : 1;
       auto* kern = route_staged_kernel<NBW>;
-      const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 RouteGeo<NBW>::kLds);
+      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           RouteGeo<NBW>::kLds);
       if (err != hipSuccess) return err;
-      hipLaunchKernelGGL(kern, grid, dim3(kThreads), (size_t)RouteGeo<NBW>::kLds, s,
-                         (const uint16_t*)X, (const uint16_t*)W_r, bias, logits, ids, gates, p.T,
-                         p.d, p.E, p.K);
+      hipLaunchKernelGGL(kern, dim3(grid.x, (unsigned)ksplit), dim3(kThreads),
+                         (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)W_r,
+                         bias, logits, ids, gates, p.T, p.d, p.E, p.K, ksplit, partial);
+      if (ksplit > 1) {
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        const int64_t n4 = p.T * (int64_t)(32 * NBW) / 4;
+        hipLaunchKernelGGL(route_sum_kernel, dim3((unsigned)((n4 + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, s, partial, ksplit, n4);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        constexpr int kSelLds = kTok * (32 * NBW + 16) * 4;
+        auto* sel = route_select_kernel<NBW>;
+        err = hipFuncSetAttribute(reinterpret_cast<const void*>(sel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kSelLds);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(sel, grid, dim3(kThreads), (size_t)kSelLds, s, partial, bias, logits,
+                           ids, gates, p.T, p.E, p.K);
+      }
     } else
       hipLaunchKernelGGL((route_bf16_kernel<NBW, false>), grid, dim3(kThreads), 0, s,
                          (const uint16_t*)X, (const uint16_t*)W_r, bias, logits, ids, gates, p.T,
@@ -579,12 +651,12 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
 }  // namespace
 
 hipError_t launch_route(const Problem& p, const void* X, const void* W_r, const float* bias,
-                        float* logits, int32_t* ids, float* gates, hipStream_t s) {
-  const int nbw = (p.E + 31) / 32;
-  if (nbw <= 1) return launch_route_nbw<1>(p, X, W_r, bias, logits, ids, gates, s);
-  if (nbw <= 2) return launch_route_nbw<2>(p, X, W_r, bias, logits, ids, gates, s);
-  if (nbw <= 4) return launch_route_nbw<4>(p, X, W_r, bias, logits, ids, gates, s);
-  return launch_route_nbw<8>(p, X, W_r, bias, logits, ids, gates, s);
+                        float* logits, int32_t* ids, float* gates, float* partial, hipStream_t s) {
+  const int nbw = route_nbw(p.E);
+  if (nbw <= 1) return launch_route_nbw<1>(p, X, W_r, bias, logits, ids, gates, partial, s);
+  if (nbw <= 2) return launch_route_nbw<2>(p, X, W_r, bias, logits, ids, gates, partial, s);
+  if (nbw <= 4) return launch_route_nbw<4>(p, X, W_r, bias, logits, ids, gates, partial, s);
+  return launch_route_nbw<8>(p, X, W_r, bias, logits, ids, gates, partial, s);
 }
 
 }  // namespace moe
