@@ -1,5 +1,5 @@
 /*
- * moe.h -- C ABI of the MI355X (gfx950) MoE layer forward library.
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer library (forward and backward).
  *
  * The layer, for tokens X[T,d] and E SwiGLU experts of width n:
  *   1. router logits  l = X W_r (+ b)              (page "Routing-Free 与 OmniMoE", §1.1)
@@ -11,6 +11,7 @@
  *   6. grouped GEMM over the gathered token rows with a SwiGLU epilogue -> H
  *   7. second grouped GEMM -> O                     (SonicMoE article §3, §6.2, §6.3)
  *   8. gate-weighted combine back to token order -> Y  (SonicMoE article §1, §6.1)
+ * and, for training, its backward (SonicMoE article §6.1, §6.3, §6.4).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -30,7 +31,8 @@
  *   H, O and Y are rounded to desc->dtype (round to nearest even).
  * - Every device pointer must be 16-byte aligned (MOE_ERR_ALIGNMENT).
  * - Supported shapes: 1 <= E <= 256, 1 <= K <= E, d and n multiples of 64
- *   (MOE_ERR_UNSUPPORTED otherwise), T >= 0 (T = 0 is a successful no-op).
+ *   (MOE_ERR_UNSUPPORTED otherwise), T >= 0 (T = 0 is a successful no-op,
+ *   except that moe_backward then writes zero weight gradients).
  * - Identical inputs give bitwise identical outputs; moe_forward gives the
  *   same bits as the step-wise chain route_ws -> permute -> grouped_ffn ->
  *   combine with the same flags.  Calls sharing a workspace must not overlap
@@ -91,8 +93,32 @@ typedef struct {
 #define MOE_FLAG_GEMM_TILED 2u
 #define MOE_FLAG_GEMM_SKINNY 4u
 
-/* Workspace selectors for moe_workspace_size. */
-enum { MOE_WS_PERMUTE = 0, MOE_WS_GROUPED_FFN = 1, MOE_WS_FORWARD = 2, MOE_WS_ROUTE = 3 };
+/* Workspace selectors for moe_workspace_size.  MOE_WS_SAVED is the state
+ * that moe_forward_train keeps for moe_backward (see moe_saved_layout);
+ * MOE_WS_BACKWARD is moe_backward's scratch. */
+enum {
+  MOE_WS_PERMUTE = 0,
+  MOE_WS_GROUPED_FFN = 1,
+  MOE_WS_FORWARD = 2,
+  MOE_WS_ROUTE = 3,
+  MOE_WS_SAVED = 4,
+  MOE_WS_BACKWARD = 5
+};
+
+/* Byte offsets of the fields of the saved state (the `saved` buffer of
+ * moe_forward_train / moe_backward), each 256-byte aligned.  Apart from the
+ * internal tile table, every field is what the step-wise entry points write. */
+typedef struct {
+  size_t logits;      /* fp32 [T][E]: the scores the selection was made on */
+  size_t topk_ids;    /* int32 [T][K] */
+  size_t topk_gates;  /* fp32 [T][K] */
+  size_t inv_slot;    /* int32 [T][K] (-1: dropped by the cap) */
+  size_t perm_token;  /* int32 [T*K]; the first offsets[E] entries are valid */
+  size_t counts;      /* int32 [E] */
+  size_t offsets;     /* int32 [E+1] */
+  size_t preact;      /* bf16 [moe_max_rows][2n]: row s = (x W_gate[e] | x W_up[e]) of slot s */
+  size_t bytes;       /* total = moe_workspace_size(MOE_WS_SAVED) */
+} moe_saved_layout;
 
 /* ---------------------------------------------------------------- host only
  * These make no HIP call and can run on a machine without a GPU. */
@@ -112,6 +138,9 @@ moe_status moe_max_rows(const moe_desc* desc, int64_t* rows_out);
 
 /* Bytes of workspace that the entry point `entry` (MOE_WS_*) needs. */
 moe_status moe_workspace_size(const moe_desc* desc, int32_t entry, size_t* bytes);
+
+/* Field offsets of the saved state for this description. */
+moe_status moe_saved_layout_of(const moe_desc* desc, moe_saved_layout* out);
 
 /* Static description of a status code. */
 const char* moe_status_str(int32_t status);
@@ -184,6 +213,44 @@ moe_status moe_combine(const moe_desc* desc, const void* O, const float* topk_ga
 moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
                        const void* W_gate, const void* W_up, const void* W_down, void* Y,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- training (bf16 only)
+ * The SonicMoE article (§6.1) keeps, per kept slot, only what the backward
+ * cannot cheaply recompute: the routing metadata and the pre-activations
+ * x W_gate | x W_up; the SwiGLU activation A and the expert outputs O are
+ * never stored for the backward.  Both calls need desc->dtype == MOE_BF16
+ * (MOE_ERR_UNSUPPORTED otherwise) and take flags 0 or MOE_FLAG_GEMM_TILED:
+ * the training path always runs the 256x256-tiled GEMMs. */
+
+/* Forward that also fills `saved` (MOE_WS_SAVED bytes, layout in
+ * moe_saved_layout) for moe_backward.  ws: MOE_WS_FORWARD bytes (scratch, not
+ * needed afterwards).  Y has the same bits as moe_forward with
+ * MOE_FLAG_GEMM_TILED. */
+moe_status moe_forward_train(const moe_desc* desc, const void* X, const void* W_r,
+                             const float* bias, const void* W_gate, const void* W_up,
+                             const void* W_down, void* Y, void* saved, size_t saved_bytes,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Gradients of sum(Y * dY) for the layer that moe_forward_train ran with the
+ * same desc and inputs (X, W_r, W_gate, W_up, W_down unchanged since; `saved`
+ * as it wrote it).  SonicMoE article §6.4 ordering: per kept slot s of
+ * expert e (token t, gate g):
+ *   dA'[s] = dY[t] W_down[e]^T; dS[s] = <dA'[s], A[s]> with A = silu(Hg) Hu
+ *   recomputed from the saved pre-activations (no O or Y is formed);
+ *   dHg = g dA' Hu silu'(Hg), dHu = g dA' silu(Hg) in the GEMM's epilogue (§6.3);
+ *   dW_down[e] = sum_s (g A[s])^T dY[t];  dW_gate[e] | dW_up[e] = sum_s X[t]^T (dHg | dHu);
+ *   router: dg[t,k] = dS[slot] (0 when dropped), dl = softmax-over-the-K Jacobian
+ *   applied to dg (the selection itself has no gradient), dW_r = X^T dl;
+ *   dX[t] = sum over kept k of (dHg W_gate^T + dHu W_up^T)[slot] + dl[t] W_r^T.
+ *   dY[T,d], dX[T,d] bf16; dW_r[d,E], dW_gate/dW_up[E,d,n], dW_down[E,n,d] fp32
+ *   (every element written; bias gets no gradient).  Intermediates (dH, g A,
+ *   per-slot dX, dl) are rounded to bf16, sums run in fp32 in a fixed order,
+ *   so identical inputs give identical bits.  ws: MOE_WS_BACKWARD bytes.
+ *   T = 0 writes zero weight gradients. */
+moe_status moe_backward(const moe_desc* desc, const void* X, const void* W_r, const void* W_gate,
+                        const void* W_up, const void* W_down, const void* dY, const void* saved,
+                        size_t saved_bytes, void* dX, float* dW_r, float* dW_gate, float* dW_up,
+                        float* dW_down, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

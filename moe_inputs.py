@@ -12,6 +12,10 @@ bf16 workloads then cast each tensor to bfloat16 (round to nearest even).
 The skewed workload adds a per-expert router bias b_e = 1.5 * ln(1/(e+1))
 (float64, stored as float32); the decode workload reuses the fine-grained
 layer's weights and takes the first 64 rows of its X.
+
+Output gradients for the backward: dY[T,d] = randn (N(0,1)) from a CPU
+generator seeded with ``seed + 7919`` (a stream of its own, so the layer's
+tensors are the same with or without it), cast like the layer's tensors.
 """
 
 from __future__ import annotations
@@ -101,6 +105,12 @@ def make_inputs(name: str, seed: int = 0) -> dict:
         out = draw(w.T, w.d, w.E, w.n, w.torch_dtype, seed, w.bias)
     out["workload"] = w
     return out
+
+
+def draw_grad_output(T: int, d: int, dtype=torch.bfloat16, seed: int = 0) -> torch.Tensor:
+    """dY for the backward (recipe above; CPU tensor)."""
+    g = torch.Generator("cpu").manual_seed(seed + 7919)
+    return _randn(g, (T, d), 1).to(dtype)
 
 
 def to_numpy_f32(t: torch.Tensor):

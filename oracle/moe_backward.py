@@ -41,7 +41,10 @@ its gate in the normalisation but contributes nothing to Y, so its dg is 0:
 
 Parity status: pinned by ``-m "not gpu"`` tests against central finite
 differences of the forward oracle's loss sum(Y * dY) on small float64 layers
-(with and without capacity drops), and by the identity <dY, O> = <dA', A>.
+(with and without capacity drops), by the identity <dY, O> = <dA', A> and by
+the zero row sums of dl (a softmax Jacobian maps onto the sum-zero plane).
+``sampled_backward`` is pinned to ``backward`` on small layers (every expert
+and token listed).
 """
 
 from __future__ import annotations
@@ -179,3 +182,67 @@ def loss(X, W_r, W_gate, W_up, W_down, K, dY, capacity_factor=0.0, bias=None) ->
     """sum(Y * dY): the scalar whose gradients ``backward`` returns."""
     Y = mo.forward(X, W_r, W_gate, W_up, W_down, K, capacity_factor, bias=bias)["Y"]
     return float(np.sum(Y * _f64(dY)))
+
+
+def route_record(X, W_r, K: int, capacity_factor=0.0, bias=None, logits=None) -> dict:
+    """Steps 1-5 of the forward oracle only (routing and expert-major
+    metadata, no expert FFN): what ``sampled_backward`` needs."""
+    X = np.asarray(X)
+    T = X.shape[0]
+    E = np.asarray(W_r).shape[1]
+    r = mo.route(X, W_r, K, bias=bias, logits=logits)
+    C = mo.capacity(T, K, E, capacity_factor)
+    out = dict(r)
+    out.update(mo.permute(r["ids"], E, C))
+    out["C"] = C
+    return out
+
+
+def sampled_backward(dY, rec, X, W_r, W_gate, W_up, W_down, experts=(), tokens=()) -> dict:
+    """Parts of ``backward``, computed one expert or one token at a time for
+    layers too large to do whole: dW_gate[e], dW_up[e], dW_down[e] for the
+    listed experts (sums over that expert's slots), and dX[t], dl[t] for the
+    listed tokens (from the token's own K assignments).  ``rec`` is a
+    ``route_record`` (or ``forward_train``) result.  Same steps as
+    ``expert_backward``, ``router_backward`` and ``backward``."""
+    X, dY = np.asarray(X), np.asarray(dY)
+    offsets = np.asarray(rec["offsets"], dtype=np.int64)
+    perm = np.asarray(rec["perm_token"], dtype=np.int64)
+    ids = np.asarray(rec["ids"], dtype=np.int64)
+    inv = np.asarray(rec["inv_slot"], dtype=np.int64)
+    g = _f64(rec["gates"])
+    E = len(offsets) - 1
+    gs = slot_gates(g, inv, int(offsets[E]))
+    out = {"dW_gate": {}, "dW_up": {}, "dW_down": {}, "dX": {}, "dl": {}}
+    for e in experts:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        Xe, dYe = _f64(X[perm[lo:hi]]), _f64(dY[perm[lo:hi]])
+        Wg, Wu, Wd = _f64(W_gate[e]), _f64(W_up[e]), _f64(W_down[e])
+        Hg, Hu = Xe @ Wg, Xe @ Wu
+        A = mo.silu(Hg) * Hu
+        ge = gs[lo:hi, None]
+        dA = ge * (dYe @ Wd.T)
+        out["dW_down"][e] = A.T @ (ge * dYe)
+        out["dW_gate"][e] = Xe.T @ (dA * Hu * dsilu(Hg))
+        out["dW_up"][e] = Xe.T @ (dA * mo.silu(Hg))
+    K = ids.shape[1]
+    for t in tokens:
+        x, dy = _f64(X[t]), _f64(dY[t])
+        dg = np.zeros(K)
+        dxs = np.zeros(x.shape[0])
+        for k in range(K):
+            if inv[t, k] < 0:
+                continue
+            e = int(ids[t, k])
+            Wg, Wu, Wd = _f64(W_gate[e]), _f64(W_up[e]), _f64(W_down[e])
+            hg, hu = x @ Wg, x @ Wu
+            dap = dy @ Wd.T
+            dg[k] = float(dap @ (mo.silu(hg) * hu))
+            da = g[t, k] * dap
+            dxs += (da * hu * dsilu(hg)) @ Wg.T + (da * mo.silu(hg)) @ Wu.T
+        dsel = g[t] * (dg - float(np.sum(g[t] * dg)))
+        dl = np.zeros(E)
+        dl[ids[t]] += dsel
+        out["dl"][t] = dl
+        out["dX"][t] = dxs + dl @ _f64(W_r).T
+    return out

@@ -23,7 +23,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 17
     lib = moe.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -159,6 +159,58 @@ def test_gemm_path_flags_are_checked_per_entry_point():
                            A, ws, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_route(ctypes.byref(T0(moe.MOE_FLAG_GEMM_TILED)), A, A, None, None, A, A, None) == \
         moe.MOE_ERR_INVALID_ARG
+
+
+def test_saved_layout_fields():
+    desc = moe.make_desc(16384, 2048, 128, 8, 768)
+    L = moe.moe_saved_layout_of(desc)
+    T, K, E, n = 16384, 8, 128, 768
+    rows = moe.moe_max_rows(desc)
+    order = [("logits", T * E * 4), ("topk_ids", T * K * 4), ("topk_gates", T * K * 4),
+             ("inv_slot", T * K * 4), ("perm_token", T * K * 4), ("counts", E * 4),
+             ("offsets", (E + 1) * 4), ("preact", rows * 2 * n * 2)]
+    end = 0
+    for name, size in order:
+        off = getattr(L, name)
+        assert off % 256 == 0 and off >= end, name
+        end = off + size
+    assert L.bytes >= end
+    assert moe.moe_workspace_size(desc, moe.MOE_WS_SAVED) == L.bytes
+    assert moe.moe_workspace_size(desc, moe.MOE_WS_BACKWARD) > rows * (2 * n + n + 2048) * 2
+
+
+def test_training_entry_points_check_arguments():
+    lib = moe.lib()
+    A = ctypes.c_void_p(1 << 20)
+    desc = moe.make_desc(64, 128, 8, 2, 128)
+    p = ctypes.byref(desc)
+    big = 1 << 30
+    # bf16 only, tiled GEMMs only
+    f32 = moe.make_desc(64, 128, 8, 2, 128, "fp32")
+    assert lib.moe_forward_train(ctypes.byref(f32), A, A, None, A, A, A, A, A, big, A, big, None) == \
+        moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_backward(ctypes.byref(f32), A, A, A, A, A, A, A, big, A, A, A, A, A, A, big,
+                            None) == moe.MOE_ERR_UNSUPPORTED
+    sk = moe.make_desc(64, 128, 8, 2, 128, flags=moe.MOE_FLAG_GEMM_SKINNY)
+    assert lib.moe_forward_train(ctypes.byref(sk), A, A, None, A, A, A, A, A, big, A, big, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    # short saved state / workspace
+    assert lib.moe_forward_train(p, A, A, None, A, A, A, A, A, 16, A, big, None) == moe.MOE_ERR_WORKSPACE
+    assert b"MOE_WS_SAVED" in lib.moe_last_error()
+    assert lib.moe_forward_train(p, A, A, None, A, A, A, A, A, big, A, 16, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_backward(p, A, A, A, A, A, A, A, 16, A, A, A, A, A, A, big, None) == \
+        moe.MOE_ERR_WORKSPACE
+    assert lib.moe_backward(p, A, A, A, A, A, A, A, big, A, A, A, A, A, A, 16, None) == \
+        moe.MOE_ERR_WORKSPACE
+    assert b"MOE_WS_BACKWARD" in lib.moe_last_error()
+    # null gradient outputs are rejected before anything else
+    assert lib.moe_backward(p, A, A, A, A, A, A, A, big, A, None, A, A, A, A, big, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert b"dW_r is NULL" in lib.moe_last_error()
+    # the training forward of an empty batch is a no-op
+    zero = moe.make_desc(0, 128, 8, 2, 128)
+    assert lib.moe_forward_train(ctypes.byref(zero), A, A, None, A, A, A, A, A, big, A, big, None) == \
+        moe.MOE_OK
 
 
 def test_missing_library_fails_loudly(monkeypatch):

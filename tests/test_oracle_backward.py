@@ -140,3 +140,32 @@ def _planted(kind):
 def test_planted_mistakes_are_caught(kind):
     worst, _ = _fd_check(6, 8, 4, 2, 5, 0.0, False, 1, bwd=_planted(kind))
     assert worst > 1e-3, kind
+
+
+def test_router_gradient_rows_sum_to_zero():
+    """dl[t] = J_t dg with J the softmax-over-the-K Jacobian, whose columns sum
+    to zero; so every row of dl, and of dW_r = X^T dl, sums to zero."""
+    X, W_r, Wg, Wu, Wd, dY, b = _layer(11, 8, 6, 3, 4, 9, bias=True)
+    fw = mb.forward_train(X, W_r, Wg, Wu, Wd, 3, 0.5, bias=b)
+    g = mb.backward(dY, fw, X, W_r, Wg, Wu, Wd)
+    assert np.max(np.abs(g["dl"].sum(axis=1))) < 1e-13
+    assert np.max(np.abs(g["dW_r"].sum(axis=1))) < 1e-12
+    assert np.max(np.abs(g["dl"])) > 1e-3
+
+
+@pytest.mark.parametrize("cf,bias", [(0.0, False), (0.5, True)])
+def test_sampled_backward_matches_whole(cf, bias):
+    T, d, E, K, n = 13, 8, 5, 2, 6
+    X, W_r, Wg, Wu, Wd, dY, b = _layer(T, d, E, K, n, 11, bias)
+    fw = mb.forward_train(X, W_r, Wg, Wu, Wd, K, cf, bias=b)
+    whole = mb.backward(dY, fw, X, W_r, Wg, Wu, Wd)
+    rec = mb.route_record(X, W_r, K, cf, bias=b)
+    for key in ("ids", "inv_slot", "offsets", "perm_token"):
+        assert np.array_equal(rec[key], fw[key])
+    part = mb.sampled_backward(dY, rec, X, W_r, Wg, Wu, Wd, experts=range(E), tokens=range(T))
+    for e in range(E):
+        for name in ("dW_gate", "dW_up", "dW_down"):
+            assert np.allclose(part[name][e], whole[name][e], rtol=1e-12, atol=1e-12)
+    for t in range(T):
+        assert np.allclose(part["dX"][t], whole["dX"][t], rtol=1e-12, atol=1e-12)
+        assert np.allclose(part["dl"][t], whole["dl"][t], rtol=1e-12, atol=1e-12)

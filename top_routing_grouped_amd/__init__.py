@@ -1,4 +1,4 @@
-"""MI355X (gfx950) MoE layer forward: Python binding over the C ABI of include/moe.h.
+"""MI355X (gfx950) MoE layer (forward and backward): Python binding over the C ABI of include/moe.h.
 
 Argument marshalling only.  Every step of the layer runs in the HIP kernels of
 ``libmoe_mi355x.so``; PyTorch supplies device memory and the stream.  If the
@@ -6,9 +6,10 @@ library has not been built, every call raises (there is no fallback path).
 
 Low-level functions carry the C names (``moe_route``, ``moe_permute``,
 ``moe_grouped_gemm_up``, ``moe_grouped_gemm_down``, ``moe_grouped_ffn``,
-``moe_combine``, ``moe_forward`` and the host-only queries) and take torch
-tensors.  ``route``, ``permute``, ``grouped_ffn``, ``combine`` and
-``forward`` allocate the outputs with torch and call them.
+``moe_combine``, ``moe_forward``, ``moe_forward_train``, ``moe_backward`` and
+the host-only queries) and take torch tensors.  ``route``, ``permute``,
+``grouped_ffn``, ``combine``, ``forward``, ``forward_train`` and ``backward``
+allocate the outputs with torch and call them.
 """
 
 from __future__ import annotations
@@ -31,6 +32,8 @@ MOE_WS_PERMUTE = 0
 MOE_WS_GROUPED_FFN = 1
 MOE_WS_FORWARD = 2
 MOE_WS_ROUTE = 3
+MOE_WS_SAVED = 4
+MOE_WS_BACKWARD = 5
 MOE_FLAG_TILE_TABLE_READY = 1
 MOE_FLAG_GEMM_TILED = 2
 MOE_FLAG_GEMM_SKINNY = 4
@@ -62,6 +65,14 @@ def make_desc(T, d, E, K, n, dtype="bf16", capacity_factor=0.0, flags=0) -> MoeD
     return MoeDesc(int(T), int(d), int(E), int(K), int(n), code, float(capacity_factor), int(flags))
 
 
+class MoeSavedLayout(ctypes.Structure):
+    """Mirror of ``moe_saved_layout``: byte offsets of the saved state's fields."""
+
+    _fields_ = [(name, ctypes.c_size_t) for name in
+                ("logits", "topk_ids", "topk_gates", "inv_slot", "perm_token", "counts",
+                 "offsets", "preact", "bytes")]
+
+
 _lib = None
 _VP = ctypes.c_void_p
 _DP = ctypes.POINTER(MoeDesc)
@@ -78,6 +89,11 @@ _SIGNATURES = {
     "moe_grouped_ffn": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "moe_combine": [_DP, _VP, _VP, _VP, _VP, _VP],
     "moe_forward": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "moe_saved_layout_of": [_DP, ctypes.POINTER(MoeSavedLayout)],
+    "moe_forward_train": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP,
+                          ctypes.c_size_t, _VP],
+    "moe_backward": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP, _VP, _VP, _VP,
+                     _VP, _VP, ctypes.c_size_t, _VP],
 }
 
 
@@ -152,6 +168,12 @@ def moe_workspace_size(desc: MoeDesc, entry: int) -> int:
     return out.value
 
 
+def moe_saved_layout_of(desc: MoeDesc) -> MoeSavedLayout:
+    out = MoeSavedLayout()
+    _check(lib().moe_saved_layout_of(ctypes.byref(desc), ctypes.byref(out)), "moe_saved_layout_of")
+    return out
+
+
 # ---------------------------------------------------------------- device entry points
 
 def moe_route(desc, X, W_r, bias, logits, ids, gates, stream=None):
@@ -200,6 +222,24 @@ def moe_forward(desc, X, W_r, bias, W_gate, W_up, W_down, Y, ws, stream=None):
     _check(lib().moe_forward(ctypes.byref(desc), _p(X), _p(W_r), _p(bias), _p(W_gate), _p(W_up),
                              _p(W_down), _p(Y), _p(ws), ws.numel() * ws.element_size(),
                              _stream(stream)), "moe_forward")
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def moe_forward_train(desc, X, W_r, bias, W_gate, W_up, W_down, Y, saved, ws, stream=None):
+    _check(lib().moe_forward_train(ctypes.byref(desc), _p(X), _p(W_r), _p(bias), _p(W_gate),
+                                   _p(W_up), _p(W_down), _p(Y), _p(saved), _nbytes(saved), _p(ws),
+                                   _nbytes(ws), _stream(stream)), "moe_forward_train")
+
+
+def moe_backward(desc, X, W_r, W_gate, W_up, W_down, dY, saved, dX, dW_r, dW_gate, dW_up, dW_down,
+                 ws, stream=None):
+    _check(lib().moe_backward(ctypes.byref(desc), _p(X), _p(W_r), _p(W_gate), _p(W_up),
+                              _p(W_down), _p(dY), _p(saved), _nbytes(saved), _p(dX), _p(dW_r),
+                              _p(dW_gate), _p(dW_up), _p(dW_down), _p(ws), _nbytes(ws),
+                              _stream(stream)), "moe_backward")
 
 
 # ---------------------------------------------------------------- allocating helpers
@@ -284,3 +324,59 @@ def forward(X, W_r, W_gate, W_up, W_down, K, capacity_factor=0.0, bias=None, ws=
     Y = torch.empty_like(X)
     moe_forward(desc, X, W_r, bias, W_gate, W_up, W_down, Y, ws)
     return Y
+
+
+def forward_train(X, W_r, W_gate, W_up, W_down, K, capacity_factor=0.0, bias=None, ws=None):
+    """Training forward (bf16).  Returns (Y [T, d], saved, desc); pass saved and
+    desc unchanged to ``backward``."""
+    import torch
+    desc = _desc_for(X, W_gate, K, capacity_factor)
+    if ws is None:
+        ws = workspace(desc, MOE_WS_FORWARD, X.device)
+    saved = workspace(desc, MOE_WS_SAVED, X.device)
+    Y = torch.empty_like(X)
+    moe_forward_train(desc, X, W_r, bias, W_gate, W_up, W_down, Y, saved, ws)
+    return Y, saved, desc
+
+
+def saved_view(desc: MoeDesc, saved):
+    """Typed views of the saved state's fields (no copies)."""
+    import torch
+    L = moe_saved_layout_of(desc)
+    T, K, E, n = desc.T, desc.K, desc.E, desc.n
+    rows = moe_max_rows(desc)
+
+    def field(off, count, dtype, shape):
+        item = torch.empty((), dtype=dtype).element_size()
+        return saved[off: off + count * item].view(dtype).view(shape)
+
+    return {
+        "logits": field(L.logits, T * E, torch.float32, (T, E)),
+        "ids": field(L.topk_ids, T * K, torch.int32, (T, K)),
+        "gates": field(L.topk_gates, T * K, torch.float32, (T, K)),
+        "inv_slot": field(L.inv_slot, T * K, torch.int32, (T, K)),
+        "perm_token": field(L.perm_token, T * K, torch.int32, (T * K,)),
+        "counts": field(L.counts, E, torch.int32, (E,)),
+        "offsets": field(L.offsets, E + 1, torch.int32, (E + 1,)),
+        "preact": field(L.preact, rows * 2 * n, torch.bfloat16, (rows, 2 * n)),
+    }
+
+
+def backward(desc: MoeDesc, saved, X, W_r, W_gate, W_up, W_down, dY, ws=None):
+    """Gradients of sum(Y * dY) after ``forward_train``.  Returns dict(dX bf16,
+    dW_r, dW_gate, dW_up, dW_down fp32)."""
+    import torch
+    dev = X.device
+    T, d, E, n = desc.T, desc.d, desc.E, desc.n
+    if ws is None:
+        ws = workspace(desc, MOE_WS_BACKWARD, dev)
+    out = {
+        "dX": torch.empty((T, d), dtype=X.dtype, device=dev),
+        "dW_r": torch.empty((d, E), dtype=torch.float32, device=dev),
+        "dW_gate": torch.empty((E, d, n), dtype=torch.float32, device=dev),
+        "dW_up": torch.empty((E, d, n), dtype=torch.float32, device=dev),
+        "dW_down": torch.empty((E, n, d), dtype=torch.float32, device=dev),
+    }
+    moe_backward(desc, X, W_r, W_gate, W_up, W_down, dY, saved, out["dX"], out["dW_r"],
+                 out["dW_gate"], out["dW_up"], out["dW_down"], ws)
+    return out

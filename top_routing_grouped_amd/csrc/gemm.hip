@@ -105,7 +105,7 @@ __device__ __forceinline__ void wait_copies(int pending) {
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return __fdividef(g, 1.0f + __expf(-g)) * u;
+  return g * dev::sigmoid(g) * u;
 }
 
 template <int WTB, int WCB>
@@ -122,6 +122,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_bf16(
     const uint16_t* __restrict__ B0,      // up: W_gate; down: W_down  ([E][Kd][N])
     const uint16_t* __restrict__ B1,      // up: W_up
     uint16_t* __restrict__ C,             // up: H [rows][N]; down: O [rows][N]
+    uint16_t* __restrict__ Hpre,          // up, or NULL: pre-activations [rows][2N] (gate | up)
     int64_t T, int Kd, int N, int NT) {
   using G = Geo<WGM, WGN, WTB, WCB, NST, BK>;
   constexpr int kCpr = G::kCpr, kSh = G::kSh, kRowsPerCopy = 64 / kCpr;
@@ -376,19 +377,58 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_bf16(
       *reinterpret_cast<bf16x8*>(C + (int64_t)(row0 + rloc) * N + col) = v;
     }
   }
+  if (UP && Hpre != nullptr) {
+    // training forward: also keep the pre-activations (x W_gate | x W_up) of
+    // the tile, staged the same way: a row of the tile holds its 128 gate
+    // columns then the same 128 up columns.
+    constexpr int kPRow = BN * 2;
+    constexpr int kPChunks = kPRow / 16;
+    __syncthreads();                          // the staged output tile has been read out
+#pragma unroll
+    for (int tb = 0; tb < WTB; ++tb) {
+      const int rloc = wm * (WTB * 32) + tb * 32 + (lane & 31);
+      unsigned char* srow = smem + rloc * kPRow;
+#pragma unroll
+      for (int cb = 0; cb < WCB; ++cb)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int colbase = (cb < kHalf) ? (wn * kHalf * 32 + cb * 32)
+                                           : (BN / 2 + wn * kHalf * 32 + (cb - kHalf) * 32);
+          const int col = colbase + 8 * v4 + 4 * (lane >> 5);
+          const u32x2 pk = {dev::pack_bf16x2(acc[cb][tb][4 * v4], acc[cb][tb][4 * v4 + 1]),
+                            dev::pack_bf16x2(acc[cb][tb][4 * v4 + 2], acc[cb][tb][4 * v4 + 3])};
+          const int chunk = (col >> 3) ^ (rloc & (kPChunks - 1));
+          *reinterpret_cast<u32x2*>(srow + chunk * 16 + ((col >> 2) & 1) * 8) = pk;
+        }
+    }
+    __syncthreads();
+    constexpr int kPIters = BM * kPChunks / G::kThreads;
+#pragma unroll
+    for (int i = 0; i < kPIters; ++i) {
+      const int idx = tid + i * G::kThreads;
+      const int rloc = idx / kPChunks, c = idx - (idx / kPChunks) * kPChunks;
+      const int half = c / (kPChunks / 2);                // 0: gate, 1: up
+      const int col = ncol0 + (c - half * (kPChunks / 2)) * 8;
+      if (rloc < nrows && col < N) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(
+            smem + rloc * kPRow + ((c ^ (rloc & (kPChunks - 1))) * 16));
+        *reinterpret_cast<bf16x8*>(Hpre + (int64_t)(row0 + rloc) * (2 * N) + half * N + col) = v;
+      }
+    }
+  }
 }
 
 template <bool UP>
 hipError_t launch_bf16(const uint16_t* A, const int32_t* perm, const int32_t* table,
-                       const uint16_t* B0, const uint16_t* B1, uint16_t* C, int64_t T, int Kd,
-                       int N, int64_t mtiles, hipStream_t s) {
+                       const uint16_t* B0, const uint16_t* B1, uint16_t* C, uint16_t* Hpre,
+                       int64_t T, int Kd, int N, int64_t mtiles, hipStream_t s) {
   const int NT = (N + (UP ? BN / 2 : BN) - 1) / (UP ? BN / 2 : BN);
   auto* kern = grouped_gemm_bf16<UP, kWGM, kWGN, kWTB, kWCB, kNST, kBK>;
   hipError_t err = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, ProdGeo::kLds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3((unsigned)(mtiles * NT)), dim3(ProdGeo::kThreads),
-                     (size_t)ProdGeo::kLds, s, A, perm, table, B0, B1, C, T, Kd, N, NT);
+                     (size_t)ProdGeo::kLds, s, A, perm, table, B0, B1, C, Hpre, T, Kd, N, NT);
   return hipGetLastError();
 }
 
@@ -473,11 +513,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
 
 hipError_t launch_gemm_up(const Problem& p, const void* X, const int32_t* perm,
                           const int32_t* table, const void* W_gate, const void* W_up, void* H,
-                          hipStream_t s) {
+                          hipStream_t s, void* Hpre) {
   const int64_t mtiles = max_row_tiles(p, kGemmBM);
   if (p.bf16)
     return launch_bf16<true>((const uint16_t*)X, perm, table, (const uint16_t*)W_gate,
-                             (const uint16_t*)W_up, (uint16_t*)H, p.T, p.d, p.n, mtiles, s);
+                             (const uint16_t*)W_up, (uint16_t*)H, (uint16_t*)Hpre, p.T, p.d, p.n,
+                             mtiles, s);
+  if (Hpre) return hipErrorNotSupported;      // the training path is bf16 only
   const int NT = (p.n + 63) / 64;
   hipLaunchKernelGGL(grouped_gemm_f32<true>, dim3((unsigned)(mtiles * kF32Sub * NT)), dim3(256), 0, s,
                      (const float*)X, perm, table, (const float*)W_gate, (const float*)W_up,
@@ -490,7 +532,7 @@ hipError_t launch_gemm_down(const Problem& p, const void* H, const int32_t* tabl
   const int64_t mtiles = max_row_tiles(p, kGemmBM);
   if (p.bf16)
     return launch_bf16<false>((const uint16_t*)H, nullptr, table, (const uint16_t*)W_down,
-                              nullptr, (uint16_t*)O, p.T, p.n, p.d, mtiles, s);
+                              nullptr, (uint16_t*)O, nullptr, p.T, p.n, p.d, mtiles, s);
   const int NT = (p.d + 63) / 64;
   hipLaunchKernelGGL(grouped_gemm_f32<false>, dim3((unsigned)(mtiles * kF32Sub * NT)), dim3(256), 0, s,
                      (const float*)H, nullptr, table, (const float*)W_down, nullptr, (float*)O,

@@ -85,7 +85,7 @@ __device__ __forceinline__ void wait_stages(int pending) {
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return __fdividef(g, 1.0f + __expf(-g)) * u;
+  return g * dev::sigmoid(g) * u;
 }
 
 template <bool UP, int ROWS, int COLS>

@@ -139,6 +139,44 @@ ForwardWs carve_forward(const moe::Problem& p, unsigned char* base) {
   return w;
 }
 
+// State kept by moe_forward_train for moe_backward (field order as in
+// moe_saved_layout, plus the row-tile table at the end).
+struct Saved {
+  float* logits;
+  int32_t* ids;
+  float* gates;
+  int32_t* inv;
+  int32_t* perm;
+  int32_t* counts;
+  int32_t* offsets;
+  uint16_t* Hpre;
+  int32_t* table;
+  moe_saved_layout layout;
+};
+Saved carve_saved(const moe::Problem& p, unsigned char* base) {
+  Saved w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes, size_t* field) {
+    if (field) *field = off;
+    unsigned char* ptr = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return ptr;
+  };
+  const size_t tk = (size_t)p.T * p.K;
+  moe_saved_layout& L = w.layout;
+  w.logits = reinterpret_cast<float*>(take((size_t)p.T * p.E * 4, &L.logits));
+  w.ids = reinterpret_cast<int32_t*>(take(tk * 4, &L.topk_ids));
+  w.gates = reinterpret_cast<float*>(take(tk * 4, &L.topk_gates));
+  w.inv = reinterpret_cast<int32_t*>(take(tk * 4, &L.inv_slot));
+  w.perm = reinterpret_cast<int32_t*>(take(tk * 4, &L.perm_token));
+  w.counts = reinterpret_cast<int32_t*>(take((size_t)p.E * 4, &L.counts));
+  w.offsets = reinterpret_cast<int32_t*>(take((size_t)(p.E + 1) * 4, &L.offsets));
+  w.Hpre = reinterpret_cast<uint16_t*>(take((size_t)p.rows_max * 2 * p.n * 2, &L.preact));
+  w.table = reinterpret_cast<int32_t*>(take(moe::tile_table_bytes(p), nullptr));
+  L.bytes = off;
+  return w;
+}
+
 bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
 
 moe_status check_ptrs(std::initializer_list<std::pair<const void*, const char*>> required,
@@ -218,9 +256,22 @@ moe_status moe_workspace_size(const moe_desc* desc, int32_t entry, size_t* bytes
     case MOE_WS_ROUTE:
       *bytes = align_up(moe::route_partial_bytes(p));
       return MOE_OK;
+    case MOE_WS_SAVED:
+      *bytes = carve_saved(p, nullptr).layout.bytes;
+      return MOE_OK;
+    case MOE_WS_BACKWARD:
+      *bytes = moe::backward_ws_bytes(p, nullptr, nullptr);
+      return MOE_OK;
     default:
       return fail(MOE_ERR_INVALID_ARG, "unknown workspace selector");
   }
+}
+
+moe_status moe_saved_layout_of(const moe_desc* desc, moe_saved_layout* out) {
+  MOE_TRY(check_desc(desc, kAllFlags));
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  *out = carve_saved(make_problem(desc), nullptr).layout;
+  return MOE_OK;
 }
 
 const char* moe_status_str(int32_t status) {
@@ -396,6 +447,67 @@ moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, con
                        "grouped GEMM (down) launch"));
   }
   return hip_status(moe::launch_combine(p, w.O, w.gates, w.inv, Y, s), "combine launch");
+}
+
+moe_status moe_forward_train(const moe_desc* desc, const void* X, const void* W_r,
+                             const float* bias, const void* W_gate, const void* W_up,
+                             const void* W_down, void* Y, void* saved, size_t saved_bytes,
+                             void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED));
+  if (desc->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the training path is bf16 only");
+  if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
+  MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {W_gate, "W_gate"}, {W_up, "W_up"},
+                      {W_down, "W_down"}, {Y, "Y"}, {saved, "saved"}, {ws, "ws"}},
+                     {{bias, "bias"}}));
+  const moe::Problem p = make_problem(desc);
+  if (saved_bytes < carve_saved(p, nullptr).layout.bytes)
+    return fail(MOE_ERR_WORKSPACE, "saved smaller than moe_workspace_size(MOE_WS_SAVED)");
+  if (ws_bytes < carve_forward(p, nullptr).bytes)
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_FORWARD)");
+  hipStream_t s = (hipStream_t)stream;
+  const Saved sv = carve_saved(p, static_cast<unsigned char*>(saved));
+  const ForwardWs w = carve_forward(p, static_cast<unsigned char*>(ws));
+  MOE_TRY(hip_status(moe::launch_route(p, X, W_r, bias, sv.logits, sv.ids, sv.gates,
+                                       w.route_partial, s),
+                     "route launch"));
+  MOE_TRY(run_permute(p, sv.ids, sv.counts, sv.offsets, nullptr, sv.perm, sv.inv, w.permute,
+                      sv.table, s));
+  MOE_TRY(hip_status(moe::launch_gemm_up(p, X, sv.perm, sv.table, W_gate, W_up, w.H, s, sv.Hpre),
+                     "grouped GEMM (up) launch"));
+  MOE_TRY(hip_status(moe::launch_gemm_down(p, w.H, sv.table, W_down, w.O, s),
+                     "grouped GEMM (down) launch"));
+  return hip_status(moe::launch_combine(p, w.O, sv.gates, sv.inv, Y, s), "combine launch");
+}
+
+moe_status moe_backward(const moe_desc* desc, const void* X, const void* W_r, const void* W_gate,
+                        const void* W_up, const void* W_down, const void* dY, const void* saved,
+                        size_t saved_bytes, void* dX, float* dW_r, float* dW_gate, float* dW_up,
+                        float* dW_down, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED));
+  if (desc->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the training path is bf16 only");
+  MOE_TRY(check_ptrs({{dW_r, "dW_r"}, {dW_gate, "dW_gate"}, {dW_up, "dW_up"}, {dW_down, "dW_down"}},
+                     {}));
+  const moe::Problem p = make_problem(desc);
+  hipStream_t s = (hipStream_t)stream;
+  if (desc->T == 0)   // no tokens: the weight gradients are zero
+    return hip_status(moe::launch_zero_grads(p, dW_r, dW_gate, dW_up, dW_down, s),
+                      "zero-gradient launch");
+  MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {W_gate, "W_gate"}, {W_up, "W_up"},
+                      {W_down, "W_down"}, {dY, "dY"}, {saved, "saved"}, {dX, "dX"}, {ws, "ws"}},
+                     {}));
+  if (saved_bytes < carve_saved(p, nullptr).layout.bytes)
+    return fail(MOE_ERR_WORKSPACE, "saved smaller than moe_workspace_size(MOE_WS_SAVED)");
+  if (ws_bytes < moe::backward_ws_bytes(p, nullptr, nullptr))
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_BACKWARD)");
+  const Saved sv = carve_saved(p, static_cast<unsigned char*>(const_cast<void*>(saved)));
+  moe::BackwardWs w;
+  moe::backward_ws_bytes(p, &w, static_cast<unsigned char*>(ws));
+  return hip_status(moe::launch_backward(p, X, W_r, W_gate, W_up, W_down, dY, sv.ids, sv.gates,
+                                         sv.inv, sv.perm, sv.offsets, sv.table, sv.Hpre, dX, dW_r,
+                                         dW_gate, dW_up, dW_down, w, s),
+                    "backward launch");
 }
 
 }  // extern "C"

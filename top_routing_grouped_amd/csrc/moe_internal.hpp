@@ -87,9 +87,11 @@ hipError_t launch_scatter(const Problem& p, const int32_t* ids, const int32_t* b
 hipError_t launch_tile_table(const Problem& p, const int32_t* offsets, int32_t* table,
                              hipStream_t s);
 
+// Hpre (bf16 only, may be NULL): also store the pre-activations [rows][2n]
+// (x W_gate | x W_up) for the backward.
 hipError_t launch_gemm_up(const Problem& p, const void* X, const int32_t* perm,
                           const int32_t* table, const void* W_gate, const void* W_up, void* H,
-                          hipStream_t s);
+                          hipStream_t s, void* Hpre = nullptr);
 hipError_t launch_gemm_down(const Problem& p, const void* H, const int32_t* table,
                             const void* W_down, void* O, hipStream_t s);
 
@@ -115,6 +117,32 @@ inline bool use_skinny(const Problem& p, uint32_t flags, uint32_t tiled_flag, ui
 hipError_t launch_combine(const Problem& p, const void* O, const float* gates,
                           const int32_t* inv_slot, void* Y, hipStream_t s);
 
+// ---------------------------------------------------------------- backward (bf16)
+// Scratch of the backward, carved from the caller's workspace.
+struct BackwardWs {
+  float* gs;           // [rows] gate of each kept slot
+  float* dS_part;      // [rows][ceil(n/256)] per-tile shares of dS = <dA', A>
+  uint16_t* dH;        // [rows][2n] (dHg | dHu)
+  uint16_t* gA;        // [rows][n]  g * silu(Hg) * Hu
+  uint16_t* dXs;       // [rows][d]  input gradient per slot
+  uint16_t* dl;        // [T][Epad]  router-logit gradient (zeros off the selected experts)
+  uint16_t* W_rT;      // [E][d]
+  uint32_t* zero;      // kZeroBytes of zeros (copy source past a group's end)
+  float* dWr_part;     // [ksplit][d][Epad] split-k partials of dW_r
+};
+constexpr int kZeroBytes = 256;
+int bwd_router_ksplit(const Problem& p);
+// Bytes of the backward scratch; with base != NULL also carves it into *w.
+size_t backward_ws_bytes(const Problem& p, BackwardWs* w, unsigned char* base);
+hipError_t launch_zero_grads(const Problem& p, float* dW_r, float* dW_gate, float* dW_up,
+                             float* dW_down, hipStream_t s);
+hipError_t launch_backward(const Problem& p, const void* X, const void* W_r, const void* W_gate,
+                           const void* W_up, const void* W_down, const void* dY,
+                           const int32_t* ids, const float* gates, const int32_t* inv,
+                           const int32_t* perm, const int32_t* offsets, const int32_t* table,
+                           const void* Hpre, void* dX, float* dW_r, float* dW_gate, float* dW_up,
+                           float* dW_down, const BackwardWs& w, hipStream_t s);
+
 }  // namespace moe
 
 // ---------------------------------------------------------------- device helpers
@@ -132,6 +160,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// 1 / (1 + e^-z) with the hardware exp2 and reciprocal (about 1 ulp each;
+// a quotient written with '/' or __fdividef compiles to the full IEEE
+// division sequence, several times the instructions and registers).
+// z -> -inf gives 1/inf = 0.
+__device__ __forceinline__ float sigmoid(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
 // Workgroup barrier without the memory fence that __syncthreads adds (the
