@@ -11,7 +11,9 @@ kernels run on, and `value` = T / median step time.  Each step is followed
 by the same work through the step-wise entry points with events between the
 stages (per-stage medians, same kernels); then the up GEMM alone is timed
 for the roofline, and everything is repeated without the flush (warm,
-labelled as such).  Prints one JSON line.
+labelled as such).  For bf16 workloads the training step (moe_forward_train
+then moe_backward on a seeded dY) is timed the same way and reported under
+"training".  Prints one JSON line.
 
 Extra modes (used for profiler runs):
     --calib-copy BYTES   only run a plain device-to-device copy of BYTES
@@ -21,6 +23,9 @@ Extra modes (used for profiler runs):
                          summary under profiles/ (no GPU needed).
     --no-cpu-baseline    skip the oracle timing on the host cores.
     --warm               skip the cache flush (profiling runs).
+    --no-train           skip the training step (counter runs of the forward GEMMs:
+                         the training forward's up GEMM also writes the
+                         pre-activations).
 """
 
 from __future__ import annotations
@@ -61,6 +66,7 @@ def parse():
     ap.add_argument("--calib-copy", type=int, default=0)
     ap.add_argument("--pmc-summary", nargs=4, default=None)
     ap.add_argument("--warm", action="store_true")
+    ap.add_argument("--no-train", action="store_true")
     return ap.parse_args()
 
 
@@ -309,6 +315,41 @@ def main():
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in evs]
 
+    train = w.dtype == "bf16" and not args.no_train
+    if train:
+        dY = mi.draw_grad_output(T, d, torch.bfloat16, seed=0).cuda()
+        Y_t = torch.empty_like(Y)
+        saved = moe.workspace(desc, moe.MOE_WS_SAVED)
+        ws_b = moe.workspace(desc, moe.MOE_WS_BACKWARD)
+        g = {"dX": torch.empty((T, d), dtype=torch.bfloat16, device="cuda"),
+             "dW_r": torch.empty((d, E), dtype=torch.float32, device="cuda"),
+             "dW_gate": torch.empty((E, d, n), dtype=torch.float32, device="cuda"),
+             "dW_up": torch.empty((E, d, n), dtype=torch.float32, device="cuda"),
+             "dW_down": torch.empty((E, n, d), dtype=torch.float32, device="cuda")}
+
+    def train_step(evs):
+        evs[0].record(stream)
+        moe.moe_forward_train(desc, dev["X"], dev["W_r"], dev["bias"], dev["W_gate"], dev["W_up"],
+                              dev["W_down"], Y_t, saved, ws_fwd)
+        evs[1].record(stream)
+        moe.moe_backward(desc, dev["X"], dev["W_r"], dev["W_gate"], dev["W_up"], dev["W_down"], dY,
+                         saved, g["dX"], g["dW_r"], g["dW_gate"], g["dW_up"], g["dW_down"], ws_b)
+        evs[2].record(stream)
+
+    def run_train(cold: bool):
+        """K training steps (forward that keeps the backward's state, then the
+        backward), each after a cache flush when `cold`."""
+        evs = [[ev() for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.warmup):
+            train_step([ev() for _ in range(3)])
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            if cold:
+                flush(i)
+            train_step(evs[i])
+        torch.cuda.synchronize()
+        return ([e[0].elapsed_time(e[1]) for e in evs], [e[1].elapsed_time(e[2]) for e in evs])
+
     cold = not args.warm
     # ---- timed region: K steps (moe_forward timed; step-wise diagnostics interleaved)
     torch.cuda.synchronize()
@@ -318,6 +359,7 @@ def main():
     wall = time.perf_counter() - t_wall
     up_kernel_ms = run_up_kernel(cold)
     warm_fused_ms, warm_stage_ms = run(False)
+    train_ms = run_train(cold) if train else None
 
     med = statistics.median(fused_ms)
     names = ["route", "permute", "gemm_up", "gemm_down", "combine"]
@@ -397,6 +439,22 @@ def main():
         "gemm_path": "weight-streaming" if skinny else "tiled",
         "input_sha256": hashes,
     }
+    if train:
+        f_ms, b_ms = statistics.median(train_ms[0]), statistics.median(train_ms[1])
+        bwd_flops = 12.0 * N * d * n + 2.0 * T * d * E
+        rec["training"] = {
+            "what": "moe_forward_train then moe_backward (dX, dW_r, dW_gate, dW_up, dW_down); "
+                    "cold cache before each step",
+            "fwd_train_ms": f_ms,
+            "bwd_ms": b_ms,
+            "tokens_per_s": T / ((f_ms + b_ms) * 1e-3),
+            "bwd_flops": bwd_flops,
+            "bwd_tflops": bwd_flops / (b_ms * 1e-3) / 1e12,
+            "bwd_mfma_frac": bwd_flops / (b_ms * 1e-3) / 1e12 / peak,
+            "bwd_flops_per_unit": "12*d*n per kept row (dA', per-slot dX, dW_down, dW_gate, "
+                                  "dW_up) + 2*d*E per token (dW_r)",
+            "bwd_ms_p10_p90": [pct(train_ms[1], 0.1), pct(train_ms[1], 0.9)],
+        }
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_tokens or min(T, 16384)
         rec["cpu_baseline"] = cpu_baseline(inp, w, sample)

@@ -396,13 +396,49 @@ __global__ __launch_bounds__(kThreads, 1) void alpha_gemm(
 // qrow go through perm when PG / QG.  Columns j < Jsplit go to C0[g][i][j]
 // (pitch Jsplit), the rest to C1[g][i][j - Jsplit] (pitch Jq - Jsplit); with
 // ksplit > 1, C0 is a partial buffer and split z writes at z * zstride.
-template <bool PG, bool QG>
+//
+// The reduction runs over an expert's rows, a few hundred to a few thousand,
+// so a tile has few k-steps.  NST stages of BK rows: on the Qwen3-shaped
+// layer two 64-row stages ran fastest (dW_gate|dW_up 1.31 ms); four or five
+// 32-row stages (more bytes in flight, twice the barriers) were 5-11% slower.
+#ifndef MOE_BETA_NST
+#define MOE_BETA_NST 2
+#endif
+#ifndef MOE_BETA_BK
+#define MOE_BETA_BK 64
+#endif
+template <int NST, int BK>
+struct BetaGeo {
+  static constexpr int kOpBytes = BK * kTile * 2;        // one operand tile of a stage
+  static constexpr int kStage = 2 * kOpBytes;
+  static constexpr int kLds = NST * kStage;
+  static constexpr int kCopies = kOpBytes / 1024 / 8;    // copy instructions per wave per operand
+  static constexpr int kInstr = 2 * kCopies;
+  static constexpr int KS = BK / 16;
+  static_assert(kCopies * 1024 * 8 == kOpBytes, "copy split");
+  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
+  static_assert(NST >= 2 && NST <= 5, "stage count");
+};
+
+// Wait until at most `pending` stages (INSTR copy instructions each) of this
+// wave are in flight.
+template <int INSTR>
+__device__ __forceinline__ void wait_stages(int pending) {
+  if (pending >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * INSTR) : "memory");
+  else if (pending == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * INSTR) : "memory");
+  else if (pending == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(INSTR) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <bool PG, bool QG, int NST, int BK>
 __global__ __launch_bounds__(kThreads, 1) void beta_gemm(
     const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets, int64_t rows_total,
     int64_t T, int Ip, int Jq, int IT, int JT, int ksplit, const uint16_t* __restrict__ zero,
     float* __restrict__ C0, float* __restrict__ C1, int Jsplit, int64_t zstride) {
-  constexpr int KS = kBK / 16;
+  using G = BetaGeo<NST, BK>;
+  constexpr int KS = G::KS, kCp = G::kCopies, kInstrS = G::kInstr;
+  constexpr int kOp = G::kOpBytes, kSt = G::kStage;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -410,10 +446,18 @@ __global__ __launch_bounds__(kThreads, 1) void beta_gemm(
   const int wm = w / kWGN, wn = w - (w / kWGN) * kWGN;
   const uint32_t lds_base = (uint32_t)(size_t)(lds_ptr_t)smem;
 
-  // tile decode: x = group * IT * JT + it * JT + jt; y = k split
+  // tile decode: logical id L = group * IT * JT + it * JT + jt; y = k split.
+  // Workgroups go to the 8 XCDs round robin; the remap gives each XCD a
+  // contiguous range of L, so the tiles running together on an XCD belong to
+  // one or two groups, advance over the same rows together and share the
+  // row slabs in its L2 (round robin spread every group over all 8 XCDs).
+  const int total = gridDim.x;
+  const int q8 = total >> 3, r8 = total & 7;
+  const int xcd = blockIdx.x & 7;
+  const int L = xcd * q8 + (xcd < r8 ? xcd : r8) + (blockIdx.x >> 3);
   const int per_group = IT * JT;
-  const int g = blockIdx.x / per_group;
-  const int rem = blockIdx.x - g * per_group;
+  const int g = L / per_group;
+  const int rem = L - g * per_group;
   const int it = rem / JT, jt = rem - (rem / JT) * JT;
   const int z = blockIdx.y;
   int64_t s0, s1;
@@ -441,50 +485,59 @@ __global__ __launch_bounds__(kThreads, 1) void beta_gemm(
     return;
   }
 
-  // copies: instruction j = kCopies*w + i fills tile rows 2j + lane/32 of each
-  // operand, slot lane%32 holding column chunk slot ^ (4 * (row & 3)).
-  // Columns past the operand's width read column 0 (in bounds; they only
-  // feed output columns that are never stored); rows past the range copy zeros.
-  int pcol[kCopies], qcol[kCopies];
+  // copies: instruction c = kCp*w + i fills tile rows 2c + lane/32 of each
+  // operand (so wave w owns rows 2*kCp*w .. 2*kCp*w + 2*kCp - 1), slot
+  // lane%32 holding column chunk slot ^ (4 * (row & 3)).  Columns past the
+  // operand's width read column 0 (in bounds; they only feed output columns
+  // that are never stored); rows past the range copy zeros.
+  int pcol[kCp], qcol[kCp];
 #pragma unroll
-  for (int i = 0; i < kCopies; ++i) {
-    const int k = 2 * (w * kCopies + i) + (lane >> 5);
+  for (int i = 0; i < kCp; ++i) {
+    const int k = 2 * (w * kCp + i) + (lane >> 5);
     const int q = (lane & 31) ^ (4 * (k & 3));
     const int pc = i0 + q * 8, qc = j0 + q * 8;
     pcol[i] = pc < Ip ? pc : 0;
     qcol[i] = qc < Jq ? qc : 0;
   }
-  // Source rows of a stage, fetched one stage ahead: a gathered row index
-  // comes from perm, and waiting for that load when the copies are issued
-  // would stall the wave once per stage.  -1: past the range (zeros).
-  int prow[kCopies], qrow[kCopies];
+  // Source rows of the next stage to issue (-1: past the range).  The row
+  // numbers are wave-uniform per half wave, so gathered ones come from perm
+  // with scalar loads: they do not count against the vector-memory counter
+  // that the stage waits use, and are fetched one stage ahead of their use.
+  int prow[kCp], qrow[kCp];
   auto fetch_rows = [&](int kt) {
+    const int64_t sb = lo + (int64_t)kt * BK + 2 * kCp * w;
 #pragma unroll
-    for (int i = 0; i < kCopies; ++i) {
-      const int k = 2 * (w * kCopies + i) + (lane >> 5);
-      const int64_t s = lo + (int64_t)kt * kBK + k;
-      int r = -1;
-      if (s < hi) {
-        if (PG || QG) {
-          const int64_t t = perm[s];
-          r = (int)(t < 0 ? 0 : (t > T - 1 ? T - 1 : t));
-        } else {
-          r = (int)s;
+    for (int i = 0; i < kCp; ++i) {
+      int r[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t sr = sb + 2 * i + h;
+        int v = -1;
+        if (sr < hi) {
+          if (PG || QG) {
+            const int64_t t = perm[sr];
+            v = (int)(t < 0 ? 0 : (t > T - 1 ? T - 1 : t));
+          } else {
+            v = (int)sr;
+          }
         }
+        r[h] = v;
       }
-      prow[i] = (s < hi) ? (PG ? r : (int)s) : -1;
-      qrow[i] = (s < hi) ? (QG ? r : (int)s) : -1;
+      const int rg = (lane >> 5) ? r[1] : r[0];                  // gathered (or own) row
+      const int rs = rg < 0 ? -1 : (int)(sb + 2 * i + (lane >> 5));  // slot row
+      prow[i] = PG ? rg : rs;
+      qrow[i] = QG ? rg : rs;
     }
   };
   auto issue_stage = [&](int kt) {
-    const uint32_t Ps = lds_base + (uint32_t)((kt & 1) * kStage);
-    const uint32_t Qs = Ps + kHalf;
+    const uint32_t Ps = lds_base + (uint32_t)((kt % NST) * kSt);
+    const uint32_t Qs = Ps + kOp;
 #pragma unroll
-    for (int i = 0; i < kCopies; ++i) {
+    for (int i = 0; i < kCp; ++i) {
       const uint16_t* ps = prow[i] >= 0 ? P + (int64_t)prow[i] * Ip + pcol[i] : zero;
       const uint16_t* qs = qrow[i] >= 0 ? Q + (int64_t)qrow[i] * Jq + qcol[i] : zero;
-      dev::lds_copy16(ps, Ps + (w * kCopies + i) * 1024);
-      dev::lds_copy16(qs, Qs + (w * kCopies + i) * 1024);
+      dev::lds_copy16(ps, Ps + (w * kCp + i) * 1024);
+      dev::lds_copy16(qs, Qs + (w * kCp + i) * 1024);
     }
   };
 
@@ -502,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 1) void beta_gemm(
       p_off[tb][h] = nat_off(k, wm * 128 + tb * 32 + 16 * (gq & 1) + 4 * (s16 & 3));
 #pragma unroll
     for (int cb = 0; cb < kWCB; ++cb)
-      q_off[cb][h] = kHalf + nat_off(k, wn * 64 + cb * 32 + 16 * (gq & 1) + 4 * (s16 & 3));
+      q_off[cb][h] = kOp + nat_off(k, wn * 64 + cb * 32 + 16 * (gq & 1) + 4 * (s16 & 3));
   }
   auto tr8 = [&](const unsigned char* S, int o0, int o1) {
     const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(S + o0));
@@ -510,7 +563,7 @@ __global__ __launch_bounds__(kThreads, 1) void beta_gemm(
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   auto read_frags = [&](Frags<kWTB, kWCB>& f, int kt, int ks) {
-    const unsigned char* S = smem + (kt & 1) * kStage + ks * 16 * 512;
+    const unsigned char* S = smem + (kt % NST) * kSt + ks * 16 * 512;
 #pragma unroll
     for (int tb = 0; tb < kWTB; ++tb) f.a[tb] = tr8(S, p_off[tb][0], p_off[tb][1]);
 #pragma unroll
@@ -531,24 +584,29 @@ __global__ __launch_bounds__(kThreads, 1) void beta_gemm(
         acc[cb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[cb], f.a[tb], acc[cb][tb], 0, 0, 0);
   };
 
-  const int KT = (int)((hi - lo + kBK - 1) / kBK);
-  fetch_rows(0);
-  issue_stage(0);
-  if (KT > 1) fetch_rows(1);
-  wait_copies(false);
+  // main loop: stages kt+1 .. kt+NST-1 in flight while stage kt is multiplied
+  const int KT = (int)((hi - lo + BK - 1) / BK);
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < KT) {
+      fetch_rows(st);
+      issue_stage(st);
+    }
+  if (NST - 1 < KT) fetch_rows(NST - 1);
+  wait_stages<kInstrS>((KT - 1 < NST - 2) ? KT - 1 : NST - 2);
   asm volatile("s_barrier" ::: "memory");
   Frags<kWTB, kWCB> cur, nxt;
   read_frags(cur, 0, 0);
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) {
-      issue_stage(kt + 1);
-      if (kt + 2 < KT) fetch_rows(kt + 2);
-    }
+    if (kt + NST - 1 < KT) issue_stage(kt + NST - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ks += 2) {
       __builtin_amdgcn_s_waitcnt(kWaitLds);
       __builtin_amdgcn_sched_barrier(0);
       read_frags(nxt, kt, ks + 1);
+      // the next stage's rows: every LDS wait also waits for scalar loads,
+      // so they are issued where the MFMAs below cover their latency
+      if (ks == 0 && kt + NST < KT) fetch_rows(kt + NST);
       __builtin_amdgcn_sched_barrier(0);
       mma(cur);
       __builtin_amdgcn_sched_barrier(0);
@@ -556,7 +614,10 @@ __global__ __launch_bounds__(kThreads, 1) void beta_gemm(
       if (ks + 2 < KS) {
         read_frags(cur, kt, ks + 2);
       } else if (kt + 1 < KT) {
-        wait_copies(false);
+        // stage kt+1 landed (own copies), then publish it to all waves; the
+        // barrier also tells every wave that stage kt's buffer is free
+        const int last = (kt + NST - 1 < KT) ? kt + NST - 1 : KT - 1;
+        wait_stages<kInstrS>(last - (kt + 1));
         asm volatile("s_barrier" ::: "memory");
         read_frags(cur, kt + 1, 0);
       }
@@ -723,12 +784,15 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
 }
 
 template <typename Kern>
-hipError_t allow_lds(Kern* k) {
+hipError_t allow_lds(Kern* k, int bytes = kLds) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
 int pad64(int E) { return (E + 63) / 64 * 64; }
+
+constexpr int kBNst = MOE_BETA_NST, kBBk = MOE_BETA_BK;
+constexpr int kBLds = BetaGeo<kBNst, kBBk>::kLds;
 
 }  // namespace
 
@@ -824,20 +888,20 @@ hipError_t launch_backward(const Problem& p, const void* X, const void* W_r, con
   MOE_BWD_TRY(hipGetLastError());
   // dW_down[e] = (g A)^T dY[perm]
   {
-    auto* k = beta_gemm<false, true>;
-    MOE_BWD_TRY(allow_lds(k));
+    auto* k = beta_gemm<false, true, kBNst, kBBk>;
+    MOE_BWD_TRY(allow_lds(k, kBLds));
     const int IT = NTn, JT = NTd;
-    hipLaunchKernelGGL(k, dim3((unsigned)(p.E * IT * JT), 1), dim3(kThreads), (size_t)kLds, s,
+    hipLaunchKernelGGL(k, dim3((unsigned)(p.E * IT * JT), 1), dim3(kThreads), (size_t)kBLds, s,
                        w.gA, (const uint16_t*)dY, perm, offsets, (int64_t)0, p.T, p.n, p.d, IT, JT,
                        1, zero, dW_down, nullptr, p.d, (int64_t)0);
     MOE_BWD_TRY(hipGetLastError());
   }
   // dW_gate[e] | dW_up[e] = X[perm]^T (dHg | dHu)
   {
-    auto* k = beta_gemm<true, false>;
-    MOE_BWD_TRY(allow_lds(k));
+    auto* k = beta_gemm<true, false, kBNst, kBBk>;
+    MOE_BWD_TRY(allow_lds(k, kBLds));
     const int IT = NTd, JT = (2 * p.n + kTile - 1) / kTile;
-    hipLaunchKernelGGL(k, dim3((unsigned)(p.E * IT * JT), 1), dim3(kThreads), (size_t)kLds, s,
+    hipLaunchKernelGGL(k, dim3((unsigned)(p.E * IT * JT), 1), dim3(kThreads), (size_t)kBLds, s,
                        (const uint16_t*)X, w.dH, perm, offsets, (int64_t)0, p.T, p.d, 2 * p.n, IT,
                        JT, 1, zero, dW_gate, dW_up, p.n, (int64_t)0);
     MOE_BWD_TRY(hipGetLastError());
@@ -846,11 +910,11 @@ hipError_t launch_backward(const Problem& p, const void* X, const void* W_r, con
   // then the sum over the splits
   {
     const int zsplit = bwd_router_ksplit(p);
-    auto* k = beta_gemm<false, false>;
-    MOE_BWD_TRY(allow_lds(k));
+    auto* k = beta_gemm<false, false, kBNst, kBBk>;
+    MOE_BWD_TRY(allow_lds(k, kBLds));
     const int IT = NTd, JT = (Epad + kTile - 1) / kTile;
     hipLaunchKernelGGL(k, dim3((unsigned)(IT * JT), (unsigned)zsplit), dim3(kThreads),
-                       (size_t)kLds, s, (const uint16_t*)X, w.dl, perm, nullptr, p.T, p.T, p.d,
+                       (size_t)kBLds, s, (const uint16_t*)X, w.dl, perm, nullptr, p.T, p.T, p.d,
                        Epad, IT, JT, zsplit, zero, w.dWr_part, nullptr, Epad,
                        (int64_t)p.d * Epad);
     MOE_BWD_TRY(hipGetLastError());
