@@ -16,6 +16,12 @@ moe_oracle
 brute
     Pure-Python loops over every (token, expert) pair for tiny inputs, written
     independently of ``moe_oracle``; it pins the oracle.
+moe_backward
+    numpy float64 backward of the layer (training), pinned by finite
+    differences of ``moe_oracle``'s loss.
+token_rounding
+    tile-aware token rounding of the expert-major metadata (readings TR1-TR4),
+    pinned by a hand-worked example and ``brute.round_tokens_brute``.
 
 Parity status of each function is listed in the module docstrings; every
 function is pinned by at least one ``-m "not gpu"`` test (worked example,
@@ -23,4 +29,4 @@ brute force, closed form or invariant).  The published performance figures
 of the pages are the only item with "parity unpinned".
 """
 
-from . import moe_oracle, brute  # noqa: F401
+from . import moe_oracle, brute, moe_backward, token_rounding  # noqa: F401

@@ -156,3 +156,32 @@ def brute_forward(X, W_r, W_gate, W_up, W_down, K, C, bias=None, logits=None):
     out = {"logits": L_ref, "ids": ids, "gates": gates, "H": H, "O": O, "Y": Y}
     out.update(meta)
     return out
+
+
+def round_tokens_brute(ids, gates, kept_pairs, E, M):
+    """Tile-aware token rounding (readings TR1-TR4 of ``token_rounding``) by
+    brute force.  ``kept_pairs`` is the set of (token, expert) assignments
+    that survived the capacity cut.  Per expert: list its kept (gate, token)
+    pairs, sort them by (gate, -token) with ``sorted``, and remove from the
+    front until the count is the multiple of M that the rule asks for.
+    Returns (counts, surviving pairs sorted by (expert, token))."""
+    ids, g = _mat(ids), _mat(gates)
+    T, K = len(ids), len(ids[0])
+    counts = []
+    survivors = []
+    for e in range(E):
+        mine = []
+        for t in range(T):
+            for k in range(K):
+                if ids[t][k] == e and (t, e) in kept_pairs:
+                    mine.append((g[t][k], -t))
+        c = len(mine)
+        target = c
+        while target >= M and target % M != 0 and (c % M) * 2 < M:
+            target -= 1
+        ranked = sorted(mine)
+        keep = ranked[c - target:] if target < c else ranked
+        toks = sorted(-mt for _, mt in keep)
+        counts.append(len(toks))
+        survivors.extend((e, t) for t in toks)
+    return counts, survivors
