@@ -13,7 +13,9 @@ stages (per-stage medians, same kernels); then the up GEMM alone is timed
 for the roofline, and everything is repeated without the flush (warm,
 labelled as such).  For bf16 workloads the training step (moe_forward_train
 then moe_backward on a seeded dY) is timed the same way and reported under
-"training".  Prints one JSON line.
+"training"; moe_forward with tile-aware token rounding is timed the same way
+under "token_rounding" (with the rows it drops and the row tiles it saves).
+Prints one JSON line.
 
 Extra modes (used for profiler runs):
     --calib-copy BYTES   only run a plain device-to-device copy of BYTES
@@ -23,9 +25,10 @@ Extra modes (used for profiler runs):
                          summary under profiles/ (no GPU needed).
     --no-cpu-baseline    skip the oracle timing on the host cores.
     --warm               skip the cache flush (profiling runs).
-    --no-train           skip the training step (counter runs of the forward GEMMs:
-                         the training forward's up GEMM also writes the
-                         pre-activations).
+    --forward-only       skip the training and token-rounding steps (counter runs
+                         of the forward GEMMs: the training forward's up GEMM
+                         also writes the pre-activations, the rounded forward's
+                         GEMMs see fewer rows); --no-train is the same switch.
 """
 
 from __future__ import annotations
@@ -66,7 +69,7 @@ def parse():
     ap.add_argument("--calib-copy", type=int, default=0)
     ap.add_argument("--pmc-summary", nargs=4, default=None)
     ap.add_argument("--warm", action="store_true")
-    ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--forward-only", "--no-train", dest="forward_only", action="store_true")
     return ap.parse_args()
 
 
@@ -315,7 +318,7 @@ def main():
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in evs]
 
-    train = w.dtype == "bf16" and not args.no_train
+    train = w.dtype == "bf16" and not args.forward_only
     if train:
         dY = mi.draw_grad_output(T, d, torch.bfloat16, seed=0).cuda()
         Y_t = torch.empty_like(Y)
@@ -350,6 +353,32 @@ def main():
         torch.cuda.synchronize()
         return ([e[0].elapsed_time(e[1]) for e in evs], [e[1].elapsed_time(e[2]) for e in evs])
 
+    desc_round = moe.make_desc(T, d, E, K, n, w.dtype, w.capacity_factor,
+                               flags=moe.MOE_FLAG_TOKEN_ROUNDING)
+    ws_round = moe.workspace(desc, moe.MOE_WS_ROUND)
+
+    def run_rounded(cold: bool):
+        """K steps of moe_forward with tile-aware token rounding, and the
+        metadata it produces (counts before and after the rounding)."""
+        for i in range(args.warmup):
+            moe.moe_forward(desc_round, dev["X"], dev["W_r"], dev["bias"], dev["W_gate"],
+                            dev["W_up"], dev["W_down"], Y, ws_fwd)
+        evs = [(ev(), ev()) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            if cold:
+                flush(i)
+            evs[i][0].record(stream)
+            moe.moe_forward(desc_round, dev["X"], dev["W_r"], dev["bias"], dev["W_gate"],
+                            dev["W_up"], dev["W_down"], Y, ws_fwd)
+            evs[i][1].record(stream)
+        moe.moe_route_ws(desc, dev["X"], dev["W_r"], dev["bias"], None, ids, gates, ws_r)
+        moe.moe_permute(desc, ids, counts, offsets, None, perm, inv, ws_p)
+        before = counts.clone()
+        moe.moe_round_tokens(desc, ids, gates, counts, offsets, perm, inv, ws_round)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs], before.cpu(), counts.clone().cpu()
+
     cold = not args.warm
     # ---- timed region: K steps (moe_forward timed; step-wise diagnostics interleaved)
     torch.cuda.synchronize()
@@ -360,6 +389,7 @@ def main():
     up_kernel_ms = run_up_kernel(cold)
     warm_fused_ms, warm_stage_ms = run(False)
     train_ms = run_train(cold) if train else None
+    rounded = None if args.forward_only else run_rounded(cold)
 
     med = statistics.median(fused_ms)
     names = ["route", "permute", "gemm_up", "gemm_down", "combine"]
@@ -454,6 +484,22 @@ def main():
             "bwd_flops_per_unit": "12*d*n per kept row (dA', per-slot dX, dW_down, dW_gate, "
                                   "dW_up) + 2*d*E per token (dW_r)",
             "bwd_ms_p10_p90": [pct(train_ms[1], 0.1), pct(train_ms[1], 0.9)],
+        }
+    tiles = lambda c: int(((c + 255) // 256).sum())
+    pad = lambda c: int(((c + 255) // 256 * 256 - c).sum())
+    if rounded is not None:
+        round_ms, round_before, round_after = rounded
+        r_med = statistics.median(round_ms)
+        rec["token_rounding"] = {
+            "what": "moe_forward with MOE_FLAG_TOKEN_ROUNDING (an expert whose last 256-row tile "
+                    "would be under half full drops its lowest-gate rows to whole tiles); cold",
+            "ms_per_step": r_med,
+            "tokens_per_s": T / (r_med * 1e-3),
+            "speedup_vs_value": med / r_med,
+            "kept_rows": [int(round_before.sum()), int(round_after.sum())],
+            "dropped_frac": 1.0 - float(round_after.sum()) / max(1, int(round_before.sum())),
+            "row_tiles": [tiles(round_before), tiles(round_after)],
+            "padded_rows": [pad(round_before), pad(round_after)],
         }
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_tokens or min(T, 16384)

@@ -93,6 +93,12 @@ typedef struct {
 #define MOE_FLAG_GEMM_TILED 2u
 #define MOE_FLAG_GEMM_SKINNY 4u
 
+/* desc->flags bit for moe_forward: apply tile-aware token rounding
+ * (moe_round_tokens) to the metadata between the permutation and the grouped
+ * GEMMs.  moe_forward with it gives the same bits as route_ws -> permute ->
+ * round_tokens -> grouped_ffn -> combine. */
+#define MOE_FLAG_TOKEN_ROUNDING 8u
+
 /* Workspace selectors for moe_workspace_size.  MOE_WS_SAVED is the state
  * that moe_forward_train keeps for moe_backward (see moe_saved_layout);
  * MOE_WS_BACKWARD is moe_backward's scratch. */
@@ -102,7 +108,8 @@ enum {
   MOE_WS_FORWARD = 2,
   MOE_WS_ROUTE = 3,
   MOE_WS_SAVED = 4,
-  MOE_WS_BACKWARD = 5
+  MOE_WS_BACKWARD = 5,
+  MOE_WS_ROUND = 6
 };
 
 /* Byte offsets of the fields of the saved state (the `saved` buffer of
@@ -197,6 +204,21 @@ moe_status moe_grouped_gemm_down(const moe_desc* desc, const void* H, const int3
                                  const void* W_down, void* O, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* Step 5b, tile-aware token rounding (SonicMoE article §6.5: make per-expert
+ * counts friendlier to the grouped GEMM's row tiles; the page gives no rule,
+ * this is the library's reading).  Updates the metadata that moe_permute
+ * wrote, in place: an expert with c >= 256 kept rows and c mod 256 < 128
+ * keeps 256*floor(c/256) of them (the tiled GEMM's row tile is 256), dropping
+ * its lowest-gate assignments (topk_gates as given; equal gates drop the
+ * larger token first); other experts are unchanged.  Dropped assignments
+ * get inv_slot = -1 like capacity drops (gates are not renormalised); each
+ * expert's surviving slots keep ascending token order; counts and offsets
+ * are rewritten; perm_token entries past the new offsets[E] are unspecified.
+ *   ws: MOE_WS_ROUND bytes. */
+moe_status moe_round_tokens(const moe_desc* desc, const int32_t* topk_ids, const float* topk_gates,
+                            int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                            int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream);
+
 /* Steps 6-7 in one call (moe_grouped_gemm_up then moe_grouped_gemm_down). */
 moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* offsets,
                            const int32_t* perm_token, const void* W_gate, const void* W_up,
@@ -209,7 +231,8 @@ moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* o
 moe_status moe_combine(const moe_desc* desc, const void* O, const float* topk_gates,
                        const int32_t* inv_slot, void* Y, void* stream);
 
-/* Steps 1-8 in one call; every intermediate lives in ws (MOE_WS_FORWARD bytes). */
+/* Steps 1-8 in one call; every intermediate lives in ws (MOE_WS_FORWARD bytes).
+ * Flags: MOE_FLAG_GEMM_TILED / MOE_FLAG_GEMM_SKINNY, MOE_FLAG_TOKEN_ROUNDING. */
 moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
                        const void* W_gate, const void* W_up, const void* W_down, void* Y,
                        void* ws, size_t ws_bytes, void* stream);

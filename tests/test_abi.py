@@ -23,7 +23,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 18
     lib = moe.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -48,14 +48,14 @@ def test_validate_cases():
         (moe.make_desc(16, 100, 8, 2, 256), moe.MOE_ERR_UNSUPPORTED),          # d % 64
         (moe.make_desc(16, 128, 8, 2, 96), moe.MOE_ERR_UNSUPPORTED),           # n % 64
         (moe.make_desc(16, 128, 8, 2, 256, flags=6), moe.MOE_ERR_INVALID_ARG),  # both GEMM paths
-        (moe.make_desc(16, 128, 8, 2, 256, flags=8), moe.MOE_ERR_INVALID_ARG),  # undefined bit
+        (moe.make_desc(16, 128, 8, 2, 256, flags=16), moe.MOE_ERR_INVALID_ARG),  # undefined bit
         (moe.make_desc(16, 128, 8, 2, 256, capacity_factor=float("nan")), moe.MOE_ERR_INVALID_ARG),
         (moe.make_desc(16, 128, 8, 2, 256, capacity_factor=float("inf")), moe.MOE_ERR_INVALID_ARG),
         (moe.make_desc(2 ** 30, 128, 8, 2, 256), moe.MOE_ERR_UNSUPPORTED),     # T*K >= 2^31
     ]
     for desc, want in bad:
         assert moe.moe_validate(desc) == want
-    for f in (1, 2, 4, 5):                                    # defined bits are valid
+    for f in (1, 2, 4, 5, 8, 10):                             # defined bits are valid
         assert moe.moe_validate(moe.make_desc(16, 128, 8, 2, 256, flags=f)) == moe.MOE_OK
     d = moe.make_desc(16, 128, 8, 2, 256)
     d.dtype = 7
@@ -218,3 +218,25 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(moe, "LIB_PATH", "/nonexistent/libmoe_mi355x.so")
     with pytest.raises(RuntimeError, match="no non-HIP fallback"):
         moe.lib()
+
+
+def test_token_rounding_arguments():
+    lib = moe.lib()
+    A = ctypes.c_void_p(1 << 20)
+    desc = moe.make_desc(64, 128, 8, 2, 128)
+    p = ctypes.byref(desc)
+    need = moe.moe_workspace_size(desc, moe.MOE_WS_ROUND)
+    assert need >= 3 * moe.moe_max_rows(desc) * 4
+    assert lib.moe_round_tokens(p, A, A, A, A, A, A, A, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert b"MOE_WS_ROUND" in lib.moe_last_error()
+    assert lib.moe_round_tokens(p, A, None, A, A, A, A, A, need, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_round_tokens(ctypes.byref(moe.make_desc(0, 128, 8, 2, 128)), A, A, A, A, A, A,
+                                A, 0, None) == moe.MOE_OK
+    # the rounding flag belongs to moe_forward, not to the grouped or training calls
+    rd = lambda f: moe.make_desc(0, 128, 8, 2, 128, flags=f)
+    big = 1 << 30
+    assert lib.moe_forward(ctypes.byref(rd(8)), A, A, None, A, A, A, A, A, big, None) == moe.MOE_OK
+    assert lib.moe_grouped_ffn(ctypes.byref(rd(8)), A, A, A, A, A, A, A, A, A, big, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_train(ctypes.byref(rd(8)), A, A, None, A, A, A, A, A, big, A, big,
+                                 None) == moe.MOE_ERR_INVALID_ARG

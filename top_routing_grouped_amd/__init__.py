@@ -6,10 +6,11 @@ library has not been built, every call raises (there is no fallback path).
 
 Low-level functions carry the C names (``moe_route``, ``moe_permute``,
 ``moe_grouped_gemm_up``, ``moe_grouped_gemm_down``, ``moe_grouped_ffn``,
-``moe_combine``, ``moe_forward``, ``moe_forward_train``, ``moe_backward`` and
-the host-only queries) and take torch tensors.  ``route``, ``permute``,
-``grouped_ffn``, ``combine``, ``forward``, ``forward_train`` and ``backward``
-allocate the outputs with torch and call them.
+``moe_round_tokens``, ``moe_combine``, ``moe_forward``, ``moe_forward_train``,
+``moe_backward`` and the host-only queries) and take torch tensors.
+``route``, ``permute``, ``round_tokens``, ``grouped_ffn``, ``combine``,
+``forward``, ``forward_train`` and ``backward`` allocate the outputs with
+torch and call them.
 """
 
 from __future__ import annotations
@@ -34,9 +35,11 @@ MOE_WS_FORWARD = 2
 MOE_WS_ROUTE = 3
 MOE_WS_SAVED = 4
 MOE_WS_BACKWARD = 5
+MOE_WS_ROUND = 6
 MOE_FLAG_TILE_TABLE_READY = 1
 MOE_FLAG_GEMM_TILED = 2
 MOE_FLAG_GEMM_SKINNY = 4
+MOE_FLAG_TOKEN_ROUNDING = 8
 
 
 class MoeError(RuntimeError):
@@ -90,6 +93,7 @@ _SIGNATURES = {
     "moe_combine": [_DP, _VP, _VP, _VP, _VP, _VP],
     "moe_forward": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "moe_saved_layout_of": [_DP, ctypes.POINTER(MoeSavedLayout)],
+    "moe_round_tokens": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "moe_forward_train": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP,
                           ctypes.c_size_t, _VP],
     "moe_backward": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP, _VP, _VP, _VP,
@@ -193,6 +197,12 @@ def moe_permute(desc, ids, counts, offsets, raw_counts, perm_token, inv_slot, ws
                              _stream(stream)), "moe_permute")
 
 
+def moe_round_tokens(desc, ids, gates, counts, offsets, perm_token, inv_slot, ws, stream=None):
+    _check(lib().moe_round_tokens(ctypes.byref(desc), _p(ids), _p(gates), _p(counts), _p(offsets),
+                                  _p(perm_token), _p(inv_slot), _p(ws), _nbytes(ws),
+                                  _stream(stream)), "moe_round_tokens")
+
+
 def moe_grouped_gemm_up(desc, X, offsets, perm_token, W_gate, W_up, H, ws, stream=None):
     _check(lib().moe_grouped_gemm_up(ctypes.byref(desc), _p(X), _p(offsets), _p(perm_token),
                                      _p(W_gate), _p(W_up), _p(H), _p(ws),
@@ -292,6 +302,15 @@ def permute(desc: MoeDesc, ids):
     moe_permute(desc, ids, out["counts"], out["offsets"], out["raw_counts"], out["perm_token"],
                 out["inv_slot"], ws)
     return out
+
+
+def round_tokens(desc: MoeDesc, ids, gates, meta):
+    """Step 5b: tile-aware token rounding of ``permute``'s metadata, in place
+    (counts, offsets, perm_token, inv_slot).  Returns meta."""
+    ws = workspace(desc, MOE_WS_ROUND, ids.device)
+    moe_round_tokens(desc, ids, gates, meta["counts"], meta["offsets"], meta["perm_token"],
+                     meta["inv_slot"], ws)
+    return meta
 
 
 def grouped_ffn(desc: MoeDesc, X, offsets, perm_token, W_gate, W_up, W_down):

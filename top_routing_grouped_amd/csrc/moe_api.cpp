@@ -62,7 +62,8 @@ moe_status check_desc(const moe_desc* d, uint32_t allowed_flags = 0) {
 }
 
 constexpr uint32_t kGemmFlags = MOE_FLAG_TILE_TABLE_READY | MOE_FLAG_GEMM_TILED | MOE_FLAG_GEMM_SKINNY;
-constexpr uint32_t kAllFlags = kGemmFlags;   // every defined bit (host-only queries accept them all)
+// every defined bit (host-only queries accept them all)
+constexpr uint32_t kAllFlags = kGemmFlags | MOE_FLAG_TOKEN_ROUNDING;
 
 bool skinny(const moe::Problem& p, const moe_desc* d) {
   return moe::use_skinny(p, d->flags, MOE_FLAG_GEMM_TILED, MOE_FLAG_GEMM_SKINNY);
@@ -112,6 +113,7 @@ struct ForwardWs {
   int32_t* table;
   void* H;
   void* O;
+  unsigned char* round;
   size_t bytes;
 };
 ForwardWs carve_forward(const moe::Problem& p, unsigned char* base) {
@@ -135,6 +137,7 @@ ForwardWs carve_forward(const moe::Problem& p, unsigned char* base) {
   w.table = reinterpret_cast<int32_t*>(take(moe::tile_table_bytes(p)));
   w.H = take((size_t)p.rows_max * p.n * elem(p));
   w.O = take((size_t)p.rows_max * p.d * elem(p));
+  w.round = take(moe::round_ws_bytes(p, nullptr, nullptr));
   w.bytes = off;
   return w;
 }
@@ -262,6 +265,9 @@ moe_status moe_workspace_size(const moe_desc* desc, int32_t entry, size_t* bytes
     case MOE_WS_BACKWARD:
       *bytes = moe::backward_ws_bytes(p, nullptr, nullptr);
       return MOE_OK;
+    case MOE_WS_ROUND:
+      *bytes = moe::round_ws_bytes(p, nullptr, nullptr);
+      return MOE_OK;
     default:
       return fail(MOE_ERR_INVALID_ARG, "unknown workspace selector");
   }
@@ -333,6 +339,26 @@ moe_status moe_permute(const moe_desc* desc, const int32_t* topk_ids, int32_t* c
     return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_PERMUTE)");
   return run_permute(p, topk_ids, counts, offsets, raw_counts, perm_token, inv_slot,
                      static_cast<unsigned char*>(ws), nullptr, (hipStream_t)stream);
+}
+
+moe_status moe_round_tokens(const moe_desc* desc, const int32_t* topk_ids, const float* topk_gates,
+                            int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                            int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc));
+  if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
+  MOE_TRY(check_ptrs({{topk_ids, "topk_ids"}, {topk_gates, "topk_gates"}, {counts, "counts"},
+                      {offsets, "offsets"}, {perm_token, "perm_token"}, {inv_slot, "inv_slot"},
+                      {ws, "ws"}},
+                     {}));
+  const moe::Problem p = make_problem(desc);
+  if (ws_bytes < moe::round_ws_bytes(p, nullptr, nullptr))
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_ROUND)");
+  moe::RoundWs w;
+  moe::round_ws_bytes(p, &w, static_cast<unsigned char*>(ws));
+  return hip_status(moe::launch_round(p, topk_ids, topk_gates, counts, offsets, perm_token,
+                                      inv_slot, w, (hipStream_t)stream),
+                    "token rounding launch");
 }
 
 moe_status moe_grouped_gemm_up(const moe_desc* desc, const void* X, const int32_t* offsets,
@@ -421,7 +447,7 @@ moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, con
                        const void* W_gate, const void* W_up, const void* W_down, void* Y,
                        void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_GEMM_SKINNY));
+  MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_GEMM_SKINNY | MOE_FLAG_TOKEN_ROUNDING));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
   MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {W_gate, "W_gate"}, {W_up, "W_up"},
                       {W_down, "W_down"}, {Y, "Y"}},
@@ -434,7 +460,18 @@ moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, con
   ForwardWs w = carve_forward(p, static_cast<unsigned char*>(ws));
   MOE_TRY(hip_status(moe::launch_route(p, X, W_r, bias, nullptr, w.ids, w.gates, w.route_partial, s),
                      "route launch"));
-  MOE_TRY(run_permute(p, w.ids, w.counts, w.offsets, nullptr, w.perm, w.inv, w.permute, w.table, s));
+  const bool rounding = (desc->flags & MOE_FLAG_TOKEN_ROUNDING) != 0;
+  MOE_TRY(run_permute(p, w.ids, w.counts, w.offsets, nullptr, w.perm, w.inv, w.permute,
+                      rounding ? nullptr : w.table, s));
+  if (rounding) {
+    moe::RoundWs rw;
+    moe::round_ws_bytes(p, &rw, w.round);
+    MOE_TRY(hip_status(moe::launch_round(p, w.ids, w.gates, w.counts, w.offsets, w.perm, w.inv,
+                                         rw, s),
+                       "token rounding launch"));
+    if (!skinny(p, desc))
+      MOE_TRY(hip_status(moe::launch_tile_table(p, w.offsets, w.table, s), "tile table launch"));
+  }
   if (skinny(p, desc)) {
     MOE_TRY(hip_status(moe::launch_gemm_up_skinny(p, X, w.perm, w.offsets, W_gate, W_up, w.H, s),
                        "grouped GEMM (up, weight-streaming) launch"));

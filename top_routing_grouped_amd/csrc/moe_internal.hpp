@@ -117,6 +117,19 @@ inline bool use_skinny(const Problem& p, uint32_t flags, uint32_t tiled_flag, ui
 hipError_t launch_combine(const Problem& p, const void* O, const float* gates,
                           const int32_t* inv_slot, void* Y, hipStream_t s);
 
+// Tile-aware token rounding of permute's metadata, in place (counts, offsets,
+// perm_token, inv_slot); M = kGemmBM.
+struct RoundWs {
+  int32_t* rank;        // [rows] rank of a surviving slot inside its expert, or -1
+  int32_t* perm_old;    // [rows] perm_token before the rounding
+  int32_t* slot_e;      // [rows] expert of each old slot
+  int32_t* old_total;   // [1]    kept rows before the rounding
+};
+size_t round_ws_bytes(const Problem& p, RoundWs* w, unsigned char* base);
+hipError_t launch_round(const Problem& p, const int32_t* ids, const float* gates, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* inv, const RoundWs& w,
+                        hipStream_t s);
+
 // ---------------------------------------------------------------- backward (bf16)
 // Scratch of the backward, carved from the caller's workspace.
 struct BackwardWs {
