@@ -120,9 +120,9 @@ hipError_t launch_combine(const Problem& p, const void* O, const float* gates,
 // Tile-aware token rounding of permute's metadata, in place (counts, offsets,
 // perm_token, inv_slot); M = kGemmBM.
 struct RoundWs {
+  uint32_t* key;        // [rows] bit pattern of each old slot's gate
+  int32_t* slot_tk;     // [rows] flat (token, k) index of each old slot
   int32_t* rank;        // [rows] rank of a surviving slot inside its expert, or -1
-  int32_t* perm_old;    // [rows] perm_token before the rounding
-  int32_t* slot_e;      // [rows] expert of each old slot
   int32_t* old_total;   // [1]    kept rows before the rounding
 };
 size_t round_ws_bytes(const Problem& p, RoundWs* w, unsigned char* base);

@@ -9,13 +9,15 @@
 // tile.  Dropped assignments become inv_slot = -1 exactly like capacity
 // drops, and each expert's surviving slots keep ascending token order.
 //
-// Three launches over metadata that moe_permute wrote:
-//   select   one workgroup per expert: gathers the gate of each of its slots
-//            (cached in LDS), finds the D-th smallest gate by a 4-pass radix
-//            select on the gates' bit patterns (non-negative floats order as
-//            their bits), then one ordered sweep assigns each surviving slot
-//            its rank inside the segment; writes the new count, a copy of
-//            the segment's perm_token and the slot's expert;
+// Four launches over metadata that moe_permute wrote:
+//   keys     one thread per (token, k): a kept entry writes its gate's bit
+//            pattern and its (token, k) index at its slot (coalesced reads);
+//   select   one workgroup per expert: reads its segment's keys (cached in
+//            LDS), finds the D-th smallest by a 4-pass radix select on the
+//            bit patterns (non-negative floats order as their bits; each
+//            pass an LDS histogram and a scan of its 256 bins), then
+//            one ordered sweep with wave-ballot prefix counts gives each
+//            surviving slot its rank inside the segment; writes the count;
 //   offsets  one workgroup: exclusive scan of the new counts;
 //   scatter  one thread per old slot: moves survivors to their new slot and
 //            rewrites inv_slot (the new slot, or -1).
@@ -32,43 +34,70 @@ __device__ __forceinline__ int rounded(int c) {
   return (c >= kGemmBM && (c % kGemmBM) < kGemmBM / 2) ? c - c % kGemmBM : c;
 }
 
-// Bit pattern of the gate of (token t, expert e): the entry of t's list that
-// holds e (the router lists distinct experts).
-__device__ __forceinline__ uint32_t gate_key(const int32_t* ids, const float* gates, int64_t t,
-                                             int K, int e) {
-  const int32_t* row = ids + t * K;
-  int k = 0;
-  for (int j = 0; j < K; ++j)
-    if (row[j] == e) { k = j; break; }
-  return __float_as_uint(gates[t * K + k]);
+// Exclusive prefix count of `flag` over the workgroup's 256 threads, and the
+// total: a ballot per wave, then the 4 wave totals through LDS.
+__device__ int wg_count_prefix(bool flag, int* lds, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t m = __ballot(flag);
+  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) lds[w] = __popcll(m);
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int j = 0; j < kThreads / 64; ++j) {
+    const int v = lds[j];
+    tot += v;
+    before += j < w ? v : 0;
+  }
+  __syncthreads();                      // lds is reused by the next call
+  *total = tot;
+  return before + in_wave;
 }
 
 // Exclusive scan of one value per thread over the 256 threads; returns the
-// prefix, *total the sum.  Every thread calls it.
+// prefix, *total the sum.  Every thread calls it.  Shuffles inside a wave,
+// then the 4 wave totals through LDS.
 __device__ int wg_exscan(int v, int* lds, int* total) {
-  const int tid = threadIdx.x;
-  lds[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int x = tid >= off ? lds[tid - off] : 0;
-    __syncthreads();
-    lds[tid] += x;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    x += lane >= o ? y : 0;
   }
-  const int incl = lds[tid];
-  *total = lds[kThreads - 1];
+  if (lane == 63) lds[w] = x;
   __syncthreads();
-  return incl - v;
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int j = 0; j < kThreads / 64; ++j) {
+    const int t = lds[j];
+    tot += t;
+    before += j < w ? t : 0;
+  }
+  __syncthreads();                      // lds is reused by the next call
+  *total = tot;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kThreads) void round_keys_kernel(const float* __restrict__ gates,
+                                                              const int32_t* __restrict__ inv,
+                                                              uint32_t* __restrict__ key,
+                                                              int32_t* __restrict__ slot_tk,
+                                                              int64_t TK) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= TK) return;
+  const int s = inv[i];
+  if (s < 0) return;
+  key[s] = __float_as_uint(gates[i]);
+  slot_tk[s] = (int32_t)i;
 }
 
 __global__ __launch_bounds__(kThreads) void round_select_kernel(
-    const int32_t* __restrict__ ids, const float* __restrict__ gates,
     int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ perm, int32_t* __restrict__ rank, int32_t* __restrict__ perm_old,
-    int32_t* __restrict__ slot_e, int64_t T, int K) {
+    const uint32_t* __restrict__ key, int32_t* __restrict__ rank) {
   __shared__ uint32_t keys[kCacheKeys];
   __shared__ int hist[256];
-  __shared__ int scan_tmp[kThreads];
+  __shared__ int red[kThreads / 64];
   __shared__ int bcast[2];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
@@ -76,22 +105,16 @@ __global__ __launch_bounds__(kThreads) void round_select_kernel(
   const int c = offsets[e + 1] - off;
   const int r = rounded(c);
   const int D = c - r;                            // assignments to drop (0 <= D < M/2)
-  const bool cached = c <= kCacheKeys;
-  for (int i = tid; i < c; i += kThreads) {
-    const int t = perm[off + i];
-    perm_old[off + i] = t;
-    slot_e[off + i] = e;
-    if (D > 0 && cached) keys[i] = gate_key(ids, gates, t, K, e);
-  }
   if (tid == 0) counts[e] = r;
   if (D == 0) {
     for (int i = tid; i < c; i += kThreads) rank[off + i] = i;
     return;
   }
+  const bool cached = c <= kCacheKeys;
+  if (cached)
+    for (int i = tid; i < c; i += kThreads) keys[i] = key[off + i];
   __syncthreads();
-  auto key_at = [&](int i) -> uint32_t {
-    return cached ? keys[i] : gate_key(ids, gates, perm[off + i], K, e);
-  };
+  auto key_at = [&](int i) -> uint32_t { return cached ? keys[i] : key[off + i]; };
 
   // radix select: the D-th smallest key (1-based), 8 bits per pass
   uint32_t prefix = 0, mask = 0;
@@ -104,14 +127,14 @@ __global__ __launch_bounds__(kThreads) void round_select_kernel(
       if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0, b = 0;
-      for (; b < 255; ++b) {
-        if (cum + hist[b] >= want) break;
-        cum += hist[b];
-      }
-      bcast[0] = b;
-      bcast[1] = want - cum;
+    // the bin holding the want-th key: the one thread whose prefix range
+    // [excl, excl + hist) contains it
+    int unused = 0;
+    const int h = hist[tid];
+    const int excl = wg_exscan(h, red, &unused);
+    if (excl < want && want <= excl + h) {
+      bcast[0] = tid;
+      bcast[1] = want - excl;
     }
     __syncthreads();
     const int b = bcast[0];
@@ -128,12 +151,12 @@ __global__ __launch_bounds__(kThreads) void round_select_kernel(
   for (int i0 = 0; i0 < c; i0 += kThreads) {
     const int i = i0 + tid;
     const uint32_t k = i < c ? key_at(i) : 0u;
-    const int is_tie = (i < c && k == prefix) ? 1 : 0;
+    const bool is_tie = i < c && k == prefix;
     int tie_total = 0;
-    const int tie_idx = tie_base + wg_exscan(is_tie, scan_tmp, &tie_total);
-    const int keep = (i < c && (k > prefix || (is_tie && tie_idx < keep_ties))) ? 1 : 0;
+    const int tie_idx = tie_base + wg_count_prefix(is_tie, red, &tie_total);
+    const bool keep = i < c && (k > prefix || (is_tie && tie_idx < keep_ties));
     int kept_total = 0;
-    const int kr = kept_base + wg_exscan(keep, scan_tmp, &kept_total);
+    const int kr = kept_base + wg_count_prefix(keep, red, &kept_total);
     if (i < c) rank[off + i] = keep ? kr : -1;
     tie_base += tie_total;
     kept_base += kept_total;
@@ -144,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void round_offsets_kernel(const int32_t* 
                                                                  int32_t* __restrict__ offsets,
                                                                  int32_t* __restrict__ old_total,
                                                                  int E) {
-  __shared__ int tmp[kThreads];
+  __shared__ int tmp[kThreads / 64];
   const int tid = threadIdx.x;
   const int before = offsets[E];
   int total = 0;
@@ -158,23 +181,19 @@ __global__ __launch_bounds__(kThreads) void round_offsets_kernel(const int32_t* 
 
 __global__ __launch_bounds__(kThreads) void round_scatter_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ rank,
-    const int32_t* __restrict__ perm_old, const int32_t* __restrict__ slot_e,
-    const int32_t* __restrict__ old_total, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int64_t rows, int K) {
+    const int32_t* __restrict__ slot_tk, const int32_t* __restrict__ old_total,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    int64_t rows, int K) {
   const int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (s >= rows || s >= old_total[0]) return;
-  const int e = slot_e[s];
-  const int t = perm_old[s];
+  const int tk = slot_tk[s];
   const int r = rank[s];
-  int k = 0;
-  for (int j = 0; j < K; ++j)
-    if (ids[(int64_t)t * K + j] == e) { k = j; break; }
   int ns = -1;
   if (r >= 0) {
-    ns = offsets[e] + r;
-    perm[ns] = t;
+    ns = offsets[ids[tk]] + r;
+    perm[ns] = tk / K;
   }
-  inv[(int64_t)t * K + k] = ns;
+  inv[tk] = ns;
 }
 
 }  // namespace
@@ -188,9 +207,9 @@ size_t round_ws_bytes(const Problem& p, RoundWs* w, unsigned char* base) {
   };
   const size_t rows = (size_t)(p.rows_max > 0 ? p.rows_max : 1);
   RoundWs ws{};
+  ws.key = reinterpret_cast<uint32_t*>(take(rows * 4));
+  ws.slot_tk = reinterpret_cast<int32_t*>(take(rows * 4));
   ws.rank = reinterpret_cast<int32_t*>(take(rows * 4));
-  ws.perm_old = reinterpret_cast<int32_t*>(take(rows * 4));
-  ws.slot_e = reinterpret_cast<int32_t*>(take(rows * 4));
   ws.old_total = reinterpret_cast<int32_t*>(take(4));
   if (w) *w = ws;
   return off;
@@ -199,9 +218,14 @@ size_t round_ws_bytes(const Problem& p, RoundWs* w, unsigned char* base) {
 hipError_t launch_round(const Problem& p, const int32_t* ids, const float* gates, int32_t* counts,
                         int32_t* offsets, int32_t* perm, int32_t* inv, const RoundWs& w,
                         hipStream_t s) {
-  hipLaunchKernelGGL(round_select_kernel, dim3((unsigned)p.E), dim3(kThreads), 0, s, ids, gates,
-                     counts, offsets, perm, w.rank, w.perm_old, w.slot_e, p.T, p.K);
+  const int64_t TK = p.T * (int64_t)p.K;
+  hipLaunchKernelGGL(round_keys_kernel, dim3((unsigned)((TK + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, gates, inv, w.key, w.slot_tk, TK);
   hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(round_select_kernel, dim3((unsigned)p.E), dim3(kThreads), 0, s, counts,
+                     offsets, w.key, w.rank);
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(round_offsets_kernel, dim3(1), dim3(kThreads), 0, s, counts, offsets,
                      w.old_total, p.E);
@@ -209,8 +233,8 @@ hipError_t launch_round(const Problem& p, const int32_t* ids, const float* gates
   if (err != hipSuccess) return err;
   const int64_t rows = p.rows_max;
   hipLaunchKernelGGL(round_scatter_kernel, dim3((unsigned)((rows + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, ids, w.rank, w.perm_old, w.slot_e, w.old_total,
-                     offsets, perm, inv, rows, p.K);
+                     dim3(kThreads), 0, s, ids, w.rank, w.slot_tk, w.old_total, offsets, perm,
+                     inv, rows, p.K);
   return hipGetLastError();
 }
 
