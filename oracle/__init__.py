@@ -22,6 +22,9 @@ moe_backward
 token_rounding
     tile-aware token rounding of the expert-major metadata (readings TR1-TR4),
     pinned by a hand-worked example and ``brute.round_tokens_brute``.
+omni_oracle
+    the atomic-expert layer with a Cartesian router (readings O1-O7), pinned
+    by ``brute.brute_omni_forward`` and the exactness of the pruned search.
 
 Parity status of each function is listed in the module docstrings; every
 function is pinned by at least one ``-m "not gpu"`` test (worked example,
@@ -29,4 +32,4 @@ brute force, closed form or invariant).  The published performance figures
 of the pages are the only item with "parity unpinned".
 """
 
-from . import moe_oracle, brute, moe_backward, token_rounding  # noqa: F401
+from . import moe_oracle, brute, moe_backward, token_rounding, omni_oracle  # noqa: F401

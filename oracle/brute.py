@@ -185,3 +185,40 @@ def round_tokens_brute(ids, gates, kept_pairs, E, M):
         counts.append(len(toks))
         survivors.extend((e, t) for t in toks)
     return counts, survivors
+
+
+def brute_omni_forward(X, W_r, W_c, W_in, W_out, K):
+    """Atomic-expert layer with a Cartesian router ([P2] §2.1-2.2; readings
+    O1-O6 of ``omni_oracle``) by brute force: every (row, column) pair of the
+    grid is scored and the whole list is sorted; each selected expert is
+    evaluated with scalar loops.  Returns (ids, gates, Y) as lists."""
+    X, Wr, Wc, Win, Wout = _mat(X), _mat(W_r), _mat(W_c), _mat(W_in), _mat(W_out)
+    T, d = len(X), len(X[0])
+    Nr, Nc = len(Wr[0]), len(Wc[0])
+
+    def logsm(row):
+        m = max(row)
+        z = sum(math.exp(v - m) for v in row)
+        return [v - m - math.log(z) for v in row]
+
+    ids_all, gates_all, Y = [], [], []
+    for t in range(T):
+        pr = [sum(X[t][i] * Wr[i][r] for i in range(d)) for r in range(Nr)]
+        pc = [sum(X[t][i] * Wc[i][c] for i in range(d)) for c in range(Nc)]
+        lr, lc = logsm(pr), logsm(pc)
+        pairs = sorted((-(lr[r] + lc[c]), r * Nc + c) for r in range(Nr) for c in range(Nc))
+        sel = pairs[:K]
+        ids = [i for _, i in sel]
+        ex = [math.exp(-s) for s, _ in sel]
+        z = sum(ex)
+        gates = [v / z for v in ex]
+        y = [0.0] * d
+        for g, e in zip(gates, ids):
+            dot = sum(X[t][i] * Win[e][i] for i in range(d))
+            h = dot / (1.0 + math.exp(-dot))
+            for i in range(d):
+                y[i] += g * h * Wout[e][i]
+        ids_all.append(ids)
+        gates_all.append(gates)
+        Y.append(y)
+    return ids_all, gates_all, Y
