@@ -275,6 +275,54 @@ moe_status moe_backward(const moe_desc* desc, const void* X, const void* W_r, co
                         size_t saved_bytes, void* dX, float* dW_r, float* dW_gate, float* dW_up,
                         float* dW_down, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- atomic experts
+ * A second layer type (page "MoE 的两个上游创新：Routing-Free 与 OmniMoE",
+ * part 2): N = Nr*Nc experts, each two d-vectors, E_i(x) = silu(x . w_in_i)
+ * w_out_i (§2.1; sigma taken as SiLU, the routing weight playing SwiGLU's
+ * gating role), chosen by a Cartesian-product router (§2.2) and executed
+ * expert by expert in (expert, token) order (§2.3).  bf16 only.
+ *   X[T,d], W_r[d,Nr], W_c[d,Nc], W_in/W_out[N,d] (row i = expert i), Y[T,d].
+ * Expert id i = i_r*Nc + i_c; score S = ls_r[i_r] + ls_c[i_c] with ls the
+ * fp32 log-softmax of x W over each axis; the K largest S by (S desc, id
+ * asc); gates = softmax over the K selected S.  The search keeps the top
+ * min(K, Nr) rows and min(K, Nc) columns (the released code's pruning,
+ * which returns the full search's result) and then only pairs whose axis
+ * ranks satisfy (i+1)(j+1) <= K.  No capacity: every task is kept.
+ * Supported: 1 <= Nr, Nc <= 256, 1 <= K <= min(64, Nr*Nc), d a multiple of
+ * 64 up to 4096, T*K < 2^31, dtype MOE_BF16, flags 0. */
+typedef struct {
+  int64_t T;
+  int32_t d, Nr, Nc, K;
+  int32_t dtype;            /* must be MOE_BF16 */
+  uint32_t flags;           /* must be 0 */
+} moe_omni_desc;
+
+enum { MOE_OMNI_WS_ROUTE = 0, MOE_OMNI_WS_PERMUTE = 1, MOE_OMNI_WS_FORWARD = 2 };
+
+/* Host only: checks the description; bytes of workspace for an entry point. */
+moe_status moe_omni_validate(const moe_omni_desc* desc);
+moe_status moe_omni_workspace_size(const moe_omni_desc* desc, int32_t entry, size_t* bytes);
+
+/* Router: ids[T,K] int32 (best first), gates[T,K] fp32; ls_r[T,Nr] and
+ * ls_c[T,Nc] (fp32 log-softmax rows the selection used) or NULL.
+ * ws: MOE_OMNI_WS_ROUTE bytes. */
+moe_status moe_omni_route(const moe_omni_desc* desc, const void* X, const void* W_r,
+                          const void* W_c, float* ls_r, float* ls_c, int32_t* ids, float* gates,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* (expert, token) order over the N experts: counts[N], offsets[N+1],
+ * perm_token[T*K] (slot -> token, ascending tokens inside an expert),
+ * inv_slot[T,K] (entry -> slot).  ws: MOE_OMNI_WS_PERMUTE bytes. */
+moe_status moe_omni_permute(const moe_omni_desc* desc, const int32_t* ids, int32_t* counts,
+                            int32_t* offsets, int32_t* perm_token, int32_t* inv_slot, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* The whole layer: Y[t] = sum over k of g[t,k] silu(X[t] . w_in[id]) w_out[id]
+ * (fp32 in k order, rounded to bf16).  ws: MOE_OMNI_WS_FORWARD bytes. */
+moe_status moe_omni_forward(const moe_omni_desc* desc, const void* X, const void* W_r,
+                            const void* W_c, const void* W_in, const void* W_out, void* Y,
+                            void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -113,6 +113,52 @@ def draw_grad_output(T: int, d: int, dtype=torch.bfloat16, seed: int = 0) -> tor
     return _randn(g, (T, d), 1).to(dtype)
 
 
+# ---------------------------------------------------------------- atomic experts
+# Layers of N = Nr*Nc rank-1 experts with a Cartesian router (the OmniMoE
+# design).  Recipe: a CPU generator seeded with ``seed`` draws, in this order,
+# X[T,d] ~ N(0,1), W_r[d,Nr] and W_c[d,Nc] ~ N(0,1/d), W_in[N,d] ~ N(0,1/d)
+# and W_out[N,d] ~ N(0,1/K) (each output sums K expert rows); then bf16.
+
+
+@dataclass(frozen=True)
+class OmniWorkload:
+    name: str
+    T: int
+    d: int
+    Nr: int
+    Nc: int
+    K: int
+    note: str = field(default="", compare=False)
+
+
+OMNI_WORKLOADS = {
+    w.name: w for w in [
+        OmniWorkload("omni_small_bf16", 300, 128, 16, 16, 8, note="parity-sized atomic-expert layer"),
+        OmniWorkload("omni_bf16", 4096, 1024, 256, 256, 64,
+                     note="N = 65536 atomic experts, K = 64, reuse L*K/N = 4"),
+    ]
+}
+
+
+def draw_omni(T, d, Nr, Nc, K, seed=0, dtype=torch.bfloat16):
+    g = torch.Generator("cpu").manual_seed(seed)
+    N = Nr * Nc
+    return {
+        "X": _randn(g, (T, d), 1).to(dtype),
+        "W_r": _randn(g, (d, Nr), d).to(dtype),
+        "W_c": _randn(g, (d, Nc), d).to(dtype),
+        "W_in": _randn(g, (N, d), d).to(dtype),
+        "W_out": _randn(g, (N, d), K).to(dtype),
+    }
+
+
+def make_omni_inputs(name: str, seed: int = 0) -> dict:
+    w = OMNI_WORKLOADS[name]
+    out = draw_omni(w.T, w.d, w.Nr, w.Nc, w.K, seed)
+    out["workload"] = w
+    return out
+
+
 def to_numpy_f32(t: torch.Tensor):
     """Exact float32 numpy copy of a bf16/fp32 tensor (for the oracle)."""
     return t.detach().to("cpu", torch.float32).numpy()

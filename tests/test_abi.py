@@ -23,7 +23,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 23
     lib = moe.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -240,3 +240,32 @@ def test_token_rounding_arguments():
         moe.MOE_ERR_INVALID_ARG
     assert lib.moe_forward_train(ctypes.byref(rd(8)), A, A, None, A, A, A, A, A, big, A, big,
                                  None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_atomic_expert_descriptor_checks():
+    ok = moe.make_omni_desc(4096, 1024, 256, 256, 64)
+    assert moe.moe_omni_validate(ok) == moe.MOE_OK
+    bad = [
+        (moe.make_omni_desc(16, 1024, 257, 4, 4), moe.MOE_ERR_UNSUPPORTED),   # axis above 256
+        (moe.make_omni_desc(16, 1024, 16, 16, 65), moe.MOE_ERR_UNSUPPORTED),  # K above 64
+        (moe.make_omni_desc(16, 1024, 2, 2, 5), moe.MOE_ERR_INVALID_ARG),     # K > N
+        (moe.make_omni_desc(16, 1024, 0, 2, 1), moe.MOE_ERR_INVALID_ARG),
+        (moe.make_omni_desc(16, 96, 4, 4, 2), moe.MOE_ERR_UNSUPPORTED),       # d % 64
+        (moe.make_omni_desc(16, 8192, 4, 4, 2), moe.MOE_ERR_UNSUPPORTED),     # d above 4096
+        (moe.make_omni_desc(16, 1024, 4, 4, 2, "fp32"), moe.MOE_ERR_UNSUPPORTED),
+        (moe.make_omni_desc(16, 1024, 4, 4, 2, flags=1), moe.MOE_ERR_INVALID_ARG),
+        (moe.make_omni_desc(-1, 1024, 4, 4, 2), moe.MOE_ERR_INVALID_ARG),
+    ]
+    for desc, want in bad:
+        assert moe.moe_omni_validate(desc) == want
+    fw = moe.moe_omni_workspace_size(ok, moe.MOE_OMNI_WS_FORWARD)
+    assert fw > moe.moe_omni_workspace_size(ok, moe.MOE_OMNI_WS_ROUTE)
+    assert fw > moe.moe_omni_workspace_size(ok, moe.MOE_OMNI_WS_PERMUTE)
+    lib = moe.lib()
+    A = ctypes.c_void_p(1 << 20)
+    p = ctypes.byref(ok)
+    assert lib.moe_omni_forward(p, A, A, A, A, A, A, A, 16, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_omni_route(p, A, A, None, None, None, A, A, A, 1 << 30, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    zero = moe.make_omni_desc(0, 1024, 4, 4, 2)
+    assert lib.moe_omni_forward(ctypes.byref(zero), A, A, A, A, A, A, A, 0, None) == moe.MOE_OK

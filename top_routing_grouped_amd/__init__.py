@@ -68,6 +68,30 @@ def make_desc(T, d, E, K, n, dtype="bf16", capacity_factor=0.0, flags=0) -> MoeD
     return MoeDesc(int(T), int(d), int(E), int(K), int(n), code, float(capacity_factor), int(flags))
 
 
+class MoeOmniDesc(ctypes.Structure):
+    """Mirror of ``moe_omni_desc``."""
+
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("d", ctypes.c_int32),
+        ("Nr", ctypes.c_int32),
+        ("Nc", ctypes.c_int32),
+        ("K", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+MOE_OMNI_WS_ROUTE = 0
+MOE_OMNI_WS_PERMUTE = 1
+MOE_OMNI_WS_FORWARD = 2
+
+
+def make_omni_desc(T, d, Nr, Nc, K, dtype="bf16", flags=0) -> MoeOmniDesc:
+    code = {"bf16": MOE_BF16, "fp32": MOE_F32, MOE_BF16: MOE_BF16, MOE_F32: MOE_F32}[dtype]
+    return MoeOmniDesc(int(T), int(d), int(Nr), int(Nc), int(K), code, int(flags))
+
+
 class MoeSavedLayout(ctypes.Structure):
     """Mirror of ``moe_saved_layout``: byte offsets of the saved state's fields."""
 
@@ -94,6 +118,12 @@ _SIGNATURES = {
     "moe_forward": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "moe_saved_layout_of": [_DP, ctypes.POINTER(MoeSavedLayout)],
     "moe_round_tokens": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "moe_omni_validate": [ctypes.c_void_p],
+    "moe_omni_workspace_size": [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
+    "moe_omni_route": [ctypes.c_void_p, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
+                       _VP],
+    "moe_omni_permute": [ctypes.c_void_p, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "moe_omni_forward": [ctypes.c_void_p, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "moe_forward_train": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP,
                           ctypes.c_size_t, _VP],
     "moe_backward": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP, _VP, _VP, _VP,
@@ -399,3 +429,84 @@ def backward(desc: MoeDesc, saved, X, W_r, W_gate, W_up, W_down, dY, ws=None):
     moe_backward(desc, X, W_r, W_gate, W_up, W_down, dY, saved, out["dX"], out["dW_r"],
                  out["dW_gate"], out["dW_up"], out["dW_down"], ws)
     return out
+
+
+# ---------------------------------------------------------------- atomic experts
+
+def moe_omni_validate(desc: MoeOmniDesc) -> int:
+    return lib().moe_omni_validate(ctypes.byref(desc))
+
+
+def moe_omni_workspace_size(desc: MoeOmniDesc, entry: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().moe_omni_workspace_size(ctypes.byref(desc), int(entry), ctypes.byref(out)),
+           "moe_omni_workspace_size")
+    return out.value
+
+
+def moe_omni_route(desc, X, W_r, W_c, ls_r, ls_c, ids, gates, ws, stream=None):
+    _check(lib().moe_omni_route(ctypes.byref(desc), _p(X), _p(W_r), _p(W_c), _p(ls_r), _p(ls_c),
+                                _p(ids), _p(gates), _p(ws), _nbytes(ws), _stream(stream)),
+           "moe_omni_route")
+
+
+def moe_omni_permute(desc, ids, counts, offsets, perm_token, inv_slot, ws, stream=None):
+    _check(lib().moe_omni_permute(ctypes.byref(desc), _p(ids), _p(counts), _p(offsets),
+                                  _p(perm_token), _p(inv_slot), _p(ws), _nbytes(ws),
+                                  _stream(stream)), "moe_omni_permute")
+
+
+def moe_omni_forward(desc, X, W_r, W_c, W_in, W_out, Y, ws, stream=None):
+    _check(lib().moe_omni_forward(ctypes.byref(desc), _p(X), _p(W_r), _p(W_c), _p(W_in),
+                                  _p(W_out), _p(Y), _p(ws), _nbytes(ws), _stream(stream)),
+           "moe_omni_forward")
+
+
+def _omni_desc_for(X, W_r, W_c, K):
+    return make_omni_desc(X.shape[0], X.shape[1], W_r.shape[1], W_c.shape[1], K)
+
+
+def _omni_ws(desc, entry, device):
+    import torch
+    return torch.empty(max(16, moe_omni_workspace_size(desc, entry)), dtype=torch.uint8,
+                       device=device)
+
+
+def omni_route(X, W_r, W_c, K):
+    """Atomic-expert router.  Returns (ids [T,K], gates [T,K], ls_r [T,Nr], ls_c [T,Nc])."""
+    import torch
+    desc = _omni_desc_for(X, W_r, W_c, K)
+    T, dev = X.shape[0], X.device
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, K), dtype=torch.float32, device=dev)
+    ls_r = torch.empty((T, W_r.shape[1]), dtype=torch.float32, device=dev)
+    ls_c = torch.empty((T, W_c.shape[1]), dtype=torch.float32, device=dev)
+    moe_omni_route(desc, X, W_r, W_c, ls_r, ls_c, ids, gates, _omni_ws(desc, MOE_OMNI_WS_ROUTE, dev))
+    return ids, gates, ls_r, ls_c
+
+
+def omni_permute(desc: MoeOmniDesc, ids):
+    """(expert, token) order over the N experts: dict(counts, offsets, perm_token, inv_slot)."""
+    import torch
+    dev = ids.device
+    N = desc.Nr * desc.Nc
+    out = {
+        "counts": torch.empty(N, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(N + 1, dtype=torch.int32, device=dev),
+        "perm_token": torch.empty(max(1, desc.T * desc.K), dtype=torch.int32, device=dev),
+        "inv_slot": torch.empty((desc.T, desc.K), dtype=torch.int32, device=dev),
+    }
+    moe_omni_permute(desc, ids, out["counts"], out["offsets"], out["perm_token"], out["inv_slot"],
+                     _omni_ws(desc, MOE_OMNI_WS_PERMUTE, dev))
+    return out
+
+
+def omni_forward(X, W_r, W_c, W_in, W_out, K, ws=None):
+    """The atomic-expert layer in one library call.  Returns Y [T, d]."""
+    import torch
+    desc = _omni_desc_for(X, W_r, W_c, K)
+    if ws is None:
+        ws = _omni_ws(desc, MOE_OMNI_WS_FORWARD, X.device)
+    Y = torch.empty_like(X)
+    moe_omni_forward(desc, X, W_r, W_c, W_in, W_out, Y, ws)
+    return Y

@@ -20,7 +20,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["route.hip", "permute.hip", "round.hip", "gemm.hip", "gemm_skinny.hip", "gemm_bwd.hip",
+SOURCES = ["route.hip", "permute.hip", "round.hip", "omni.hip", "gemm.hip", "gemm_skinny.hip",
+           "gemm_bwd.hip",
            "combine.hip",
            "moe_api.cpp"]
 

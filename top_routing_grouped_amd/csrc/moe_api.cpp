@@ -219,9 +219,153 @@ moe_status run_permute(const moe::Problem& p, const int32_t* ids, int32_t* count
                     "scatter launch");
 }
 
+moe_status check_omni(const moe_omni_desc* d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is NULL");
+  if (d->flags != 0) return fail(MOE_ERR_INVALID_ARG, "desc->flags must be 0");
+  if (d->T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0");
+  if (d->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the atomic-expert layer is bf16 only");
+  if (d->Nr < 1 || d->Nc < 1) return fail(MOE_ERR_INVALID_ARG, "Nr and Nc must be >= 1");
+  if (d->Nr > 256 || d->Nc > 256) return fail(MOE_ERR_UNSUPPORTED, "Nr and Nc above 256 are not supported");
+  if (d->K < 1 || (int64_t)d->K > (int64_t)d->Nr * d->Nc)
+    return fail(MOE_ERR_INVALID_ARG, "K must satisfy 1 <= K <= Nr*Nc");
+  if (d->K > 64) return fail(MOE_ERR_UNSUPPORTED, "K above 64 is not supported");
+  if (d->d < 64 || d->d % 64 != 0 || d->d > 4096)
+    return fail(MOE_ERR_UNSUPPORTED, "d must be a multiple of 64 up to 4096");
+  if (d->T * (int64_t)d->K >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T*K must stay below 2^31 (int32 slots)");
+  return MOE_OK;
+}
+
+moe::OmniProblem omni_problem(const moe_omni_desc* d) {
+  moe::OmniProblem p;
+  p.T = d->T;
+  p.d = d->d;
+  p.Nr = d->Nr;
+  p.Nc = d->Nc;
+  p.K = d->K;
+  return p;
+}
+
+struct OmniForwardWs {
+  unsigned char* route;
+  int32_t* ids;
+  float* gates;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+  unsigned char* permute;
+  float* a;
+  size_t bytes;
+};
+OmniForwardWs carve_omni_forward(const moe::OmniProblem& p, unsigned char* base) {
+  OmniForwardWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    unsigned char* ptr = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return ptr;
+  };
+  const size_t tk = (size_t)p.T * p.K, N = (size_t)p.Nr * p.Nc;
+  w.route = take(moe::omni_route_ws_bytes(p, nullptr, nullptr));
+  w.ids = reinterpret_cast<int32_t*>(take(tk * 4));
+  w.gates = reinterpret_cast<float*>(take(tk * 4));
+  w.counts = reinterpret_cast<int32_t*>(take(N * 4));
+  w.offsets = reinterpret_cast<int32_t*>(take((N + 1) * 4));
+  w.perm = reinterpret_cast<int32_t*>(take(tk * 4));
+  w.inv = reinterpret_cast<int32_t*>(take(tk * 4));
+  w.permute = take(moe::omni_permute_ws_bytes(p, nullptr, nullptr));
+  w.a = reinterpret_cast<float*>(take(tk * 4));
+  w.bytes = off;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
+
+moe_status moe_omni_validate(const moe_omni_desc* desc) {
+  g_last_error.clear();
+  return check_omni(desc);
+}
+
+moe_status moe_omni_workspace_size(const moe_omni_desc* desc, int32_t entry, size_t* bytes) {
+  MOE_TRY(check_omni(desc));
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  const moe::OmniProblem p = omni_problem(desc);
+  switch (entry) {
+    case MOE_OMNI_WS_ROUTE: *bytes = moe::omni_route_ws_bytes(p, nullptr, nullptr); return MOE_OK;
+    case MOE_OMNI_WS_PERMUTE: *bytes = moe::omni_permute_ws_bytes(p, nullptr, nullptr); return MOE_OK;
+    case MOE_OMNI_WS_FORWARD: *bytes = carve_omni_forward(p, nullptr).bytes; return MOE_OK;
+    default: return fail(MOE_ERR_INVALID_ARG, "unknown workspace selector");
+  }
+}
+
+moe_status moe_omni_route(const moe_omni_desc* desc, const void* X, const void* W_r,
+                          const void* W_c, float* ls_r, float* ls_c, int32_t* ids, float* gates,
+                          void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_omni(desc));
+  if (desc->T == 0) return MOE_OK;
+  MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {W_c, "W_c"}, {ids, "ids"}, {gates, "gates"},
+                      {ws, "ws"}},
+                     {{ls_r, "ls_r"}, {ls_c, "ls_c"}}));
+  const moe::OmniProblem p = omni_problem(desc);
+  if (ws_bytes < moe::omni_route_ws_bytes(p, nullptr, nullptr))
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_omni_workspace_size(MOE_OMNI_WS_ROUTE)");
+  moe::OmniRouteWs w;
+  moe::omni_route_ws_bytes(p, &w, static_cast<unsigned char*>(ws));
+  return hip_status(moe::launch_omni_route(p, X, W_r, W_c, ls_r, ls_c, ids, gates, w,
+                                           (hipStream_t)stream),
+                    "atomic-expert router launch");
+}
+
+moe_status moe_omni_permute(const moe_omni_desc* desc, const int32_t* ids, int32_t* counts,
+                            int32_t* offsets, int32_t* perm_token, int32_t* inv_slot, void* ws,
+                            size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_omni(desc));
+  if (desc->T == 0) return MOE_OK;
+  MOE_TRY(check_ptrs({{ids, "ids"}, {counts, "counts"}, {offsets, "offsets"},
+                      {perm_token, "perm_token"}, {inv_slot, "inv_slot"}, {ws, "ws"}},
+                     {}));
+  const moe::OmniProblem p = omni_problem(desc);
+  if (ws_bytes < moe::omni_permute_ws_bytes(p, nullptr, nullptr))
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_omni_workspace_size(MOE_OMNI_WS_PERMUTE)");
+  moe::OmniPermuteWs w;
+  moe::omni_permute_ws_bytes(p, &w, static_cast<unsigned char*>(ws));
+  return hip_status(moe::launch_omni_permute(p, ids, counts, offsets, perm_token, inv_slot, w,
+                                             (hipStream_t)stream),
+                    "atomic-expert permutation launch");
+}
+
+moe_status moe_omni_forward(const moe_omni_desc* desc, const void* X, const void* W_r,
+                            const void* W_c, const void* W_in, const void* W_out, void* Y,
+                            void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_omni(desc));
+  if (desc->T == 0) return MOE_OK;
+  MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {W_c, "W_c"}, {W_in, "W_in"}, {W_out, "W_out"},
+                      {Y, "Y"}, {ws, "ws"}},
+                     {}));
+  const moe::OmniProblem p = omni_problem(desc);
+  if (ws_bytes < carve_omni_forward(p, nullptr).bytes)
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_omni_workspace_size(MOE_OMNI_WS_FORWARD)");
+  const OmniForwardWs w = carve_omni_forward(p, static_cast<unsigned char*>(ws));
+  hipStream_t s = (hipStream_t)stream;
+  moe::OmniRouteWs rw;
+  moe::omni_route_ws_bytes(p, &rw, w.route);
+  MOE_TRY(hip_status(moe::launch_omni_route(p, X, W_r, W_c, nullptr, nullptr, w.ids, w.gates, rw, s),
+                     "atomic-expert router launch"));
+  moe::OmniPermuteWs pw;
+  moe::omni_permute_ws_bytes(p, &pw, w.permute);
+  MOE_TRY(hip_status(moe::launch_omni_permute(p, w.ids, w.counts, w.offsets, w.perm, w.inv, pw, s),
+                     "atomic-expert permutation launch"));
+  return hip_status(moe::launch_omni_experts(p, X, W_in, W_out, w.ids, w.gates, w.offsets, w.perm,
+                                             w.inv, w.a, Y, s),
+                    "atomic-expert launch");
+}
+
 
 moe_status moe_validate(const moe_desc* desc) {
   g_last_error.clear();

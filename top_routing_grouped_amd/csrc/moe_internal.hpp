@@ -117,6 +117,35 @@ inline bool use_skinny(const Problem& p, uint32_t flags, uint32_t tiled_flag, ui
 hipError_t launch_combine(const Problem& p, const void* O, const float* gates,
                           const int32_t* inv_slot, void* Y, hipStream_t s);
 
+// ---------------------------------------------------------------- atomic experts
+// Layer of N = Nr*Nc rank-1 experts with a Cartesian-product router (bf16).
+struct OmniProblem {
+  int64_t T;
+  int d, Nr, Nc, K;
+};
+struct OmniRouteWs {
+  float* p_r;           // [T][Nr] raw axis logits
+  float* p_c;           // [T][Nc]
+  int32_t* ids1;        // [T] scratch of the projection launches
+  float* gates1;        // [T]
+};
+struct OmniPermuteWs {
+  int32_t* cursor;      // [N] fill position of each expert's segment
+  int32_t* tmp_tk;      // [T*K] entries in arrival order
+};
+size_t omni_route_ws_bytes(const OmniProblem& p, OmniRouteWs* w, unsigned char* base);
+size_t omni_permute_ws_bytes(const OmniProblem& p, OmniPermuteWs* w, unsigned char* base);
+hipError_t launch_omni_route(const OmniProblem& p, const void* X, const void* W_r, const void* W_c,
+                             float* ls_r, float* ls_c, int32_t* ids, float* gates,
+                             const OmniRouteWs& w, hipStream_t s);
+hipError_t launch_omni_permute(const OmniProblem& p, const int32_t* ids, int32_t* counts,
+                               int32_t* offsets, int32_t* perm, int32_t* inv,
+                               const OmniPermuteWs& w, hipStream_t s);
+hipError_t launch_omni_experts(const OmniProblem& p, const void* X, const void* W_in,
+                               const void* W_out, const int32_t* ids, const float* gates,
+                               const int32_t* offsets, const int32_t* perm, const int32_t* inv,
+                               float* a, void* Y, hipStream_t s);
+
 // Tile-aware token rounding of permute's metadata, in place (counts, offsets,
 // perm_token, inv_slot); M = kGemmBM.
 struct RoundWs {
