@@ -14,8 +14,10 @@ for the roofline, and everything is repeated without the flush (warm,
 labelled as such).  For bf16 workloads the training step (moe_forward_train
 then moe_backward on a seeded dY) is timed the same way and reported under
 "training"; moe_forward with tile-aware token rounding is timed the same way
-under "token_rounding" (with the rows it drops and the row tiles it saves).
-Prints one JSON line.
+under "token_rounding" (with the rows it drops and the row tiles it saves);
+the atomic-expert layer (moe_omni_forward on its 4096-token, 65536-expert
+workload) is timed the same way under "atomic_experts".  Prints one JSON
+line.
 
 Extra modes (used for profiler runs):
     --calib-copy BYTES   only run a plain device-to-device copy of BYTES
@@ -379,6 +381,34 @@ def main():
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in evs], before.cpu(), counts.clone().cpu()
 
+    def run_omni(cold: bool):
+        """The atomic-expert layer (omni_bf16: T=4096, d=1024, N=256x256,
+        K=64): K cold steps of moe_omni_forward, plus its active experts."""
+        oi = mi.make_omni_inputs("omni_bf16")
+        ow = oi["workload"]
+        od = {k: oi[k].cuda() for k in ("X", "W_r", "W_c", "W_in", "W_out")}
+        odesc = moe.make_omni_desc(ow.T, ow.d, ow.Nr, ow.Nc, ow.K)
+        ows = torch.empty(moe.moe_omni_workspace_size(odesc, moe.MOE_OMNI_WS_FORWARD),
+                          dtype=torch.uint8, device="cuda")
+        oY = torch.empty_like(od["X"])
+        step = lambda: moe.moe_omni_forward(odesc, od["X"], od["W_r"], od["W_c"], od["W_in"],
+                                            od["W_out"], oY, ows)
+        for _ in range(args.warmup):
+            step()
+        evs = [(ev(), ev()) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            if cold:
+                flush(i)
+            evs[i][0].record(stream)
+            step()
+            evs[i][1].record(stream)
+        oids, _, _, _ = moe.omni_route(od["X"], od["W_r"], od["W_c"], ow.K)
+        ometa = moe.omni_permute(odesc, oids)
+        torch.cuda.synchronize()
+        act = int((ometa["counts"] > 0).sum().item())
+        return ow, [a.elapsed_time(b) for a, b in evs], act
+
     cold = not args.warm
     # ---- timed region: K steps (moe_forward timed; step-wise diagnostics interleaved)
     torch.cuda.synchronize()
@@ -390,6 +420,7 @@ def main():
     warm_fused_ms, warm_stage_ms = run(False)
     train_ms = run_train(cold) if train else None
     rounded = None if args.forward_only else run_rounded(cold)
+    omni = None if args.forward_only else run_omni(cold)
 
     med = statistics.median(fused_ms)
     names = ["route", "permute", "gemm_up", "gemm_down", "combine"]
@@ -500,6 +531,23 @@ def main():
             "dropped_frac": 1.0 - float(round_after.sum()) / max(1, int(round_before.sum())),
             "row_tiles": [tiles(round_before), tiles(round_after)],
             "padded_rows": [pad(round_before), pad(round_after)],
+        }
+    if omni is not None:
+        ow, o_ms, act = omni
+        o_med = statistics.median(o_ms)
+        # algorithmic bytes: X and Y once, both router projections, and the two
+        # vectors of every active expert once (the expert-centric order reads
+        # them once for all their tokens)
+        o_bytes = (2 * ow.T * ow.d * 2 + ow.d * (ow.Nr + ow.Nc) * 2 + act * 2 * ow.d * 2)
+        rec["atomic_experts"] = {
+            "what": "moe_omni_forward: Cartesian router, (expert, token) permutation, "
+                    "expert-centric rank-1 experts, combine; cold",
+            "workload": {"name": ow.name, "T": ow.T, "d": ow.d, "Nr": ow.Nr, "Nc": ow.Nc,
+                         "K": ow.K, "active_experts": act, "eta": ow.T * ow.K / max(1, act)},
+            "ms_per_step": o_med,
+            "tokens_per_s": ow.T / (o_med * 1e-3),
+            "algorithmic_GBps": o_bytes / (o_med * 1e-3) / 1e9,
+            "hbm_frac": o_bytes / (o_med * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         }
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_tokens or min(T, 16384)

@@ -132,6 +132,7 @@ struct OmniRouteWs {
 struct OmniPermuteWs {
   int32_t* cursor;      // [N] fill position of each expert's segment
   int32_t* tmp_tk;      // [T*K] entries in arrival order
+  int32_t* bsum;        // [64] per-workgroup count sums of the scan
 };
 size_t omni_route_ws_bytes(const OmniProblem& p, OmniRouteWs* w, unsigned char* base);
 size_t omni_permute_ws_bytes(const OmniProblem& p, OmniPermuteWs* w, unsigned char* base);

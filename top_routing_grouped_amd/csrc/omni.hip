@@ -41,35 +41,55 @@ constexpr int kMaxAxis = 256;             // N_r, N_c <= 256: 4 scores per lane
 constexpr int kMaxK = 64;
 constexpr int kMaxCand = 320;             // >= sum over i = 1..64 of floor(64 / i) = 280
 
-__device__ __forceinline__ uint32_t ord(float v) {
+// Order-preserving int32 key of a float: signed order of the key = order of
+// the value.  Selection reduces (key desc, id asc) with two DPP reductions.
+__device__ __forceinline__ int skey(float v) {
   const uint32_t b = __float_as_uint(v);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (int)((b & 0x80000000u) ? ~b : (b | 0x80000000u)) ^ (int)0x80000000u;
 }
-__device__ __forceinline__ float unord(uint32_t o) {
+__device__ __forceinline__ float unskey(int k) {
+  const uint32_t o = (uint32_t)k ^ 0x80000000u;
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
-// key ordering (score desc, id asc) as an unsigned max
-__device__ __forceinline__ uint64_t mkkey(float v, uint32_t id) {
-  return ((uint64_t)ord(v) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
 }
-__device__ __forceinline__ uint64_t wave_max64(uint64_t k) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)k, o), hi = __shfl_xor((uint32_t)(k >> 32), o);
-    const uint64_t other = ((uint64_t)hi << 32) | lo;
-    k = other > k ? other : k;
-  }
-  return k;
+// all-reduce over the wave: within 16-lane rows by DPP, then the 4 rows
+__device__ __forceinline__ int wave_max_i(int x) {
+  x = max(x, dpp<0xB1>(x));    // quad_perm [1,0,3,2]
+  x = max(x, dpp<0x4E>(x));    // quad_perm [2,3,0,1]
+  x = max(x, dpp<0x141>(x));   // row_half_mirror
+  x = max(x, dpp<0x140>(x));   // row_mirror
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ __forceinline__ int wave_min_i(int x) {
+  x = min(x, dpp<0xB1>(x));
+  x = min(x, dpp<0x4E>(x));
+  x = min(x, dpp<0x141>(x));
+  x = min(x, dpp<0x140>(x));
+  return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
-__device__ __forceinline__ float wave_maxf(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+__device__ __forceinline__ float dppf(float x, int ctrl_sel) {
+  const int v = __float_as_int(x);
+  return __int_as_float(ctrl_sel == 0 ? dpp<0xB1>(v) : ctrl_sel == 1 ? dpp<0x4E>(v)
+                                     : ctrl_sel == 2 ? dpp<0x141>(v) : dpp<0x140>(v));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dppf(x, 0);
+  x += dppf(x, 1);
+  x += dppf(x, 2);
+  x += dppf(x, 3);
+  return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
+}
+__device__ __forceinline__ float wave_maxf(float x) {
+  return unskey(wave_max_i(skey(x)));
 }
 
 // Log-softmax of one axis row (n <= 256 scores, lane holds entries lane + 64 j);
@@ -98,29 +118,37 @@ __device__ __forceinline__ void axis_log_softmax(const float* p, int n, float* o
   }
 }
 
+// Wave arg-max over one (key, id) per lane by (key desc, id asc): returns
+// the winner's key and id (wave-uniform).
+__device__ __forceinline__ void wave_best(int key, int id, int* wk, int* wid) {
+  const int m = wave_max_i(key);
+  *wk = m;
+  *wid = wave_min_i(key == m ? id : 0x7FFFFFFF);
+}
+
 // The top r entries of an axis by (score desc, id asc): lane q < r receives
 // the q-th (score, id).
 __device__ __forceinline__ void axis_top(const float v[4], int n, int r, float* tv, int* ti) {
   const int lane = threadIdx.x & 63;
-  uint64_t key[4];
+  int key[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = lane + 64 * j;
-    key[j] = i < n ? mkkey(v[j], (uint32_t)i) : 0ull;
-  }
+  for (int j = 0; j < 4; ++j) key[j] = (lane + 64 * j < n) ? skey(v[j]) : INT_MIN;
   for (int q = 0; q < r; ++q) {
-    uint64_t best = key[0];
+    // lane-local best: entries are in ascending id order, so a strictly
+    // larger key is needed to replace an earlier one
+    int bk = key[0], bi = lane;
 #pragma unroll
-    for (int j = 1; j < 4; ++j) best = key[j] > best ? key[j] : best;
-    best = wave_max64(best);
-    const int id = (int)(0xFFFFFFFFu - (uint32_t)best);
+    for (int j = 1; j < 4; ++j)
+      if (key[j] > bk) { bk = key[j]; bi = lane + 64 * j; }
+    int wk, wid;
+    wave_best(bk, bi, &wk, &wid);
     if (lane == q) {
-      *tv = unord((uint32_t)(best >> 32));
-      *ti = id;
+      *tv = unskey(wk);
+      *ti = wid;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j == id) key[j] = 0ull;     // retire the winner
+      if (lane + 64 * j == wid) key[j] = INT_MIN;   // retire the winner
   }
 }
 
@@ -128,7 +156,8 @@ __global__ __launch_bounds__(kThreads) void omni_select_kernel(
     const float* __restrict__ p_r, const float* __restrict__ p_c, float* __restrict__ ls_r,
     float* __restrict__ ls_c, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
     int Nr, int Nc, int K) {
-  __shared__ uint64_t cand[kWaves][kMaxCand];
+  __shared__ int ckey[kWaves][kMaxCand];
+  __shared__ int cid[kWaves][kMaxCand];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * kWaves + wv;
   if (t >= T) return;                                  // wave-uniform; no block barrier below
@@ -142,41 +171,52 @@ __global__ __launch_bounds__(kThreads) void omni_select_kernel(
   axis_top(vc, Nc, C, &cv, &ci);
   // candidate pairs (i, j) of axis ranks with (i+1)(j+1) <= K; lane j holds
   // column rank j, row rank i is broadcast
-  uint64_t* cl = cand[wv];
+  int* ck = ckey[wv];
+  int* cidl = cid[wv];
   int nc = 0;
   for (int i = 0; i < R; ++i) {
     int jmax = K / (i + 1);
     jmax = jmax < C ? jmax : C;
-    const float a = __shfl(rv, i);
-    const int ar = __shfl(ri, i);
-    if (lane < jmax) cl[nc + lane] = mkkey(a + cv, (uint32_t)(ar * Nc + ci));
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rv), i));
+    const int ar = __builtin_amdgcn_readlane(ri, i);
+    if (lane < jmax) {
+      ck[nc + lane] = skey(a + cv);
+      cidl[nc + lane] = ar * Nc + ci;
+    }
     nc += jmax;
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // each lane keeps its share of the candidates in registers
+  constexpr int kPer = (kMaxCand + 63) / 64;
+  int mk[kPer], mi[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = lane + 64 * u;
+    mk[u] = c < nc ? ck[c] : INT_MIN;
+    mi[u] = c < nc ? cidl[c] : 0x7FFFFFFF;
+  }
   // top K of the candidates; lane q receives the q-th
   float sv = 0.f;
   int sid = 0;
   for (int q = 0; q < K; ++q) {
-    uint64_t best = 0ull;
-    int where = -1;
-    for (int c = lane; c < nc; c += 64) {
-      const uint64_t k = cl[c];
-      if (k > best) { best = k; where = c; }
-    }
-    const uint64_t top = wave_max64(best);
-    if (best == top && where >= 0) cl[where] = 0ull;  // keys are distinct (ids differ)
+    int bk = mk[0], bi = mi[0];
+#pragma unroll
+    for (int u = 1; u < kPer; ++u)
+      if (mk[u] > bk || (mk[u] == bk && mi[u] < bi)) { bk = mk[u]; bi = mi[u]; }
+    int wk, wid;
+    wave_best(bk, bi, &wk, &wid);
     if (lane == q) {
-      sv = unord((uint32_t)(top >> 32));
-      sid = (int)(0xFFFFFFFFu - (uint32_t)top);
+      sv = unskey(wk);
+      sid = wid;
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (mi[u] == wid) mk[u] = INT_MIN;              // ids are distinct
   }
   // gates: softmax over the K selected sums (lane 0 holds the largest)
-  const float s0 = __shfl(sv, 0);
+  const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), 0));
   const float ex = lane < K ? __expf(sv - s0) : 0.f;
   const float z = wave_sum(ex);
   if (lane < K) {
@@ -198,33 +238,84 @@ __global__ __launch_bounds__(kThreads) void omni_count_kernel(const int32_t* __r
   if (i < TK) atomicAdd(&counts[ids[i]], 1);
 }
 
-// One workgroup of 1024 threads: thread q owns a contiguous run of experts.
-constexpr int kScanThreads = 1024;
-__global__ __launch_bounds__(kScanThreads) void omni_scan_kernel(const int32_t* __restrict__ counts,
-                                                                 int32_t* __restrict__ offsets,
-                                                                 int32_t* __restrict__ cursor,
-                                                                 int N) {
-  __shared__ int part[kScanThreads];
-  const int q = threadIdx.x;
-  const int per = (N + kScanThreads - 1) / kScanThreads;
-  const int lo = q * per, hi = (lo + per < N) ? lo + per : N;
-  int sum = 0;
-  for (int e = lo; e < hi; ++e) sum += counts[e];
-  part[q] = sum;
+// Exclusive scan over N <= 65536 counts in two launches of N/1024
+// workgroups: block sums, then each block adds the sums before it and scans
+// its own 1024 counts (thread q owns 4 consecutive ones: coalesced 16-byte
+// accesses).
+constexpr int kScanBlock = 4 * kThreads;
+__device__ __forceinline__ void load4(const int32_t* p, int base, int N, int v[4]) {
+  if (base + 3 < N) {
+    const int4 q = *reinterpret_cast<const int4*>(p + base);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = base + r < N ? p[base + r] : 0;
+  }
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__global__ __launch_bounds__(kThreads) void omni_blocksum_kernel(const int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ bsum, int N) {
+  __shared__ int tmp[kWaves];
+  int v[4];
+  load4(counts, blockIdx.x * kScanBlock + 4 * threadIdx.x, N, v);
+  const int s = wave_sum_i(v[0] + v[1] + v[2] + v[3]);
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = s;
   __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int x = q >= off ? part[q - off] : 0;
-    __syncthreads();
-    part[q] += x;
-    __syncthreads();
+  if (threadIdx.x == 0) bsum[blockIdx.x] = (tmp[0] + tmp[1]) + (tmp[2] + tmp[3]);
+}
+
+__global__ __launch_bounds__(kThreads) void omni_scan_kernel(const int32_t* __restrict__ counts,
+                                                             const int32_t* __restrict__ bsum,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ cursor, int N) {
+  __shared__ int tmp[kWaves];
+  __shared__ int carry_sh;
+  const int q = threadIdx.x, lane = q & 63, w = q >> 6;
+  const int b = blockIdx.x;
+  if (w == 0) {                                   // blocks before this one (b <= 64)
+    const int c = wave_sum_i(lane < b ? bsum[lane] : 0);
+    if (lane == 0) carry_sh = c;
   }
-  int run = part[q] - sum;
-  for (int e = lo; e < hi; ++e) {
-    offsets[e] = run;
-    cursor[e] = run;
-    run += counts[e];
+  const int base = b * kScanBlock + 4 * q;
+  int v[4];
+  load4(counts, base, N, v);
+  const int mine = (v[0] + v[1]) + (v[2] + v[3]);
+  int x = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    x += lane >= o ? y : 0;
   }
-  if (q == kScanThreads - 1) offsets[N] = part[q];
+  if (lane == 63) tmp[w] = x;
+  __syncthreads();
+  int before = carry_sh, total = 0;
+#pragma unroll
+  for (int j = 0; j < kWaves; ++j) {
+    total += tmp[j];
+    before += j < w ? tmp[j] : 0;
+  }
+  int o[4];
+  o[0] = before + x - mine;
+  o[1] = o[0] + v[0];
+  o[2] = o[1] + v[1];
+  o[3] = o[2] + v[2];
+  if (base + 3 < N) {
+    *reinterpret_cast<int4*>(offsets + base) = int4{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<int4*>(cursor + base) = int4{o[0], o[1], o[2], o[3]};
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (base + r < N) {
+        offsets[base + r] = o[r];
+        cursor[base + r] = o[r];
+      }
+  }
+  if (b == (int)gridDim.x - 1 && q == 0) offsets[N] = carry_sh + total;
 }
 
 __global__ __launch_bounds__(kThreads) void omni_scatter_kernel(const int32_t* __restrict__ ids,
@@ -261,87 +352,141 @@ __global__ __launch_bounds__(kThreads) void omni_rank_kernel(const int32_t* __re
 }
 
 // ---------------------------------------------------------------- experts
-// d <= 4096: a lane owns 8-element chunks lane, lane+64, ... of the row.
-constexpr int kMaxChunks = 8;
-
-__device__ __forceinline__ void load_row(const uint16_t* row, int nchunk, float* v) {
+// A lane owns NCH 8-element chunks (lane, lane+64, ...) of a d-row; NCH =
+// ceil(d / 512) keeps the registers, and so the waves per SIMD, to what d needs.
+template <int NCH>
+__device__ __forceinline__ void load_row(const uint16_t* row, int nchunk, u32x4* q) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
+  for (int c = 0; c < NCH; ++c) {
     const int ch = lane + 64 * c;
-    if (c * 64 < nchunk) {
-      u32x4 q = {0u, 0u, 0u, 0u};
-      if (ch < nchunk) q = *reinterpret_cast<const u32x4*>(row + ch * 8);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        v[c * 8 + 2 * h] = dev::bf16_bits_to_f32(q[h] & 0xFFFFu);
-        v[c * 8 + 2 * h + 1] = dev::bf16_bits_to_f32(q[h] >> 16);
-      }
-    }
+    q[c] = ch < nchunk ? *reinterpret_cast<const u32x4*>(row + ch * 8) : u32x4{0u, 0u, 0u, 0u};
   }
 }
+template <int NCH>
+__device__ __forceinline__ float dot_rows(const u32x4* a, const float* w) {
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      s = fmaf(dev::bf16_bits_to_f32(a[c][h] & 0xFFFFu), w[c * 8 + 2 * h], s);
+      s = fmaf(dev::bf16_bits_to_f32(a[c][h] >> 16), w[c * 8 + 2 * h + 1], s);
+    }
+  return s;
+}
 
+// One wave per expert: w_in once, then its tokens four at a time (their
+// rows loaded together), a[s] = silu(x . w_in).
+template <int NCH>
 __global__ __launch_bounds__(kThreads) void omni_expert_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W_in,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, float* __restrict__ a,
     int N, int d) {
+  constexpr int kTasks = 4;
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (e >= N) return;
   const int off = offsets[e], c = offsets[e + 1] - off;
   if (c == 0) return;
   const int nchunk = d / 8;
-  float w[kMaxChunks * 8];
-  load_row(W_in + (int64_t)e * d, nchunk, w);
-  for (int s = off; s < off + c; ++s) {
-    const int t = __builtin_amdgcn_readfirstlane(perm[s]);
-    float x[kMaxChunks * 8];
-    load_row(X + (int64_t)t * d, nchunk, x);
-    float dot = 0.f;
+  float w[NCH * 8];
+  {
+    u32x4 q[NCH];
+    load_row<NCH>(W_in + (int64_t)e * d, nchunk, q);
 #pragma unroll
-    for (int i = 0; i < kMaxChunks * 8; ++i)
-      if ((i / 8) * 64 < nchunk) dot = fmaf(x[i], w[i], dot);
-    dot = wave_sum(dot);
-    if (lane == 0) a[s] = dot * dev::sigmoid(dot);
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        w[ch * 8 + 2 * h] = dev::bf16_bits_to_f32(q[ch][h] & 0xFFFFu);
+        w[ch * 8 + 2 * h + 1] = dev::bf16_bits_to_f32(q[ch][h] >> 16);
+      }
+  }
+  for (int s0 = 0; s0 < c; s0 += kTasks) {
+    u32x4 x[kTasks][NCH];
+#pragma unroll
+    for (int u = 0; u < kTasks; ++u) {
+      const int s = off + (s0 + u < c ? s0 + u : c - 1);
+      const int t = __builtin_amdgcn_readfirstlane(perm[s]);
+      load_row<NCH>(X + (int64_t)t * d, nchunk, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kTasks; ++u) {
+      const float dot = wave_sum(dot_rows<NCH>(x[u], w));
+      if (lane == 0 && s0 + u < c) a[off + s0 + u] = dot * dev::sigmoid(dot);
+    }
   }
 }
 
+// One wave per token: lane k first loads the token's id and coefficient
+// g_k * a[slot] for entry k (so the row loads below depend on nothing but a
+// broadcast), then rows go in groups (16 for d <= 1024) with all their
+// loads in flight.
+template <int NCH>
 __global__ __launch_bounds__(kThreads) void omni_combine_kernel(
     const uint16_t* __restrict__ W_out, const int32_t* __restrict__ ids,
     const float* __restrict__ gates, const int32_t* __restrict__ inv, const float* __restrict__ a,
     uint16_t* __restrict__ Y, int64_t T, int d, int K) {
+  constexpr int KG = NCH >= 4 ? 32 / NCH : 16;   // 16-byte loads in flight: 16..32 per lane
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (t >= T) return;
   const int nchunk = d / 8;
-  for (int c0 = lane; c0 < nchunk; c0 += 64) {
-    float acc[8];
+  int myid = 0;
+  float mycoef = 0.f;
+  if (lane < K) {
+    const int64_t tk = t * K + lane;
+    myid = ids[tk];
+    mycoef = gates[tk] * a[inv[tk]];
+  }
+  float acc[NCH * 8];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) acc[v] = 0.f;
-    constexpr int KG = 8;                       // rows in flight per group
-    for (int k0 = 0; k0 < K; k0 += KG) {
-      u32x4 q[KG];
-      float coef[KG];
+  for (int v = 0; v < NCH * 8; ++v) acc[v] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += KG) {
+    u32x4 q[KG][NCH];
 #pragma unroll
-      for (int u = 0; u < KG; ++u) {
-        const int k = k0 + u < K ? k0 + u : K - 1;
-        const int64_t tk = t * K + k;
-        coef[u] = k0 + u < K ? gates[tk] * a[inv[tk]] : 0.f;
-        q[u] = *reinterpret_cast<const u32x4*>(W_out + (int64_t)ids[tk] * d + c0 * 8);
-      }
+    for (int u = 0; u < KG; ++u) {
+      const int k = k0 + u < K ? k0 + u : K - 1;
+      const int row = __builtin_amdgcn_readlane(myid, k);
+      load_row<NCH>(W_out + (int64_t)row * d, nchunk, q[u]);
+    }
 #pragma unroll
-      for (int u = 0; u < KG; ++u)
+    for (int u = 0; u < KG; ++u) {
+      const int k = k0 + u < K ? k0 + u : K - 1;
+      const float cf = k0 + u < K ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mycoef), k)) : 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          acc[2 * h] = fmaf(coef[u], dev::bf16_bits_to_f32(q[u][h] & 0xFFFFu), acc[2 * h]);
-          acc[2 * h + 1] = fmaf(coef[u], dev::bf16_bits_to_f32(q[u][h] >> 16), acc[2 * h + 1]);
+          acc[c * 8 + 2 * h] = fmaf(cf, dev::bf16_bits_to_f32(q[u][c][h] & 0xFFFFu), acc[c * 8 + 2 * h]);
+          acc[c * 8 + 2 * h + 1] = fmaf(cf, dev::bf16_bits_to_f32(q[u][c][h] >> 16), acc[c * 8 + 2 * h + 1]);
         }
     }
-    u32x4 out;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) out[h] = dev::pack_bf16x2(acc[2 * h], acc[2 * h + 1]);
-    *reinterpret_cast<u32x4*>(Y + t * (int64_t)d + c0 * 8) = out;
   }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nchunk) {
+      u32x4 out;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) out[h] = dev::pack_bf16x2(acc[c * 8 + 2 * h], acc[c * 8 + 2 * h + 1]);
+      *reinterpret_cast<u32x4*>(Y + t * (int64_t)d + ch * 8) = out;
+    }
+  }
+}
+
+// The router GEMM's problem for one axis (top-1 outputs go to scratch).
+Problem axis_problem(const OmniProblem& p, int E) {
+  Problem q{};
+  q.T = p.T;
+  q.d = p.d;
+  q.E = E;
+  q.K = 1;
+  q.n = 64;
+  q.bf16 = true;
+  q.C = p.T;
+  q.rows_max = p.T;
+  return q;
 }
 
 }  // namespace
@@ -372,6 +517,7 @@ size_t omni_permute_ws_bytes(const OmniProblem& p, OmniPermuteWs* w, unsigned ch
   OmniPermuteWs ws{};
   ws.cursor = reinterpret_cast<int32_t*>(take((size_t)p.Nr * p.Nc * 4));
   ws.tmp_tk = reinterpret_cast<int32_t*>(take((size_t)p.T * p.K * 4));
+  ws.bsum = reinterpret_cast<int32_t*>(take(64 * 4));
   if (w) *w = ws;
   return off;
 }
@@ -381,19 +527,11 @@ hipError_t launch_omni_route(const OmniProblem& p, const void* X, const void* W_
                              const OmniRouteWs& w, hipStream_t s) {
   // the two axis projections: the router GEMM with fp32 logits out (top-1
   // outputs go to scratch)
-  Problem q{};
-  q.T = p.T;
-  q.d = p.d;
-  q.K = 1;
-  q.n = 64;
-  q.bf16 = true;
-  q.C = p.T;
-  q.rows_max = p.T;
-  q.E = p.Nr;
-  hipError_t err = launch_route(q, X, W_r, nullptr, w.p_r, w.ids1, w.gates1, nullptr, s);
+  // (no k split: its extra selection pass costs more than it saves here)
+  hipError_t err = launch_route(axis_problem(p, p.Nr), X, W_r, nullptr, w.p_r, w.ids1, w.gates1,
+                                nullptr, s);
   if (err != hipSuccess) return err;
-  q.E = p.Nc;
-  err = launch_route(q, X, W_c, nullptr, w.p_c, w.ids1, w.gates1, nullptr, s);
+  err = launch_route(axis_problem(p, p.Nc), X, W_c, nullptr, w.p_c, w.ids1, w.gates1, nullptr, s);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(omni_select_kernel, dim3((unsigned)((p.T + kWaves - 1) / kWaves)),
                      dim3(kThreads), 0, s, w.p_r, w.p_c, ls_r, ls_c, ids, gates, p.T, p.Nr, p.Nc,
@@ -413,7 +551,10 @@ hipError_t launch_omni_permute(const OmniProblem& p, const int32_t* ids, int32_t
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(omni_count_kernel, dim3(gTK), dim3(kThreads), 0, s, ids, counts, TK);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(omni_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, offsets,
+  const unsigned nb = (unsigned)((N + kScanBlock - 1) / kScanBlock);
+  hipLaunchKernelGGL(omni_blocksum_kernel, dim3(nb), dim3(kThreads), 0, s, counts, w.bsum, N);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(omni_scan_kernel, dim3(nb), dim3(kThreads), 0, s, counts, w.bsum, offsets,
                      w.cursor, N);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(omni_scatter_kernel, dim3(gTK), dim3(kThreads), 0, s, ids, w.cursor,
@@ -429,14 +570,27 @@ hipError_t launch_omni_experts(const OmniProblem& p, const void* X, const void* 
                                const int32_t* offsets, const int32_t* perm, const int32_t* inv,
                                float* a, void* Y, hipStream_t s) {
   const int N = p.Nr * p.Nc;
-  hipLaunchKernelGGL(omni_expert_kernel, dim3((unsigned)((N + kWaves - 1) / kWaves)),
-                     dim3(kThreads), 0, s, (const uint16_t*)X, (const uint16_t*)W_in, offsets,
-                     perm, a, N, p.d);
+  const dim3 eg((unsigned)((N + kWaves - 1) / kWaves));
+  const int nch = (p.d + 511) / 512;
+  auto run = [&](auto kern) {
+    hipLaunchKernelGGL(kern, eg, dim3(kThreads), 0, s, (const uint16_t*)X, (const uint16_t*)W_in,
+                       offsets, perm, a, N, p.d);
+  };
+  if (nch <= 1) run(omni_expert_kernel<1>);
+  else if (nch <= 2) run(omni_expert_kernel<2>);
+  else if (nch <= 4) run(omni_expert_kernel<4>);
+  else run(omni_expert_kernel<8>);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(omni_combine_kernel, dim3((unsigned)((p.T + kWaves - 1) / kWaves)),
-                     dim3(kThreads), 0, s, (const uint16_t*)W_out, ids, gates, inv, a,
-                     (uint16_t*)Y, p.T, p.d, p.K);
+  const dim3 cg((unsigned)((p.T + kWaves - 1) / kWaves));
+  auto comb = [&](auto kern) {
+    hipLaunchKernelGGL(kern, cg, dim3(kThreads), 0, s, (const uint16_t*)W_out, ids, gates, inv, a,
+                       (uint16_t*)Y, p.T, p.d, p.K);
+  };
+  if (nch <= 1) comb(omni_combine_kernel<1>);
+  else if (nch <= 2) comb(omni_combine_kernel<2>);
+  else if (nch <= 4) comb(omni_combine_kernel<4>);
+  else comb(omni_combine_kernel<8>);
   return hipGetLastError();
 }
 
