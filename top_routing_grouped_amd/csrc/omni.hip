@@ -12,8 +12,9 @@
 //
 // Kernels (after the two axis projections, which reuse the router GEMM):
 //   omni_select   one wave per token: log-softmax of both axes (exported),
-//                 the top min(K, N_r) rows and min(K, N_c) columns by repeated
-//                 wave arg-max on (score, -id) keys, then the top K of the
+//                 the top min(K, N_r) rows and min(K, N_c) columns by
+//                 (score desc, id asc) -- a bitwise threshold search with
+//                 ballot counts, not a sort -- then the top K of the
 //                 row+column sums among the pairs (i, j) of axis ranks with
 //                 (i+1)(j+1) <= K (a pair with more than K-1 pairs ranked
 //                 above it cannot be in the top K); gates = softmax over the
@@ -42,7 +43,7 @@ constexpr int kMaxK = 64;
 constexpr int kMaxCand = 320;             // >= sum over i = 1..64 of floor(64 / i) = 280
 
 // Order-preserving int32 key of a float: signed order of the key = order of
-// the value.  Selection reduces (key desc, id asc) with two DPP reductions.
+// the value (the wave max of floats runs as an integer DPP reduction).
 __device__ __forceinline__ int skey(float v) {
   const uint32_t b = __float_as_uint(v);
   return (int)((b & 0x80000000u) ? ~b : (b | 0x80000000u)) ^ (int)0x80000000u;
@@ -64,14 +65,6 @@ __device__ __forceinline__ int wave_max_i(int x) {
   x = max(x, dpp<0x140>(x));   // row_mirror
   return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
              max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
-}
-__device__ __forceinline__ int wave_min_i(int x) {
-  x = min(x, dpp<0xB1>(x));
-  x = min(x, dpp<0x4E>(x));
-  x = min(x, dpp<0x141>(x));
-  x = min(x, dpp<0x140>(x));
-  return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
-             min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 __device__ __forceinline__ float dppf(float x, int ctrl_sel) {
   const int v = __float_as_int(x);
@@ -118,38 +111,86 @@ __device__ __forceinline__ void axis_log_softmax(const float* p, int n, float* o
   }
 }
 
-// Wave arg-max over one (key, id) per lane by (key desc, id asc): returns
-// the winner's key and id (wave-uniform).
-__device__ __forceinline__ void wave_best(int key, int id, int* wk, int* wid) {
-  const int m = wave_max_i(key);
-  *wk = m;
-  *wid = wave_min_i(key == m ? id : 0x7FFFFFFF);
+// Unsigned order-preserving key of a float (0 is below every finite value,
+// so it marks an empty slot).
+__device__ __forceinline__ uint32_t ukey(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
+__device__ __forceinline__ float unukey(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
 
-// The top r entries of an axis by (score desc, id asc): lane q < r receives
-// the q-th (score, id).
-__device__ __forceinline__ void axis_top(const float v[4], int n, int r, float* tv, int* ti) {
+// Top r (1 <= r <= 64) of the wave's entries -- S slots per lane, entry
+// (u, lane) with key k[u] (0 = empty) and a distinct id i[u] < 2^17 -- by
+// (key desc, id asc).  Lane q < r receives the q-th key and id.
+// Without a sort: the r-th largest key th by a bitwise search with ballot
+// counts, the ties at th resolved by the same search over ids, the winners
+// compacted to lanes 0..r-1 through LDS, then each winner's rank counted
+// against the others (readlane broadcasts) and the winners placed by rank.
+// Ballot counts and the searches run on the scalar unit.
+template <int S>
+__device__ __forceinline__ void wave_top(const uint32_t* k, const int* id, int r, uint32_t* ok,
+                                         int* oi, int* lk, int* li) {
   const int lane = threadIdx.x & 63;
-  int key[4];
+  uint32_t th = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = th | (1u << bit);
+    int c = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) key[j] = (lane + 64 * j < n) ? skey(v[j]) : INT_MIN;
-  for (int q = 0; q < r; ++q) {
-    // lane-local best: entries are in ascending id order, so a strictly
-    // larger key is needed to replace an earlier one
-    int bk = key[0], bi = lane;
-#pragma unroll
-    for (int j = 1; j < 4; ++j)
-      if (key[j] > bk) { bk = key[j]; bi = lane + 64 * j; }
-    int wk, wid;
-    wave_best(bk, bi, &wk, &wid);
-    if (lane == q) {
-      *tv = unskey(wk);
-      *ti = wid;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j == wid) key[j] = INT_MIN;   // retire the winner
+    for (int u = 0; u < S; ++u) c += wave_count(k[u] >= cand);
+    if (c >= r) th = cand;
   }
+  int gt = 0;
+#pragma unroll
+  for (int u = 0; u < S; ++u) gt += wave_count(k[u] > th);
+  const int need = r - gt;                       // ties at th to take, lowest ids first
+  int x = 0;                                     // the need-th smallest id among the ties
+  for (int bit = 16; bit >= 0; --bit) {
+    const int cand = x | (1 << bit);
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < S; ++u) c += wave_count(k[u] == th && id[u] < cand);
+    if (c < need) x = cand;
+  }
+  // compact the r winners to positions 0..r-1 (slot-major, lane order)
+  const uint64_t below = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int u = 0; u < S; ++u) {
+    const bool sel = k[u] > th || (k[u] == th && id[u] <= x);
+    const uint64_t m = __ballot(sel);
+    if (sel) {
+      const int pos = base + __popcll(m & below);
+      lk[pos] = (int)k[u];
+      li[pos] = id[u];
+    }
+    base += __popcll(m);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint32_t mk = lane < r ? (uint32_t)lk[lane] : 0u;
+  const int mi = lane < r ? li[lane] : 0x7FFFFFFF;
+  int rank = 0;
+  for (int q = 0; q < r; ++q) {
+    const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)mk, q);
+    const int iq = __builtin_amdgcn_readlane(mi, q);
+    rank += (kq > mk || (kq == mk && iq < mi)) ? 1 : 0;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < r) {
+    lk[64 + rank] = (int)mk;
+    li[64 + rank] = mi;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  *ok = lane < r ? (uint32_t)lk[64 + lane] : 0u;
+  *oi = lane < r ? li[64 + lane] : 0;
 }
 
 __global__ __launch_bounds__(kThreads) void omni_select_kernel(
@@ -158,6 +199,8 @@ __global__ __launch_bounds__(kThreads) void omni_select_kernel(
     int Nr, int Nc, int K) {
   __shared__ int ckey[kWaves][kMaxCand];
   __shared__ int cid[kWaves][kMaxCand];
+  __shared__ int tk[kWaves][128];
+  __shared__ int ti[kWaves][128];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * kWaves + wv;
   if (t >= T) return;                                  // wave-uniform; no block barrier below
@@ -165,14 +208,24 @@ __global__ __launch_bounds__(kThreads) void omni_select_kernel(
   axis_log_softmax(p_r + t * Nr, Nr, ls_r ? ls_r + t * Nr : nullptr, vr);
   axis_log_softmax(p_c + t * Nc, Nc, ls_c ? ls_c + t * Nc : nullptr, vc);
   const int R = K < Nr ? K : Nr, C = K < Nc ? K : Nc;
-  float rv = 0.f, cv = 0.f;
-  int ri = 0, ci = 0;
-  axis_top(vr, Nr, R, &rv, &ri);
-  axis_top(vc, Nc, C, &cv, &ci);
+  uint32_t kr[4], kc[4];
+  int ir[4], ic[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = lane + 64 * j;
+    kr[j] = i < Nr ? ukey(vr[j]) : 0u;
+    kc[j] = i < Nc ? ukey(vc[j]) : 0u;
+    ir[j] = ic[j] = i;
+  }
+  uint32_t rk, ck;
+  int ri, ci;
+  wave_top<4>(kr, ir, R, &rk, &ri, tk[wv], ti[wv]);
+  wave_top<4>(kc, ic, C, &ck, &ci, tk[wv], ti[wv]);
+  const float rv = unukey(rk), cv = unukey(ck);
   // candidate pairs (i, j) of axis ranks with (i+1)(j+1) <= K; lane j holds
   // column rank j, row rank i is broadcast
-  int* ck = ckey[wv];
-  int* cidl = cid[wv];
+  int* cks = ckey[wv];
+  int* cis = cid[wv];
   int nc = 0;
   for (int i = 0; i < R; ++i) {
     int jmax = K / (i + 1);
@@ -180,41 +233,27 @@ __global__ __launch_bounds__(kThreads) void omni_select_kernel(
     const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rv), i));
     const int ar = __builtin_amdgcn_readlane(ri, i);
     if (lane < jmax) {
-      ck[nc + lane] = skey(a + cv);
-      cidl[nc + lane] = ar * Nc + ci;
+      cks[nc + lane] = (int)ukey(a + cv);
+      cis[nc + lane] = ar * Nc + ci;
     }
     nc += jmax;
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // each lane keeps its share of the candidates in registers
   constexpr int kPer = (kMaxCand + 63) / 64;
-  int mk[kPer], mi[kPer];
+  uint32_t mk[kPer];
+  int mi[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int c = lane + 64 * u;
-    mk[u] = c < nc ? ck[c] : INT_MIN;
-    mi[u] = c < nc ? cidl[c] : 0x7FFFFFFF;
+    mk[u] = c < nc ? (uint32_t)cks[c] : 0u;
+    mi[u] = c < nc ? cis[c] : (1 << 17);
   }
-  // top K of the candidates; lane q receives the q-th
-  float sv = 0.f;
-  int sid = 0;
-  for (int q = 0; q < K; ++q) {
-    int bk = mk[0], bi = mi[0];
-#pragma unroll
-    for (int u = 1; u < kPer; ++u)
-      if (mk[u] > bk || (mk[u] == bk && mi[u] < bi)) { bk = mk[u]; bi = mi[u]; }
-    int wk, wid;
-    wave_best(bk, bi, &wk, &wid);
-    if (lane == q) {
-      sv = unskey(wk);
-      sid = wid;
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      if (mi[u] == wid) mk[u] = INT_MIN;              // ids are distinct
-  }
+  uint32_t sk;
+  int sid;
+  wave_top<kPer>(mk, mi, K, &sk, &sid, tk[wv], ti[wv]);
+  const float sv = unukey(sk);
   // gates: softmax over the K selected sums (lane 0 holds the largest)
   const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), 0));
   const float ex = lane < K ? __expf(sv - s0) : 0.f;
