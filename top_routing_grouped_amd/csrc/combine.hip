@@ -25,7 +25,9 @@ constexpr int kTokPerBlock = kThreads / 64;
 // all of them for 8 experts at once -- one memory round trip per token row
 // block -- then accumulates in k order.  Dropped assignments point their
 // load at a kept row of the same token (no extra HBM traffic) and are left
-// out of the sum by a select, so the load sequence has no branches.
+// out of the sum by a select, so the load sequence has no branches.  O is
+// read once and Y written once, both with the non-temporal hint (9% faster
+// than cached accesses at the Qwen3 shape: the stream does not fill L2).
 template <int CB>
 __global__ __launch_bounds__(kThreads) void combine_bf16(const uint16_t* __restrict__ O,
                                                         const float* __restrict__ gates,
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void combine_bf16(const uint16_t* __restr
       for (int u = 0; u < KG; ++u)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
-          o[u][cb] = *reinterpret_cast<const u32x4*>(O + (int64_t)sl[u] * d + cc[cb] * 8);
+          o[u][cb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(O + (int64_t)sl[u] * d + cc[cb] * 8));
 #pragma unroll
       for (int u = 0; u < KG; ++u)
 #pragma unroll
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void combine_bf16(const uint16_t* __restr
         u32x4 out;
 #pragma unroll
         for (int h = 0; h < 4; ++h) out[h] = dev::pack_bf16x2(acc[cb][2 * h], acc[cb][2 * h + 1]);
-        *reinterpret_cast<u32x4*>(Y + t * (int64_t)d + c * 8) = out;
+        __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(Y + t * (int64_t)d + c * 8));
       }
     }
   }

@@ -11,10 +11,12 @@
 //   columns (up: 128 W_gate columns + the same 128 W_up columns, so SwiGLU is
 //   register-local; down: 256 W_down columns).  Experts without rows exit
 //   at once; only active experts' weights are read.  Measured at the decode
-//   size (T=64, d=4096, E=256, n=512): the weight stream runs at 4.7-4.9 TB/s
-//   whether or not the MFMAs run and for 3 to 8 stages, i.e. it is bound by
-//   the memory system for these strided 512-byte row pieces (128-column
-//   blocks: 4.5-4.75 TB/s).
+//   size (T=64, d=4096, E=256, n=512) with cached copies: the weight stream
+//   ran at 4.7-4.9 TB/s whether or not the MFMAs ran and for 3 to 8 stages,
+//   i.e. bound by the memory system for these strided 512-byte row pieces
+//   (128-column blocks: 4.5-4.75 TB/s).  The weight copies carry the
+//   non-temporal hint (each weight is read once per launch): that lifted the
+//   up projection from 374 to 305 us at this size.
 // * The expert's rows are taken in passes of up to 64 (four 16-row MFMA
 //   blocks; 32 when the batch averages at most 16 rows per expert); a pass
 //   streams the column block over the whole k range through four LDS
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(kThreads, (SkinnyGeo<ROWS, COLS>::kOcc)) void skinn
       for (int i = 0; i < kAI; ++i) dev::lds_copy16(asrc[i] + kt * kBK, base + (w * kAI + i) * 1024);
 #pragma unroll
       for (int i = 0; i < kBI; ++i)
-        dev::lds_copy16(bsrc[i] + (int64_t)kt * kBK * N, base + kA + (w * kBI + i) * 1024);
+        dev::lds_copy16_stream(bsrc[i] + (int64_t)kt * kBK * N, base + kA + (w * kBI + i) * 1024);
     };
 
     f32x4 acc[kRB][CB];

