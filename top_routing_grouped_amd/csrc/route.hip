@@ -353,12 +353,16 @@ __device__ __forceinline__ int wr_swizzle(int r) {
 template <int NBW>
 struct RouteGeo {
   static constexpr int Epad = 32 * NBW;
-  static constexpr int NST = (NBW >= 8) ? 3 : 4;     // LDS stages (X tile + W_r tile each)
+  // LDS stages (X tile + W_r tile each).  Four at every width (E = 256: 4 x
+  // 40 KB, the whole LDS; 136 instead of 144 us with three at T = 32768,
+  // d = 4096); more at E = 128 were slower (five or six: 34-35 against 30 us).
+  static constexpr int NST = 4;
   static constexpr int kX = kTok * kBK * 2;          // X tile bytes (8 KB)
   static constexpr int kW = kBK * Epad * 2;          // W_r tile bytes
   static constexpr int kStage = kX + kW;
   static constexpr int S = Epad + 16;                // floats per score row
   static constexpr int kLds = (NST * kStage > kTok * S * 4) ? NST * kStage : kTok * S * 4;
+  static_assert(kLds <= 160 * 1024, "one workgroup's LDS");
   static constexpr int kXInstr = kX / 1024 / 4;      // copies per wave per tile (4 waves)
   static constexpr int kWInstr = kW / 1024 / 4;
   static constexpr int kInstr = kXInstr + kWInstr;
