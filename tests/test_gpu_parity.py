@@ -65,6 +65,7 @@ SMALL = [
     (200, 192, 1, 1, 64, "bf16", 0.0, None),         # single expert
     (300, 128, 64, 6, 256, "bf16", 0.3, "zipf"),     # heavy drops, fully dropped tokens
     (70, 64, 40, 20, 64, "bf16", 0.0, None),         # K above 16
+    (60, 64, 64, 64, 64, "bf16", 0.0, None),         # K = E = 64: every token in every expert
     (1, 128, 8, 2, 128, "bf16", 0.0, None),          # one token
     (256, 128, 8, 2, 256, "fp32", 0.0, None),        # the tiny fp32 layer's shape, other seed
     (100, 64, 5, 3, 64, "fp32", 0.5, "zipf"),
@@ -194,6 +195,60 @@ def test_zero_tokens_is_a_no_op():
     Y = moe.forward(X, W_r, Wg, Wg, Wg.transpose(1, 2).contiguous(), 2)
     torch.cuda.synchronize()
     assert Y.shape == (0, 128)
+
+
+def _bench_chain(inp, K, cf):
+    """The entry-point sequence bench.py times: route and permute with their
+    workspaces, the up GEMM building the tile table, the down GEMM and a
+    second up GEMM on that table (MOE_FLAG_TILE_TABLE_READY), the combine,
+    and moe_forward on the same inputs."""
+    dev = device_inputs(inp)
+    X = dev["X"]
+    T, d = X.shape
+    E, _, n = dev["W_gate"].shape
+    dtype = "bf16" if X.dtype == torch.bfloat16 else "fp32"
+    desc = moe.make_desc(T, d, E, K, n, dtype, cf)
+    ready = moe.make_desc(T, d, E, K, n, dtype, cf, flags=moe.MOE_FLAG_TILE_TABLE_READY)
+    rows = moe.moe_max_rows(desc)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ids, inv = torch.empty((T, K), **i32), torch.empty((T, K), **i32)
+    gates = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    counts, offsets, perm = torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(T * K, **i32)
+    H = [torch.empty((rows, n), dtype=X.dtype, device="cuda") for _ in range(2)]
+    O = [torch.empty((rows, d), dtype=X.dtype, device="cuda") for _ in range(2)]
+    Y = [torch.empty((T, d), dtype=X.dtype, device="cuda") for _ in range(2)]
+    ws_f = moe.workspace(desc, moe.MOE_WS_GROUPED_FFN)
+    moe.moe_route_ws(desc, X, dev["W_r"], dev["bias"], None, ids, gates, moe.workspace(desc, moe.MOE_WS_ROUTE))
+    moe.moe_permute(desc, ids, counts, offsets, None, perm, inv, moe.workspace(desc, moe.MOE_WS_PERMUTE))
+    moe.moe_grouped_gemm_up(desc, X, offsets, perm, dev["W_gate"], dev["W_up"], H[0], ws_f)
+    moe.moe_grouped_gemm_down(ready, H[0], offsets, dev["W_down"], O[0], ws_f)
+    moe.moe_grouped_gemm_up(ready, X, offsets, perm, dev["W_gate"], dev["W_up"], H[1], ws_f)
+    moe.moe_grouped_gemm_down(desc, H[1], offsets, dev["W_down"], O[1], moe.workspace(desc, moe.MOE_WS_GROUPED_FFN))
+    moe.moe_combine(desc, O[0], gates, inv, Y[0])
+    moe.moe_forward(desc, X, dev["W_r"], dev["bias"], dev["W_gate"], dev["W_up"], dev["W_down"], Y[1],
+                    moe.workspace(desc, moe.MOE_WS_FORWARD))
+    torch.cuda.synchronize()
+    N = int(offsets[E].item())
+    return N, H, O, Y
+
+
+@pytest.mark.parametrize("case", ["small", "qwen3_bf16"])
+def test_prebuilt_tile_table_as_timed(case):
+    """GEMMs launched on a tile table built by an earlier call (the bench's
+    configuration) give the bits of a freshly built table, and the chain the
+    bench times gives the bits of moe_forward."""
+    if case == "small":
+        inp, K, cf = mi.draw(3001, 256, 16, 384, torch.bfloat16, seed=11), 4, 0.0
+    else:
+        inp = mi.make_inputs(case)
+        w = inp["workload"]
+        K, cf = w.K, w.capacity_factor
+    print(f"prebuilt tile table: {case}", flush=True)
+    N, H, O, Y = _bench_chain(inp, K, cf)
+    assert N > 0
+    assert torch.equal(H[0][:N], H[1][:N])
+    assert torch.equal(O[0][:N], O[1][:N])
+    assert torch.equal(Y[0], Y[1])
 
 
 # ---------------------------------------------------------------- full workloads
