@@ -353,6 +353,15 @@ __device__ __forceinline__ int wr_swizzle(int r) {
 template <int NBW>
 struct RouteGeo {
   static constexpr int Epad = 32 * NBW;
+  // Waves: 4 (2 token halves x 2 expert halves), or 8 (2 x 4) from 128
+  // padded experts on.  One workgroup per CU either way; 8 waves put two on
+  // each SIMD, so one wave's LDS and barrier waits overlap the other's MFMAs
+  // (measured: E = 256, T = 32768, d = 4096: 133 -> 122 us; E = 128: 30 ->
+  // 29 us).  Below 128 the W_r tile has too few copies to split over 8 waves.
+  static constexpr int NW = (NBW >= 4) ? 8 : 4;
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int WN = NW / 2;                  // waves along the experts
+  static constexpr int CBW = 2 * NBW / WN;           // 16-expert MFMA blocks per wave
   // LDS stages (X tile + W_r tile each).  Four at every width (E = 256: 4 x
   // 40 KB, the whole LDS; 136 instead of 144 us with three at T = 32768,
   // d = 4096); more at E = 128 were slower (five or six: 34-35 against 30 us).
@@ -363,8 +372,9 @@ struct RouteGeo {
   static constexpr int S = Epad + 16;                // floats per score row
   static constexpr int kLds = (NST * kStage > kTok * S * 4) ? NST * kStage : kTok * S * 4;
   static_assert(kLds <= 160 * 1024, "one workgroup's LDS");
-  static constexpr int kXInstr = kX / 1024 / 4;      // copies per wave per tile (4 waves)
-  static constexpr int kWInstr = kW / 1024 / 4;
+  static constexpr int kXInstr = kX / 1024 / NW;     // copies per wave per tile
+  static constexpr int kWInstr = kW / 1024 / NW;
+  static_assert(kXInstr * 1024 * NW == kX && kWInstr * 1024 * NW == kW, "copy split");
   static constexpr int kInstr = kXInstr + kWInstr;
   static constexpr int CPR = Epad / 8;               // 16-byte chunks per W_r tile row
   static constexpr int kWRows = 64 / CPR;            // W_r rows per copy instruction
@@ -383,20 +393,20 @@ __device__ __forceinline__ void wait_stages(int pending) {
 // partial scores to partial[ks][T][Epad]; route_sum_kernel and
 // route_select_kernel finish.
 template <int NBW>
-__global__ __launch_bounds__(kThreads, 1) void route_staged_kernel(
+__global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
     int d, int E, int K, int ksplit, float* __restrict__ partial) {
   using G = RouteGeo<NBW>;
   constexpr int Epad = G::Epad, NST = G::NST, CPR = G::CPR;
-  constexpr int XI = G::kXInstr, WI = G::kWInstr;
+  constexpr int XI = G::kXInstr, WI = G::kWInstr, CBW = G::CBW;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   float* L = reinterpret_cast<float*>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / G::WN, wn = w - (w / G::WN) * G::WN;
   const int64_t t0 = (int64_t)blockIdx.x * kTok;
   const int KT_all = d / kBK;
   const int kt0 = (int)(((int64_t)blockIdx.y * KT_all) / ksplit);   // this workgroup's k-steps
@@ -460,23 +470,23 @@ __global__ __launch_bounds__(kThreads, 1) void route_staged_kernel(
       xo[rb][ks] = r * 128 + ((c ^ ((r >> 1) & 7)) * 16);
     }
   const int g = lane >> 4, s4 = lane & 15;
-  int wo[NBW][2][2];
+  int wo[CBW][2][2];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
+  for (int nb = 0; nb < CBW; ++nb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int r = 32 * ks + 8 * g + (s4 >> 2) + 4 * h;
-        const int col = wn * 16 * NBW + nb * 16 + 4 * (s4 & 3);
+        const int col = wn * 16 * CBW + nb * 16 + 4 * (s4 & 3);
         wo[nb][ks][h] = G::kX + r * (Epad * 2) + (((col >> 3) ^ wr_swizzle<CPR>(r)) * 16) + (col & 7) * 2;
       }
 
-  f32x4 acc[2][NBW];
+  f32x4 acc[2][CBW];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < CBW; ++nb) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
@@ -495,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void route_staged_kernel(
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) a[rb] = *reinterpret_cast<const bf16x8*>(S + xo[rb][ks]);
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
+      for (int nb = 0; nb < CBW; ++nb) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(S + wo[nb][ks][0]));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -512,11 +522,11 @@ __global__ __launch_bounds__(kThreads, 1) void route_staged_kernel(
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
+      for (int nb = 0; nb < CBW; ++nb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int64_t t = t0 + wm * 32 + rb * 16 + 4 * (lane >> 4) + r;
-          const int col = wn * 16 * NBW + nb * 16 + (lane & 15);
+          const int col = wn * 16 * CBW + nb * 16 + (lane & 15);
           if (t < T) partial[((int64_t)blockIdx.y * T + t) * Epad + col] = acc[rb][nb][r];
         }
     return;
@@ -524,25 +534,34 @@ __global__ __launch_bounds__(kThreads, 1) void route_staged_kernel(
 
   // scores (+ bias; -inf in the padding columns) -> LDS, reusing the stage
   // buffers once every wave is done reading them
-  float bcol[NBW];
+  float bcol[CBW];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const int col = wn * 16 * NBW + nb * 16 + (lane & 15);
+  for (int nb = 0; nb < CBW; ++nb) {
+    const int col = wn * 16 * CBW + nb * 16 + (lane & 15);
     bcol[nb] = (col < E) ? (bias ? bias[col] : 0.f) : -__builtin_inff();
   }
   __syncthreads();
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
+    for (int nb = 0; nb < CBW; ++nb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wm * 32 + rb * 16 + 4 * (lane >> 4) + r;
-        const int col = wn * 16 * NBW + nb * 16 + (lane & 15);
+        const int col = wn * 16 * CBW + nb * 16 + (lane & 15);
         L[row * G::S + col] = (col < E) ? acc[rb][nb][r] + bcol[nb] : bcol[nb];
       }
   __syncthreads();
-  route_tail<2 * NBW, true>(L, G::S, t0, T, E, K, Epad, bias, logits, ids, gates);
+  // optional export by every thread, then the selection by waves 0-3 (16
+  // tokens each; it has no workgroup barrier, so the other waves may leave)
+  if (logits) {
+    for (int idx = tid; idx < kTok * E; idx += G::kThreads) {
+      const int r = idx / E, e = idx - (idx / E) * E;
+      if (t0 + r < T) logits[(t0 + r) * E + e] = L[r * G::S + e];
+    }
+    __syncthreads();  // selection rewrites the rows being exported
+  }
+  if (w < kTok / 16) topk_from_lds<2 * NBW>(L, G::S, t0, T, E, K, ids, gates);
 }
 
 // Split-k finish, part 1: partial[0] = sum over ks of partial[ks], in ks
@@ -625,7 +644,7 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            RouteGeo<NBW>::kLds);
       if (err != hipSuccess) return err;
-      hipLaunchKernelGGL(kern, dim3(grid.x, (unsigned)ksplit), dim3(kThreads),
+      hipLaunchKernelGGL(kern, dim3(grid.x, (unsigned)ksplit), dim3(RouteGeo<NBW>::kThreads),
                          (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)W_r,
                          bias, logits, ids, gates, p.T, p.d, p.E, p.K, ksplit, partial);
       if (ksplit > 1) {
