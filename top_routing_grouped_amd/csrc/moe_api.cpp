@@ -211,6 +211,10 @@ moe_status run_permute(const moe::Problem& p, const int32_t* ids, int32_t* count
                        int32_t* offsets, int32_t* raw, int32_t* perm, int32_t* inv,
                        unsigned char* ws, int32_t* table, hipStream_t s) {
   PermuteWs w = carve_permute(p, ws);
+  if (moe::permute_blocks(p.T) == 1)
+    return hip_status(moe::launch_permute_one_block(p, ids, raw ? raw : w.raw, counts, offsets,
+                                                    table, perm, inv, s),
+                      "permutation launch");
   MOE_TRY(hip_status(moe::launch_histogram(p, ids, w.blockcnt, s), "histogram launch"));
   MOE_TRY(hip_status(moe::launch_scan(p, w.blockcnt, w.blockbase, raw ? raw : w.raw, counts,
                                       offsets, table, s),

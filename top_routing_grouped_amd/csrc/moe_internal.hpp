@@ -86,6 +86,11 @@ hipError_t launch_scatter(const Problem& p, const int32_t* ids, const int32_t* b
                           hipStream_t s);
 hipError_t launch_tile_table(const Problem& p, const int32_t* offsets, int32_t* table,
                              hipStream_t s);
+// The whole permutation in one workgroup when permute_blocks(p.T) == 1
+// (outputs identical to histogram + scan + scatter; table may be NULL).
+hipError_t launch_permute_one_block(const Problem& p, const int32_t* ids, int32_t* raw,
+                                   int32_t* counts, int32_t* offsets, int32_t* table,
+                                   int32_t* perm, int32_t* inv, hipStream_t s);
 
 // Hpre (bf16 only, may be NULL): also store the pre-activations [rows][2n]
 // (x W_gate | x W_up) for the backward.
