@@ -69,12 +69,14 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// Top-K of 64 tokens whose scores sit in LDS (row stride S floats, padded
-// columns hold -inf).  Wave w handles tokens 16w..16w+15; DPP row q takes
-// tokens 16w+4q+r, r = 0..3; lane i of the row holds experts i + 16j.
-// Round results go to ids (global) and, as values, back into the token's own
-// LDS row (no longer read) for the gate pass.
-template <int V>
+// Top-K of the tokens whose scores sit in LDS (row stride S floats, padded
+// columns hold -inf).  Each 16-lane DPP row takes R tokens, so wave w
+// handles tokens 4Rw .. 4Rw + 4R - 1 and DPP row q takes tokens 4Rw + Rq + r,
+// r < R; lane i of the row holds experts i + 16j.  Round results go to ids
+// (global) and, as values, back into the token's own LDS row (no longer
+// read) for the gate pass.  Larger R interleaves more independent chains
+// per wave; smaller R spreads the tokens over more waves.
+template <int V, int R = 4>
 __device__ __forceinline__ void topk_from_lds(float* L, int S, int64_t t0, int64_t T, int E, int K,
                                               int32_t* __restrict__ ids, float* __restrict__ gates) {
   const int lane = threadIdx.x & 63;
@@ -82,31 +84,31 @@ __device__ __forceinline__ void topk_from_lds(float* L, int S, int64_t t0, int64
   const int q = lane >> 4;
   const int i = lane & 15;
   constexpr int kRetired = (int)0x80000000;
-  int key[4][V];
+  int key[R][V];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float* row = L + (16 * w + 4 * q + r) * S;
+  for (int r = 0; r < R; ++r) {
+    const float* row = L + (4 * R * w + R * q + r) * S;
 #pragma unroll
     for (int j = 0; j < V; ++j) key[r][j] = sort_key(row[i + 16 * j]);
   }
-  int top[4];
+  int top[R];
   for (int k = 0; k < K; ++k) {
-    // the four tokens of a row are independent chains: keep them in one
+    // the R tokens of a row are independent chains: keep them in one
     // branch-free block so their DPP steps interleave
-    int m[4], cand[4];
+    int m[R], cand[R];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < R; ++r) {
       m[r] = key[r][0];
 #pragma unroll
       for (int j = 1; j < V; ++j) m[r] = max(m[r], key[r][j]);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) m[r] = row_max16(m[r]);
+    for (int r = 0; r < R; ++r) m[r] = row_max16(m[r]);
     // Candidate = lowest expert id whose key equals the row maximum, and the
     // winner's key is retired.  Written with plain integer arithmetic (no
     // compare masks), so the four chains need no scalar mask registers.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < R; ++r) {
       cand[r] = 0x7FFFFFFF;
 #pragma unroll
       for (int j = 0; j < V; ++j) {
@@ -115,9 +117,9 @@ __device__ __forceinline__ void topk_from_lds(float* L, int S, int64_t t0, int64
       }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) cand[r] = row_min16(cand[r]);
+    for (int r = 0; r < R; ++r) cand[r] = row_min16(cand[r]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < R; ++r) {
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         const uint32_t keep = 0u - min((uint32_t)((i + 16 * j) ^ cand[r]), 1u);  // 0 iff winner
@@ -127,8 +129,8 @@ __device__ __forceinline__ void topk_from_lds(float* L, int S, int64_t t0, int64
     }
     if (i == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tl = 16 * w + 4 * q + r;
+      for (int r = 0; r < R; ++r) {
+        const int tl = 4 * R * w + R * q + r;
         L[tl * S + k] = key_value(m[r]);
         if (t0 + tl < T) ids[(t0 + tl) * K + k] = cand[r];
       }
@@ -139,8 +141,8 @@ __device__ __forceinline__ void topk_from_lds(float* L, int S, int64_t t0, int64
   // gates: softmax over the K selected scores (the full-softmax denominator
   // cancels in the renormalisation).
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int tl = 16 * w + 4 * q + r;
+  for (int r = 0; r < R; ++r) {
+    const int tl = 4 * R * w + R * q + r;
     const float m0 = key_value(top[r]);
     float part = 0.f;
     for (int c = i; c < K; c += 16) part += expf(L[tl * S + c] - m0);
@@ -552,8 +554,8 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
         L[row * G::S + col] = (col < E) ? acc[rb][nb][r] + bcol[nb] : bcol[nb];
       }
   __syncthreads();
-  // optional export by every thread, then the selection by waves 0-3 (16
-  // tokens each; it has no workgroup barrier, so the other waves may leave)
+  // optional export by every thread, then the selection by every wave
+  // (64 / NW tokens each: 16 with 4 waves, 8 with 8)
   if (logits) {
     for (int idx = tid; idx < kTok * E; idx += G::kThreads) {
       const int r = idx / E, e = idx - (idx / E) * E;
@@ -561,7 +563,7 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
     }
     __syncthreads();  // selection rewrites the rows being exported
   }
-  if (w < kTok / 16) topk_from_lds<2 * NBW>(L, G::S, t0, T, E, K, ids, gates);
+  topk_from_lds<2 * NBW, kTok / (4 * G::NW)>(L, G::S, t0, T, E, K, ids, gates);
 }
 
 // Split-k finish, part 1: partial[0] = sum over ks of partial[ks], in ks
@@ -588,24 +590,35 @@ __global__ __launch_bounds__(kThreads) void route_sum_kernel(float* __restrict__
   P[i] = v;
 }
 
-// Split-k finish, part 2: the summed scores of 64 tokens, plus bias (-inf in
-// the padding), then the same selection tail as the unsplit router.
+// Split-k finish, part 2: the summed scores of TW tokens per workgroup, plus
+// bias (-inf in the padding), then the selection by 4 waves of 4R tokens.
+// Wide expert ranges (E > 64) take TW = 16 and one token per DPP row, so the
+// serial selection chains of a small batch spread over several CUs (decode,
+// T = 64, E = 256: the route 30 -> 21 us); narrower ones keep TW = 64, R = 4.
+template <int NBW>
+struct SelGeo {
+  static constexpr int Epad = 32 * NBW, S = Epad + 16;
+  static constexpr int TW = (NBW >= 4) ? 16 : kTok;
+  static constexpr int R = TW / 16;
+  static constexpr int kLds = TW * S * 4;
+};
 template <int NBW>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const float* __restrict__ scores, const float* __restrict__ bias, float* __restrict__ logits,
     int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T, int E, int K) {
-  constexpr int Epad = 32 * NBW, S = Epad + 16;
+  using G = SelGeo<NBW>;
+  constexpr int Epad = G::Epad, S = G::S, TW = G::TW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   float* L = reinterpret_cast<float*>(smem);
-  const int64_t t0 = (int64_t)blockIdx.x * kTok;
+  const int64_t t0 = (int64_t)blockIdx.x * TW;
   // Each thread owns one 4-column group and kPer rows of it: all of its
   // 16-byte loads are issued before the first is used (one at a time, the
   // 64 x Epad scores took ~30 us of L2 round trips at Epad = 256).
   using f4 = float __attribute__((ext_vector_type(4)));
   constexpr int kGroups = Epad / 4;                  // 4-column groups per row
   constexpr int kRowStep = kThreads / kGroups;
-  constexpr int kPer = kTok / kRowStep;              // rows per thread (2 * NBW)
-  static_assert(kRowStep * kGroups == kThreads && kPer * kRowStep == kTok, "score split");
+  constexpr int kPer = TW / kRowStep;                // rows per thread
+  static_assert(kRowStep * kGroups == kThreads && kPer * kRowStep == TW, "score split");
   const int c4 = threadIdx.x % kGroups, r0 = threadIdx.x / kGroups;
   float bv[4];
 #pragma unroll
@@ -628,7 +641,14 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
     *reinterpret_cast<f4*>(L + (r0 + kRowStep * i) * S + 4 * c4) = o;
   }
   __syncthreads();
-  route_tail<2 * NBW, true>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates);
+  if (logits) {
+    for (int idx = threadIdx.x; idx < TW * E; idx += kThreads) {
+      const int r = idx / E, e = idx - (idx / E) * E;
+      if (t0 + r < T) logits[(t0 + r) * E + e] = L[r * S + e];
+    }
+    __syncthreads();  // selection rewrites the rows being exported
+  }
+  topk_from_lds<2 * NBW, G::R>(L, S, t0, T, E, K, ids, gates);
 }
 
 // ---------------------------------------------------------------- fp32 router (plain FMA)
@@ -678,13 +698,13 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
                            dim3(kThreads), 0, s, partial, ksplit, n4);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
-        constexpr int kSelLds = kTok * (32 * NBW + 16) * 4;
+        constexpr int kSelLds = SelGeo<NBW>::kLds, TW = SelGeo<NBW>::TW;
         auto* sel = route_select_kernel<NBW>;
         err = hipFuncSetAttribute(reinterpret_cast<const void*>(sel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kSelLds);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(sel, grid, dim3(kThreads), (size_t)kSelLds, s, partial, bias, logits,
-                           ids, gates, p.T, p.E, p.K);
+        hipLaunchKernelGGL(sel, dim3((unsigned)((p.T + TW - 1) / TW)), dim3(kThreads),
+                           (size_t)kSelLds, s, partial, bias, logits, ids, gates, p.T, p.E, p.K);
       }
     } else
       hipLaunchKernelGGL((route_bf16_kernel<NBW, false>), grid, dim3(kThreads), 0, s,
