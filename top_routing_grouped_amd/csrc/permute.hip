@@ -28,6 +28,7 @@ namespace {
 constexpr int kB = kPermuteBlock;        // tokens per block (== threads)
 constexpr int kWords = kB / 32;          // bitmask words per expert
 constexpr int kScanThreads = 1024;
+constexpr int kChunk = 8;                // ids loaded per round trip
 
 __global__ __launch_bounds__(kB) void histogram_kernel(const int32_t* __restrict__ ids,
                                                        int32_t* __restrict__ blockcnt, int64_t T,
@@ -39,9 +40,18 @@ __global__ __launch_bounds__(kB) void histogram_kernel(const int32_t* __restrict
   const int64_t ntok = (T - tb < kB) ? (T - tb) : kB;
   const int64_t nid = ntok * K;
   const int32_t* base = ids + tb * K;
-  for (int64_t j = threadIdx.x; j < nid; j += kB) {
-    const int e = base[j];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  // kChunk independent loads per round trip (a load feeding a branch is
+  // otherwise waited for before the next one is issued)
+  for (int64_t j0 = 0; j0 < nid; j0 += (int64_t)kB * kChunk) {
+    int ee[kChunk];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const int64_t j = j0 + threadIdx.x + (int64_t)kB * c;
+      ee[c] = j < nid ? base[j] : -1;
+    }
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c)
+      if (ee[c] >= 0 && ee[c] < E) atomicAdd(&cnt[ee[c]], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kB) blockcnt[(int64_t)blockIdx.x * E + e] = cnt[e];
@@ -160,27 +170,46 @@ __global__ __launch_bounds__(kB) void scatter_kernel(
   const bool valid = t < T;
   const int w = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
+  // a token's ids in chunks of kChunk independent loads, then per chunk the
+  // block bases and offsets of those experts (independent again)
   if (valid)
-    for (int k = 0; k < K; ++k) {
-      const int e = ids[t * K + k];
-      if (e >= 0 && e < E) atomicOr(&bits[e * kWords + w], bit);
+    for (int k0 = 0; k0 < K; k0 += kChunk) {
+      int ee[kChunk];
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) ee[c] = (k0 + c < K) ? ids[t * K + k0 + c] : -1;
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c)
+        if (ee[c] >= 0 && ee[c] < E) atomicOr(&bits[ee[c] * kWords + w], bit);
     }
   __syncthreads();
   if (!valid) return;
-  for (int k = 0; k < K; ++k) {
-    const int e = ids[t * K + k];
-    int32_t slot = -1;
-    if (e >= 0 && e < E) {
-      const uint32_t* m = bits + e * kWords;
-      int below = __popc(m[w] & (bit - 1u));
-      for (int ww = 0; ww < w; ++ww) below += __popc(m[ww]);
-      const int64_t rank = (int64_t)blockbase[(int64_t)blockIdx.x * E + e] + below;
-      if (rank < C) {
-        slot = (int32_t)(offsets[e] + rank);
-        perm[slot] = (int32_t)t;
-      }
+  for (int k0 = 0; k0 < K; k0 += kChunk) {
+    int ee[kChunk], bb[kChunk], oo[kChunk];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) ee[c] = (k0 + c < K) ? ids[t * K + k0 + c] : -1;
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const bool ok = ee[c] >= 0 && ee[c] < E;
+      bb[c] = ok ? blockbase[(int64_t)blockIdx.x * E + ee[c]] : 0;
+      oo[c] = ok ? offsets[ee[c]] : 0;
     }
-    inv[t * K + k] = slot;
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      if (k0 + c >= K) break;
+      const int e = ee[c];
+      int32_t slot = -1;
+      if (e >= 0 && e < E) {
+        const uint32_t* m = bits + e * kWords;
+        int below = __popc(m[w] & (bit - 1u));
+        for (int ww = 0; ww < w; ++ww) below += __popc(m[ww]);
+        const int64_t rank = (int64_t)bb[c] + below;
+        if (rank < C) {
+          slot = (int32_t)(oo[c] + rank);
+          perm[slot] = (int32_t)t;
+        }
+      }
+      inv[t * K + k0 + c] = slot;
+    }
   }
 }
 
@@ -205,12 +234,16 @@ __global__ __launch_bounds__(kB) void permute_one_block_kernel(
   const int w = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
   if (valid)
-    for (int k = 0; k < K; ++k) {
-      const int e = ids[(int64_t)tid * K + k];
-      if (e >= 0 && e < E) {
-        atomicAdd(&cnt[e], 1);
-        atomicOr(&bits[e * kWords + w], bit);
-      }
+    for (int k0 = 0; k0 < K; k0 += kChunk) {
+      int ee[kChunk];
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) ee[c] = (k0 + c < K) ? ids[(int64_t)tid * K + k0 + c] : -1;
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c)
+        if (ee[c] >= 0 && ee[c] < E) {
+          atomicAdd(&cnt[ee[c]], 1);
+          atomicOr(&bits[ee[c] * kWords + w], bit);
+        }
     }
   __syncthreads();
   const int r = (tid < E) ? cnt[tid] : 0;
@@ -236,19 +269,26 @@ __global__ __launch_bounds__(kB) void permute_one_block_kernel(
   }
   __syncthreads();                            // offs complete
   if (!valid) return;
-  for (int k = 0; k < K; ++k) {
-    const int e = ids[(int64_t)tid * K + k];
-    int32_t slot = -1;
-    if (e >= 0 && e < E) {
-      const uint32_t* m = bits + e * kWords;
-      int below = __popc(m[w] & (bit - 1u));
-      for (int ww = 0; ww < w; ++ww) below += __popc(m[ww]);
-      if ((int64_t)below < C) {
-        slot = (int32_t)(offs[e] + below);
-        perm[slot] = tid;
+  for (int k0 = 0; k0 < K; k0 += kChunk) {
+    int ee[kChunk];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) ee[c] = (k0 + c < K) ? ids[(int64_t)tid * K + k0 + c] : -1;
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      if (k0 + c >= K) break;
+      const int e = ee[c];
+      int32_t slot = -1;
+      if (e >= 0 && e < E) {
+        const uint32_t* m = bits + e * kWords;
+        int below = __popc(m[w] & (bit - 1u));
+        for (int ww = 0; ww < w; ++ww) below += __popc(m[ww]);
+        if ((int64_t)below < C) {
+          slot = (int32_t)(offs[e] + below);
+          perm[slot] = tid;
+        }
       }
+      inv[(int64_t)tid * K + k0 + c] = slot;
     }
-    inv[(int64_t)tid * K + k] = slot;
   }
 }
 
