@@ -93,7 +93,8 @@ def test_small_layer_parity_each_gemm_path(T, d, E, K, n, dtype, cf, bias, path)
 
 
 @pytest.mark.parametrize("T,d,E,K", [(64, 4096, 256, 8), (100, 512, 64, 6), (700, 1024, 16, 2),
-                                     (3, 256, 128, 8)])
+                                     (3, 256, 128, 8),
+                                     (37, 512, 160, 7)])   # 16-token finishing blocks, ragged, padded E
 def test_route_with_and_without_k_split(T, d, E, K):
     """moe_route_ws splits the k range over workgroups for small batches;
     moe_route never does.  Both: logits within tolerance of fp64, ids and
