@@ -218,15 +218,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_bf16(
     bsrc[par] = base + (int64_t)e * Kd * N + (int64_t)(lane >> 5) * N + col;
   }
 
+  // Down projection: tile L starts its k loop at k-step L mod KT and wraps.
+  // An XCD starts about one tile per k-step, so the tiles running together
+  // then work on the same k slice and share it in L2 (the down projection's
+  // working set per XCD, ~10 row tiles and 3 column slices, is just above
+  // L2).  3% faster there; neutral for the up projection, which keeps the
+  // natural order.  The order of each tile's sum is fixed by L alone, so
+  // results stay bit-reproducible.
+  const int KTall = Kd / BK;
+  const int rot = UP ? 0 : L % KTall;
   auto issue_stage = [&](int kt) {
     const uint32_t As = lds_base + (uint32_t)((kt % kStages) * kStageBytes);
     const uint32_t Bs = As + kAStage;
+    int kk = kt + rot;
+    if (kk >= KTall) kk -= KTall;
 #pragma unroll
-    for (int i = 0; i < kAInstr; ++i) dev::lds_copy16(asrc[i] + kt * BK, As + (w * kAInstr + i) * 1024);
+    for (int i = 0; i < kAInstr; ++i) dev::lds_copy16(asrc[i] + kk * BK, As + (w * kAInstr + i) * 1024);
 #pragma unroll
     for (int i = 0; i < kBInstr; ++i) {
       const int jb = w * kBInstr + i;
-      dev::lds_copy16(bsrc[jb & 1] + (int64_t)(kt * BK + 2 * jb) * N, Bs + jb * 1024);
+      dev::lds_copy16(bsrc[jb & 1] + (int64_t)(kk * BK + 2 * jb) * N, Bs + jb * 1024);
     }
   };
 
