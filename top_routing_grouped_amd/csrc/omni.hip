@@ -126,7 +126,9 @@ __device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p))
 // (u, lane) with key k[u] (0 = empty) and a distinct id i[u] < 2^17 -- by
 // (key desc, id asc).  Lane q < r receives the q-th key and id.
 // Without a sort: the r-th largest key th by a bitwise search with ballot
-// counts, the ties at th resolved by the same search over ids, the winners
+// counts (over the bits below the common prefix of the largest and the
+// smallest non-empty key), the ties at th, when not all are taken, resolved
+// by the same search over ids, the winners
 // compacted to lanes 0..r-1 through LDS, then each winner's rank counted
 // against the others (readlane broadcasts) and the winners placed by rank.
 // Ballot counts and the searches run on the scalar unit.
@@ -134,25 +136,46 @@ template <int S>
 __device__ __forceinline__ void wave_top(const uint32_t* k, const int* id, int r, uint32_t* ok,
                                          int* oi, int* lk, int* li) {
   const int lane = threadIdx.x & 63;
-  uint32_t th = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  // th is a non-empty key (r never exceeds the non-empty entries), so it
+  // lies in [smallest non-empty key, largest key] and shares their common
+  // high bits: the search starts below the highest bit where they differ.
+  // Keys are compared as signed ints after flipping the top bit.
+  int smax = (int)0x80000000, snot = (int)0x80000000;   // max of s, max of ~s
+#pragma unroll
+  for (int u = 0; u < S; ++u) {
+    const int sk = (int)(k[u] ^ 0x80000000u);
+    smax = max(smax, sk);
+    if (k[u] != 0u) snot = max(snot, ~sk);
+  }
+  const uint32_t kmax = (uint32_t)wave_max_i(smax) ^ 0x80000000u;
+  const uint32_t kmin = (uint32_t)(~wave_max_i(snot)) ^ 0x80000000u;
+  const uint32_t diff = kmax ^ kmin;
+  const int top = diff ? 31 - __builtin_clz(diff) : -1;
+  uint32_t th = (top >= 0) ? (kmax & ~((2u << top) - 1u)) : kmax;
+  for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = th | (1u << bit);
     int c = 0;
 #pragma unroll
     for (int u = 0; u < S; ++u) c += wave_count(k[u] >= cand);
     if (c >= r) th = cand;
   }
-  int gt = 0;
+  int gt = 0, eq = 0;
 #pragma unroll
-  for (int u = 0; u < S; ++u) gt += wave_count(k[u] > th);
+  for (int u = 0; u < S; ++u) {
+    gt += wave_count(k[u] > th);
+    eq += wave_count(k[u] == th);
+  }
   const int need = r - gt;                       // ties at th to take, lowest ids first
-  int x = 0;                                     // the need-th smallest id among the ties
-  for (int bit = 16; bit >= 0; --bit) {
-    const int cand = x | (1 << bit);
-    int c = 0;
+  int x = (1 << 17) - 1;                         // every tie taken (the usual case: th unique)
+  if (need < eq) {
+    x = 0;                                       // the need-th smallest id among the ties
+    for (int bit = 16; bit >= 0; --bit) {
+      const int cand = x | (1 << bit);
+      int c = 0;
 #pragma unroll
-    for (int u = 0; u < S; ++u) c += wave_count(k[u] == th && id[u] < cand);
-    if (c < need) x = cand;
+      for (int u = 0; u < S; ++u) c += wave_count(k[u] == th && id[u] < cand);
+      if (c < need) x = cand;
+    }
   }
   // compact the r winners to positions 0..r-1 (slot-major, lane order)
   const uint64_t below = (1ull << lane) - 1ull;
