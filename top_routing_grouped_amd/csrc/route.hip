@@ -5,11 +5,12 @@
 // K a run-time value ([P4] "AI芯片如何支持MoE架构" §4.3), gates renormalised
 // over the selected experts.
 //
-// One workgroup = 64 tokens, 4 waves in a 2x2 grid over (32 tokens) x (half of
-// the padded expert range), 16x16x32 bf16 MFMA.  For E % 8 == 0 the X tile
-// (64 tokens x 64 k) and the W_r tile (64 k x E, natural [k][e] layout) of
-// each k-step go global -> LDS with global_load_lds_dwordx4 through 3-4
-// stages whose completion is counted with explicit vmcnt waits; the W_r tile
+// One workgroup = 64 tokens, 16x16x32 bf16 MFMA, waves in a 2 x (NW/2) grid
+// over (32 tokens) x (a slice of the padded expert range): 4 waves below 128
+// padded experts, 8 from 128 on.  For E % 8 == 0 the X tile (64 tokens x
+// 64 k) and the W_r tile (64 k x E, natural [k][e] layout) of each k-step go
+// global -> LDS with global_load_lds_dwordx4 through four stages whose
+// completion is counted with explicit vmcnt waits; the W_r tile
 // is read with the gfx950 transpose load (ds_read_b64_tr_b16), so the weights
 // need no transpose in memory, and both tiles are XOR-swizzled so that every
 // fragment read is bank-conflict free.  (Other E use a register-staged
