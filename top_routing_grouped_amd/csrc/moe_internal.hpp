@@ -74,6 +74,11 @@ inline size_t route_partial_bytes(const Problem& p) {
 // partial: route_partial_bytes(p) of workspace, or NULL (no k split).
 hipError_t launch_route(const Problem& p, const void* X, const void* W_r, const float* bias,
                         float* logits, int32_t* ids, float* gates, float* partial, hipStream_t s);
+// The fp32 scores X W1 and X W2 of the same bf16 tokens in one launch (no
+// bias, no selection); both widths must be multiples of 8 and at most 256.
+bool route_pair_supported(int E1, int E2);
+hipError_t launch_logits_pair(int64_t T, int d, int E1, int E2, const void* X, const void* W1,
+                              const void* W2, float* logits1, float* logits2, hipStream_t s);
 
 hipError_t launch_histogram(const Problem& p, const int32_t* ids, int32_t* blockcnt,
                             hipStream_t s);

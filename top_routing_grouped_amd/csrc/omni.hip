@@ -599,14 +599,21 @@ size_t omni_permute_ws_bytes(const OmniProblem& p, OmniPermuteWs* w, unsigned ch
 hipError_t launch_omni_route(const OmniProblem& p, const void* X, const void* W_r, const void* W_c,
                              float* ls_r, float* ls_c, int32_t* ids, float* gates,
                              const OmniRouteWs& w, hipStream_t s) {
-  // the two axis projections: the router GEMM with fp32 logits out (top-1
-  // outputs go to scratch)
+  // the two axis projections: the router GEMM with fp32 logits out.  Both in
+  // one launch where the widths allow it (twice the workgroups of one axis,
+  // which alone fills a quarter of the chip at T = 4096); otherwise one
+  // launch per axis, their top-1 outputs going to scratch.
   // (no k split: its extra selection pass costs more than it saves here)
-  hipError_t err = launch_route(axis_problem(p, p.Nr), X, W_r, nullptr, w.p_r, w.ids1, w.gates1,
-                                nullptr, s);
-  if (err != hipSuccess) return err;
-  err = launch_route(axis_problem(p, p.Nc), X, W_c, nullptr, w.p_c, w.ids1, w.gates1, nullptr, s);
-  if (err != hipSuccess) return err;
+  hipError_t err;
+  if (route_pair_supported(p.Nr, p.Nc)) {
+    err = launch_logits_pair(p.T, p.d, p.Nr, p.Nc, X, W_r, W_c, w.p_r, w.p_c, s);
+    if (err != hipSuccess) return err;
+  } else {
+    err = launch_route(axis_problem(p, p.Nr), X, W_r, nullptr, w.p_r, w.ids1, w.gates1, nullptr, s);
+    if (err != hipSuccess) return err;
+    err = launch_route(axis_problem(p, p.Nc), X, W_c, nullptr, w.p_c, w.ids1, w.gates1, nullptr, s);
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(omni_select_kernel, dim3((unsigned)((p.T + kWaves - 1) / kWaves)),
                      dim3(kThreads), 0, s, w.p_r, w.p_c, ls_r, ls_c, ids, gates, p.T, p.Nr, p.Nc,
                      p.K);

@@ -419,7 +419,8 @@ template <int NBW>
 __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
-    int d, int E, int K, int ksplit, float* __restrict__ partial) {
+    int d, int E, int K, int ksplit, float* __restrict__ partial, const uint16_t* __restrict__ Wr2,
+    float* __restrict__ logits2, int E2, int nblk) {
   using G = RouteGeo<NBW>;
   constexpr int Epad = G::Epad, NST = G::NST, CPR = G::CPR;
   constexpr int XI = G::kXInstr, WI = G::kWInstr, CBW = G::CBW;
@@ -430,7 +431,17 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / G::WN, wn = w - (w / G::WN) * G::WN;
-  const int64_t t0 = (int64_t)blockIdx.x * kTok;
+  // A second router matrix over the same tokens may share the launch
+  // (logits only, no selection): workgroups nblk.. take it.
+  int bx = blockIdx.x;
+  if (bx >= nblk) {
+    bx -= nblk;
+    Wr = Wr2;
+    logits = logits2;
+    E = E2;
+    ids = nullptr;
+  }
+  const int64_t t0 = (int64_t)bx * kTok;
   const int KT_all = d / kBK;
   const int kt0 = (int)(((int64_t)blockIdx.y * KT_all) / ksplit);   // this workgroup's k-steps
   const int KT = (int)(((int64_t)(blockIdx.y + 1) * KT_all) / ksplit) - kt0;
@@ -584,7 +595,7 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
     }
     __syncthreads();  // selection rewrites the rows being exported
   }
-  topk_from_lds<2 * NBW, kTok / (4 * G::NW)>(L, G::S, t0, T, E, K, ids, gates);
+  if (ids) topk_from_lds<2 * NBW, kTok / (4 * G::NW)>(L, G::S, t0, T, E, K, ids, gates);
 }
 
 // Split-k finish, part 1: partial[0] = sum over ks of partial[ks], in ks
@@ -710,7 +721,8 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
       if (err != hipSuccess) return err;
       hipLaunchKernelGGL(kern, dim3(grid.x, (unsigned)ksplit), dim3(RouteGeo<NBW>::kThreads),
                          (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)W_r,
-                         bias, logits, ids, gates, p.T, p.d, p.E, p.K, ksplit, partial);
+                         bias, logits, ids, gates, p.T, p.d, p.E, p.K, ksplit, partial,
+                         (const uint16_t*)nullptr, (float*)nullptr, 0, (int)grid.x);
       if (ksplit > 1) {
         err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -739,6 +751,39 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
 }
 
 }  // namespace
+
+namespace {
+template <int NBW>
+hipError_t launch_logits_pair_nbw(int64_t T, int d, int E1, int E2, const void* X, const void* W1,
+                                  const void* W2, float* logits1, float* logits2, hipStream_t s) {
+  auto* kern = route_staged_kernel<NBW>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       RouteGeo<NBW>::kLds);
+  if (err != hipSuccess) return err;
+  const unsigned nblk = (unsigned)((T + kTok - 1) / kTok);
+  hipLaunchKernelGGL(kern, dim3(2 * nblk, 1), dim3(RouteGeo<NBW>::kThreads),
+                     (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)W1,
+                     (const float*)nullptr, logits1, (int32_t*)nullptr, (float*)nullptr, T, d, E1,
+                     1, 1, (float*)nullptr, (const uint16_t*)W2, logits2, E2, (int)nblk);
+  return hipGetLastError();
+}
+}  // namespace
+
+bool route_pair_supported(int E1, int E2) {
+  return E1 % 8 == 0 && E2 % 8 == 0 && E1 >= 1 && E2 >= 1 && E1 <= 256 && E2 <= 256;
+}
+
+hipError_t launch_logits_pair(int64_t T, int d, int E1, int E2, const void* X, const void* W1,
+                              const void* W2, float* logits1, float* logits2, hipStream_t s) {
+  if (!route_pair_supported(E1, E2)) return hipErrorInvalidValue;
+  if (T == 0) return hipSuccess;
+  const int nbw = route_nbw(E1 > E2 ? E1 : E2);
+  if (nbw <= 1) return launch_logits_pair_nbw<1>(T, d, E1, E2, X, W1, W2, logits1, logits2, s);
+  if (nbw <= 2) return launch_logits_pair_nbw<2>(T, d, E1, E2, X, W1, W2, logits1, logits2, s);
+  if (nbw <= 4) return launch_logits_pair_nbw<4>(T, d, E1, E2, X, W1, W2, logits1, logits2, s);
+  return launch_logits_pair_nbw<8>(T, d, E1, E2, X, W1, W2, logits1, logits2, s);
+}
 
 hipError_t launch_route(const Problem& p, const void* X, const void* W_r, const float* bias,
                         float* logits, int32_t* ids, float* gates, float* partial, hipStream_t s) {
