@@ -58,6 +58,8 @@ SHAPES = [
     (50, 64, 8, 8, 64),          # K = N: every expert
     (64, 256, 256, 256, 64),     # largest axes and K
     (3, 64, 5, 5, 7),            # K above each axis' length
+    (200, 128, 16, 64, 12),      # both axes in one router launch, the first padded to 64
+    (130, 192, 136, 8, 9),       # both axes in one router launch, the second padded to 256
 ]
 
 
