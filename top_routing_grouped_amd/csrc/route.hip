@@ -70,25 +70,41 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// Sorts v[0..V) into descending order with Batcher's odd-even merge
-// network (V a power of two; after unrolling every index is a constant, so
-// the entries stay in registers).
+// Batcher's odd-even merge network on V inputs (V a power of two), listed
+// at compile time: comparator c orders entries lo[c] < hi[c].
+template <int V>
+struct BatcherNet {
+  int lo[V * V] = {}, hi[V * V] = {};
+  int n = 0;
+  constexpr BatcherNet() {
+    for (int p = 1; p < V; p <<= 1)
+      for (int k = p; k >= 1; k >>= 1)
+        for (int j = k % p; j + k < V; j += 2 * k)
+          for (int i = 0; i < k && i < V - j - k; ++i)
+            if ((i + j) / (2 * p) == (i + j + k) / (2 * p)) {
+              lo[n] = i + j;
+              hi[n] = i + j + k;
+              ++n;
+            }
+  }
+};
+
+// Sorts v[0..V) into descending order.  The comparator list is a constant
+// and the loop over it has a constant trip count, so after unrolling every
+// index is a constant and the entries stay in registers.  (Written as nested
+// loops over the network's stages, the 16-entry case was not fully unrolled
+// in one kernel: the entries were then picked by chains of selects and the
+// decode-batch selection took 33 instead of 5 us.)
 template <int V>
 __device__ __forceinline__ void sort_desc(int64_t* v) {
+  constexpr BatcherNet<V> net{};
 #pragma unroll
-  for (int p = 1; p < V; p <<= 1)
-#pragma unroll
-    for (int k = p; k >= 1; k >>= 1)
-#pragma unroll
-      for (int j = k % p; j + k < V; j += 2 * k)
-#pragma unroll
-        for (int i = 0; i < k; ++i)
-          if (i < V - j - k && (i + j) / (2 * p) == (i + j + k) / (2 * p)) {
-            const int64_t a = v[i + j], b = v[i + j + k];
-            const bool sw = b > a;
-            v[i + j] = sw ? b : a;
-            v[i + j + k] = sw ? a : b;
-          }
+  for (int c = 0; c < net.n; ++c) {
+    const int64_t a = v[net.lo[c]], b = v[net.hi[c]];
+    const bool sw = b > a;
+    v[net.lo[c]] = sw ? b : a;
+    v[net.hi[c]] = sw ? a : b;
+  }
 }
 
 // Top-K of the tokens whose scores sit in LDS (row stride S floats, padded
@@ -101,9 +117,9 @@ __device__ __forceinline__ void sort_desc(int64_t* v) {
 // heads holding it, and the lane that owns that id pops its head.  (The lowest
 // id of the maximum key in a lane is that lane's head, so this is the lowest
 // id of the maximum overall, as the oracle rules.)  Rescanning all V entries
-// every round took about twice the VALU instructions (the router 22.6
-// instead of 21.9 us at E = 128, 115.5 instead of 111.4 at E = 256).  Round
-// results go to ids (global) and, as values,
+// every round takes about twice the VALU instructions; measured, the router
+// gains 0.3-0.7 us at E = 128 and is within run-to-run noise (+-3 us of
+// 113) at E = 256.  Round results go to ids (global) and, as values,
 // back into the token's own LDS row (no longer read) for the gate pass.
 template <int V, int R = 4>
 __device__ __forceinline__ void topk_from_lds(float* L, int S, int64_t t0, int64_t T, int E, int K,
@@ -141,11 +157,19 @@ __device__ __forceinline__ void topk_from_lds(float* L, int S, int64_t t0, int64
     for (int r = 0; r < R; ++r) cand[r] = row_min16(cand[r]);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      // ids are distinct within the row, so exactly one lane pops
+      // ids are distinct within the row, so exactly one lane pops.  The pop
+      // is a bitwise blend under an opaque all-ones / all-zeros mask: written
+      // as selects, the compiler turned the shift into loads at index j + win
+      // and so into compare-and-select chains over every entry (quadratic in
+      // V, and at V = 16 the masks spilled to vector lanes).
       const bool win = ((int)(v[r][0] >> 32) == m[r]) && (255 - (int)(uint32_t)v[r][0] == cand[r]);
+      int wm32 = win ? -1 : 0;
+      asm volatile("" : "+v"(wm32));
+      const uint64_t wmask = (uint64_t)(int64_t)wm32;
 #pragma unroll
-      for (int j = 0; j + 1 < V; ++j) v[r][j] = win ? v[r][j + 1] : v[r][j];
-      v[r][V - 1] = win ? kRetired : v[r][V - 1];
+      for (int j = 0; j + 1 < V; ++j)
+        v[r][j] = (int64_t)(((uint64_t)v[r][j + 1] & wmask) | ((uint64_t)v[r][j] & ~wmask));
+      v[r][V - 1] = (int64_t)(((uint64_t)kRetired & wmask) | ((uint64_t)v[r][V - 1] & ~wmask));
       if (k == 0) top[r] = m[r];
     }
     if (i == 0) {
