@@ -43,8 +43,8 @@ Parity status: pinned by ``-m "not gpu"`` tests against central finite
 differences of the forward oracle's loss sum(Y * dY) on small float64 layers
 (with and without capacity drops), by the identity <dY, O> = <dA', A> and by
 the zero row sums of dl (a softmax Jacobian maps onto the sum-zero plane).
-``sampled_backward`` is pinned to ``backward`` on small layers (every expert
-and token listed).
+``sampled_backward`` and ``backward_by_expert`` are pinned to ``backward`` on
+small layers (every expert and token listed).
 """
 
 from __future__ import annotations
@@ -246,3 +246,52 @@ def sampled_backward(dY, rec, X, W_r, W_gate, W_up, W_down, experts=(), tokens=(
         out["dl"][t] = dl
         out["dX"][t] = dxs + dl @ _f64(W_r).T
     return out
+
+
+def backward_by_expert(dY, rec, X, W_r, W_gate, W_up, W_down, visit=None) -> dict:
+    """All gradients of ``backward``, computed one expert at a time.
+
+    The same steps as ``expert_backward``, ``router_backward`` and
+    ``backward`` ([P5] §6.4, §6.3), arranged so that only one expert's rows
+    and weight gradients exist at a time: for each expert e with kept slots
+    [lo, hi) the pre-activations are recomputed from its gathered rows,
+    dA' = dY W_down^T, dS = <dA', A> and the dSwiGLU terms follow, the
+    callback ``visit(e, dW_gate_e, dW_up_e, dW_down_e)`` (if given) sees the
+    expert's weight gradients, and each slot's input gradient is added to
+    its token's dX row.  Then the router part (dl from dS) and dX, dW_r.
+    ``rec`` is a ``route_record`` (or ``forward_train``) result.  Returns
+    dX, dW_r, dl, dg and dS[N]; the per-expert weight gradients are only
+    handed to ``visit``."""
+    X, dY = np.asarray(X), np.asarray(dY)
+    offsets = np.asarray(rec["offsets"], dtype=np.int64)
+    perm = np.asarray(rec["perm_token"], dtype=np.int64)
+    inv = np.asarray(rec["inv_slot"], dtype=np.int64)
+    T, d = X.shape
+    E = len(offsets) - 1
+    N = int(offsets[E])
+    gs = slot_gates(rec["gates"], inv, N)
+    dS = np.zeros(N)
+    dX_ffn = np.zeros((T, d))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        rows = perm[lo:hi]
+        if np.any(np.diff(rows) <= 0):
+            raise ValueError("backward_by_expert: tokens of a segment must be strictly increasing")
+        Xe, dYe = _f64(X[rows]), _f64(dY[rows])
+        Wg, Wu, Wd = _f64(W_gate[e]), _f64(W_up[e]), _f64(W_down[e])
+        Hg, Hu = Xe @ Wg, Xe @ Wu
+        A = mo.silu(Hg) * Hu
+        ge = gs[lo:hi, None]
+        dAp = dYe @ Wd.T
+        dS[lo:hi] = np.sum(dAp * A, axis=1)
+        dA = ge * dAp
+        dHg = dA * Hu * dsilu(Hg)
+        dHu = dA * mo.silu(Hg)
+        if visit is not None:
+            visit(e, Xe.T @ dHg, Xe.T @ dHu, A.T @ (ge * dYe))
+        dX_ffn[rows] += dHg @ Wg.T + dHu @ Wu.T
+    dl, dg = router_backward(dS, rec, T, np.asarray(W_r).shape[1])
+    return {"dS": dS, "dl": dl, "dg": dg, "dW_r": _f64(X).T @ dl,
+            "dX": dX_ffn + dl @ _f64(W_r).T}

@@ -313,12 +313,74 @@ def slot_outputs(slots, X, offsets, perm_token, W_gate, W_up, W_down):
     return np.array(hs), np.array(os_)
 
 
+def forward_by_expert(X, gates, offsets, perm_token, inv_slot, W_gate, W_up, W_down,
+                      visit=None) -> np.ndarray:
+    """Steps 6-8 one expert at a time; returns Y [T, d] in float64.
+
+    The same definitions as ``grouped_ffn`` followed by ``combine`` ([P5] §3
+    steps 3-6, §1), arranged so that only one expert's H and O rows exist at
+    a time: for each expert e with kept slots [lo, hi) the rows
+    a = X[perm_token[lo:hi]] go through the expert (``expert_ffn``), the
+    callback ``visit(e, lo, hi, h, o)`` (if given) sees that segment of H and
+    O, and each row o_s, times the gate of its (token, k) entry, is added to
+    its token's row of Y.  Inside a segment the tokens are strictly
+    increasing (R7), so every token occurs at most once there; this is
+    checked.  Used where the whole H and O would not fit in memory.
+    """
+    X = np.asarray(X)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    perm_token = np.asarray(perm_token, dtype=np.int64)
+    inv_slot = np.asarray(inv_slot, dtype=np.int64)
+    g = _f64(gates)
+    T, d = X.shape
+    E = len(offsets) - 1
+    N = int(offsets[E])
+    kept = inv_slot >= 0
+    slot_gate = np.zeros(N)
+    slot_gate[inv_slot[kept]] = g[kept]
+    Y = np.zeros((T, d))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        toks = perm_token[lo:hi]
+        if np.any(np.diff(toks) <= 0):
+            raise ValueError("forward_by_expert: tokens of a segment must be strictly increasing")
+        h, o = expert_ffn(_f64(X[toks]), W_gate[e], W_up[e], W_down[e])
+        if visit is not None:
+            visit(e, lo, hi, h, o)
+        Y[toks] += slot_gate[lo:hi, None] * o
+    return Y
+
+
 def rel_l2(a, b) -> float:
-    """||a - b||_2 / ||b||_2 (0 when both are zero)."""
+    """||a - b||_2 / ||b||_2 over all elements (0 when both are zero, inf
+    when only b is zero).  The relative-L2 error is the measure the output
+    tolerances are stated in; a and b must have the same shape (no
+    broadcasting)."""
     a = _f64(a)
     b = _f64(b)
+    if a.shape != b.shape:
+        raise ValueError(f"rel_l2: shapes differ {a.shape} vs {b.shape}")
     den = float(np.linalg.norm(b))
     num = float(np.linalg.norm(a - b))
     if den == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return num / den
+
+
+def rel_l2_rows(a, b) -> np.ndarray:
+    """``rel_l2`` of each row (last axis) of two equal-shape 2-D arrays:
+    ||a[i] - b[i]||_2 / ||b[i]||_2, 0 where both rows are zero and inf where
+    only b's row is zero."""
+    a = _f64(a)
+    b = _f64(b)
+    if a.shape != b.shape or a.ndim != 2:
+        raise ValueError(f"rel_l2_rows: equal 2-D shapes expected, got {a.shape} vs {b.shape}")
+    den = np.linalg.norm(b, axis=1)
+    num = np.linalg.norm(a - b, axis=1)
+    out = np.zeros(a.shape[0])
+    nz = den > 0.0
+    out[nz] = num[nz] / den[nz]
+    out[~nz & (num > 0.0)] = np.inf
+    return out

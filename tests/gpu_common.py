@@ -74,3 +74,53 @@ def check_permutation(res, ids, E, C):
     N = int(ref["offsets"][-1])
     assert np.array_equal(intnp(res["perm_token"])[:N], ref["perm_token"][:N].astype(np.int64))
     return ref
+
+
+TILE_ROWS = 256      # row tile of the tiled grouped GEMMs (rows of one expert segment)
+
+
+def check_outputs_streamed(inp, ref, gates, H, O, Y, tol, label=""):
+    """Every kept row of H and O and every row of Y against the oracle.
+
+    The oracle runs expert by expert (``forward_by_expert``), so that the
+    float64 H and O of only one expert exist at a time.  Each expert segment
+    of H and O must meet ``tol`` as a whole, per row tile of TILE_ROWS rows
+    (the grouped GEMM's tile, counted from the segment start) and row by
+    row; Y must meet it as a whole and row by row (a fully dropped token's
+    row is exactly zero on both sides).  Returns the worst values seen."""
+    X32 = f32np(inp["X"])
+    Wg, Wu, Wd = (f32np(inp[k]) for k in ("W_gate", "W_up", "W_down"))
+    Hc, Oc = H.detach().cpu(), O.detach().cpu()
+    worst = {"H": 0.0, "O": 0.0, "H_row": 0.0, "O_row": 0.0, "segments": 0, "tiles": 0}
+
+    def visit(e, lo, hi, h, o):
+        for name, want in (("H", h), ("O", o)):
+            got = Hc[lo:hi] if name == "H" else Oc[lo:hi]
+            got = got.to(torch.float64).numpy()
+            err = mo.rel_l2(got, want)
+            assert err <= tol, f"{label} {name} expert {e} rows [{lo},{hi}): rel-L2 {err:.3e}"
+            for r0 in range(0, hi - lo, TILE_ROWS):
+                r1 = min(hi - lo, r0 + TILE_ROWS)
+                et = mo.rel_l2(got[r0:r1], want[r0:r1])
+                assert et <= tol, f"{label} {name} expert {e} tile rows [{lo + r0},{lo + r1}): {et:.3e}"
+                worst["tiles"] += name == "H"
+            rows = mo.rel_l2_rows(got, want)
+            i = int(np.argmax(rows))
+            assert rows[i] <= tol, f"{label} {name} expert {e} slot {lo + i}: rel-L2 {rows[i]:.3e}"
+            worst[name] = max(worst[name], err)
+            worst[name + "_row"] = max(worst[name + "_row"], float(rows[i]))
+        worst["segments"] += 1
+
+    Y_ref = mo.forward_by_expert(X32, gates, ref["offsets"], ref["perm_token"], ref["inv_slot"],
+                                 Wg, Wu, Wd, visit=visit)
+    Y_gpu = Y.detach().cpu().to(torch.float64).numpy()
+    err = mo.rel_l2(Y_gpu, Y_ref)
+    assert err <= tol, f"{label} Y rel-L2 {err:.3e}"
+    rows = mo.rel_l2_rows(Y_gpu, Y_ref)
+    i = int(np.argmax(rows))
+    assert rows[i] <= tol, f"{label} Y token {i}: rel-L2 {rows[i]:.3e}"
+    dropped = np.all(np.asarray(ref["inv_slot"]) < 0, axis=1)
+    assert np.all(Y_gpu[dropped] == 0.0)
+    worst["Y"], worst["Y_row"] = err, float(rows[i])
+    assert worst["segments"] == int(np.count_nonzero(np.asarray(ref["counts"])))
+    return worst

@@ -5,7 +5,7 @@ The oracle takes its routing decision on the device's exported fp32
 log-softmax rows (adding them in float32 as the device does), so ids must
 match bit for bit; the rows themselves are checked against the float64
 definition, gates within 2e-6, the permutation bit for bit, Y within the bf16
-tolerance."""
+tolerance (every row at full size)."""
 
 import numpy as np
 import pytest
@@ -93,14 +93,21 @@ def test_repeat_runs_are_bitwise_identical():
     assert torch.equal(Y1, Y2)
 
 
-def test_workload_full_size_atomic_experts(n_sample=24):
+def test_workload_full_size_atomic_experts():
+    """The 65536-expert workload at full size: routing and the permutation
+    bit-exact, and every row of Y against the whole oracle forward (as a
+    whole and row by row)."""
     inp = mi.make_omni_inputs("omni_bf16")
     w = inp["workload"]
     print(f"atomic-expert workload: T={w.T} d={w.d} Nr={w.Nr} Nc={w.Nc} K={w.K}", flush=True)
     dev, ids, gates, ls_r, ls_c, meta, Y = _run(inp, w.K)
-    _, _, rid = _check_route_and_permutation(inp, w.K, ids, gates, ls_r, ls_c, meta)
-    rng = np.random.default_rng(0)
-    toks = np.sort(rng.choice(w.T, size=n_sample, replace=False))
-    y_ref = om.token_outputs(toks, f32np(inp["X"]), rid, f32np(gates), f32np(inp["W_in"]),
-                             f32np(inp["W_out"]))
-    assert mo.rel_l2(f32np(Y)[toks], y_ref) <= TOL["bf16"]
+    lr, lc, rid = _check_route_and_permutation(inp, w.K, ids, gates, ls_r, ls_c, meta)
+    a = {k: f32np(inp[k]) for k in ("X", "W_r", "W_c", "W_in", "W_out")}
+    ref = om.forward(a["X"], a["W_r"], a["W_c"], a["W_in"], a["W_out"], w.K, scores=(lr, lc))
+    assert np.array_equal(ref["ids"], rid)
+    Yg = f32np(Y)
+    assert mo.rel_l2(Yg, ref["Y"]) <= TOL["bf16"]
+    rows = mo.rel_l2_rows(Yg, ref["Y"])
+    assert float(rows.max()) <= TOL["bf16"], (int(np.argmax(rows)), float(rows.max()))
+    print(f"atomic-expert workload: Y rel-L2 {mo.rel_l2(Yg, ref['Y']):.3e}, worst row "
+          f"{float(rows.max()):.3e}", flush=True)

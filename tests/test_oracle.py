@@ -358,3 +358,116 @@ def test_planted_mistakes(monkeypatch):
         exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
         assert not _pins_pass(mod), "planted mistake not caught: " + name
     importlib.reload(mo)
+
+
+# ---------------------------------------------------------------- comparison measure
+
+def test_rel_l2_hand_values():
+    assert mo.rel_l2([1.0, 1.0], [1.0, 0.0]) == 1.0
+    assert mo.rel_l2([6.0, 8.0], [3.0, 4.0]) == 1.0            # |(3,4)| / |(3,4)|
+    assert mo.rel_l2([0.0, 0.0], [3.0, 4.0]) == 1.0
+    assert mo.rel_l2([1.0, 2.0, 2.0], [1.0, 0.0, 0.0]) == pytest.approx(math.sqrt(8.0), rel=1e-15)
+    assert mo.rel_l2([3.0, 4.5], [3.0, 4.0]) == pytest.approx(0.1, rel=1e-15)  # 0.5 / 5
+    b = np.array([[1.5, -2.0], [0.25, 7.0]])
+    assert mo.rel_l2(b, b) == 0.0
+    assert mo.rel_l2(np.zeros(3), np.zeros(3)) == 0.0
+    assert mo.rel_l2([0.0, 1e-30], [0.0, 0.0]) == float("inf")
+    # not symmetric: the reference is the second argument
+    assert mo.rel_l2([2.0], [1.0]) == 1.0 and mo.rel_l2([1.0], [2.0]) == 0.5
+
+
+def test_rel_l2_rejects_shape_mismatch():
+    with pytest.raises(ValueError):
+        mo.rel_l2(np.ones((2, 3)), np.ones(3))          # would broadcast silently
+    with pytest.raises(ValueError):
+        mo.rel_l2(np.ones((4, 1)), np.ones((1, 4)))
+    with pytest.raises(ValueError):
+        mo.rel_l2_rows(np.ones((2, 3)), np.ones((3, 2)))
+
+
+def test_rel_l2_rows_hand_values():
+    a = np.array([[1.0, 1.0], [6.0, 8.0], [0.0, 0.0], [0.0, 2.0], [3.0, 4.5]])
+    b = np.array([[1.0, 0.0], [3.0, 4.0], [0.0, 0.0], [0.0, 0.0], [3.0, 4.0]])
+    got = mo.rel_l2_rows(a, b)
+    assert got[:4].tolist() == [1.0, 1.0, 0.0, float("inf")]
+    assert got[4] == pytest.approx(0.1, rel=1e-15)
+    # whole-array value from the rows: squares of the numerators add up
+    c = np.array([[3.0, 4.0], [0.0, 5.0]])
+    d = np.array([[3.0, 0.0], [0.0, 5.0]])
+    assert mo.rel_l2(c, d) == pytest.approx(4.0 / math.sqrt(34.0), rel=1e-15)
+    assert mo.rel_l2_rows(c, d).tolist() == [4.0 / 3.0, 0.0]
+
+
+def test_rel_l2_planted_mistakes():
+    import types
+    src = open(mo.__file__).read()
+    mutants = {
+        "denominator from a": ("den = float(np.linalg.norm(b))", "den = float(np.linalg.norm(a))"),
+        "squared norms": ("num = float(np.linalg.norm(a - b))", "num = float(np.linalg.norm(a - b)) ** 2"),
+        "zero reference passes": ('return 0.0 if num == 0.0 else float("inf")', "return 0.0"),
+        "rows: no inf": ("out[~nz & (num > 0.0)] = np.inf", "pass"),
+        "rows: denominator from a": ("den = np.linalg.norm(b, axis=1)", "den = np.linalg.norm(a, axis=1)"),
+        "no shape check": ("if a.shape != b.shape:\n        raise", "if False:\n        raise"),
+    }
+
+    def pins(m):
+        try:
+            return (m.rel_l2([1.0, 1.0], [1.0, 0.0]) == 1.0
+                    and m.rel_l2([1.0], [2.0]) == 0.5
+                    and m.rel_l2([3.0, 4.5], [3.0, 4.0]) == pytest.approx(0.1, rel=1e-15)
+                    and m.rel_l2([0.0, 1e-30], [0.0, 0.0]) == float("inf")
+                    and m.rel_l2_rows(np.array([[0.0, 2.0], [1.0, 1.0]]),
+                                      np.array([[0.0, 0.0], [1.0, 0.0]])).tolist() == [float("inf"), 1.0]
+                    and m.rel_l2_rows(np.array([[2.0]]), np.array([[1.0]])).tolist() == [1.0]
+                    and _raises(lambda: m.rel_l2(np.ones((2, 3)), np.ones(3))))
+        except Exception:
+            return False
+
+    assert pins(mo)
+    for name, (old, new) in mutants.items():
+        assert old in src, name
+        mod = types.ModuleType("oracle_mutant")
+        exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+        assert not pins(mod), "planted mistake not caught: " + name
+
+
+def _raises(fn):
+    try:
+        fn()
+    except ValueError:
+        return True
+    return False
+
+
+@pytest.mark.parametrize("cf,bias", [(0.0, False), (0.6, True)])
+def test_forward_by_expert_matches_whole_forward(cf, bias):
+    X, W_r, Wg, Wu, Wd = _tiny(60, 8, 7, 6, 12, scale_r=2.0)
+    b = np.array([1.5 * math.log(1.0 / (e + 1)) for e in range(7)]) if bias else None
+    out = mo.forward(X, W_r, Wg, Wu, Wd, 3, capacity_factor=cf, bias=b)
+    seen = []
+
+    def visit(e, lo, hi, h, o):
+        seen.append(e)
+        np.testing.assert_allclose(h, out["H"][lo:hi], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(o, out["O"][lo:hi], rtol=1e-13, atol=1e-15)
+
+    Y = mo.forward_by_expert(X, out["gates"], out["offsets"], out["perm_token"], out["inv_slot"],
+                             Wg, Wu, Wd, visit=visit)
+    assert seen == [e for e in range(7) if out["counts"][e] > 0]
+    np.testing.assert_allclose(Y, out["Y"], rtol=1e-12, atol=1e-14)
+    # and against the brute force, which shares no step with either
+    C = mo.capacity(60, 3, 7, cf)
+    bf = brute.brute_forward(X, W_r, Wg, Wu, Wd, 3, C, bias=b)
+    np.testing.assert_allclose(Y, np.array(bf["Y"]), rtol=1e-9, atol=1e-11)
+    if cf:
+        assert np.any(out["inv_slot"] < 0)                # the cap dropped something
+
+
+def test_forward_by_expert_rejects_unordered_segments():
+    X, W_r, Wg, Wu, Wd = _tiny(6, 4, 2, 3, 13)
+    ids = np.array([[0], [0], [1], [0], [1], [1]])
+    meta = mo.permute(ids, 2, 6)
+    perm = meta["perm_token"].copy()
+    perm[[0, 1]] = perm[[1, 0]]
+    with pytest.raises(ValueError):
+        mo.forward_by_expert(X, np.ones((6, 1)), meta["offsets"], perm, meta["inv_slot"], Wg, Wu, Wd)

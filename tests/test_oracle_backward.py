@@ -169,3 +169,39 @@ def test_sampled_backward_matches_whole(cf, bias):
     for t in range(T):
         assert np.allclose(part["dX"][t], whole["dX"][t], rtol=1e-12, atol=1e-12)
         assert np.allclose(part["dl"][t], whole["dl"][t], rtol=1e-12, atol=1e-12)
+
+
+def _by_expert_as_whole(dY, fw, X, W_r, Wg, Wu, Wd):
+    """backward_by_expert with the visited weight gradients gathered back
+    into [E, ...] arrays (experts with no kept row stay zero)."""
+    E = Wg.shape[0]
+    out = {"dW_gate": np.zeros(Wg.shape), "dW_up": np.zeros(Wu.shape), "dW_down": np.zeros(Wd.shape)}
+    seen = []
+
+    def visit(e, dwg, dwu, dwd):
+        seen.append(e)
+        out["dW_gate"][e], out["dW_up"][e], out["dW_down"][e] = dwg, dwu, dwd
+
+    r = mb.backward_by_expert(dY, fw, X, W_r, Wg, Wu, Wd, visit=visit)
+    assert seen == [e for e in range(E) if fw["offsets"][e + 1] > fw["offsets"][e]]
+    out.update(r)
+    return out
+
+
+@pytest.mark.parametrize("cf,bias", [(0.0, False), (0.5, True)])
+def test_backward_by_expert_matches_whole(cf, bias):
+    T, d, E, K, n = 17, 8, 6, 3, 5
+    X, W_r, Wg, Wu, Wd, dY, b = _layer(T, d, E, K, n, 21, bias)
+    fw = mb.forward_train(X, W_r, Wg, Wu, Wd, K, cf, bias=b)
+    whole = mb.backward(dY, fw, X, W_r, Wg, Wu, Wd)
+    rec = mb.route_record(X, W_r, K, cf, bias=b)
+    part = _by_expert_as_whole(dY, rec, X, W_r, Wg, Wu, Wd)
+    for name in ("dX", "dW_r", "dW_gate", "dW_up", "dW_down", "dl", "dS"):
+        assert np.allclose(part[name], whole[name], rtol=1e-12, atol=1e-12), name
+
+
+@pytest.mark.parametrize("T,d,E,K,n,cf,bias,seed", CASES[1:2])
+def test_backward_by_expert_matches_central_differences(T, d, E, K, n, cf, bias, seed):
+    worst, skipped = _fd_check(T, d, E, K, n, cf, bias, seed, bwd=_by_expert_as_whole)
+    assert skipped == 0
+    assert worst < 1e-5
