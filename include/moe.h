@@ -190,6 +190,30 @@ moe_status moe_permute(const moe_desc* desc, const int32_t* topk_ids, int32_t* c
                        int32_t* offsets, int32_t* raw_counts, int32_t* perm_token,
                        int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream);
 
+/* Allocation-free moe_permute, for callers that cannot allocate device memory
+ * or hand in a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and outputs as moe_permute
+ * (bit for bit) without ws/ws_bytes: its scratch (the per-block histogram and
+ * block bases, and the raw counts when raw_counts is NULL) lives in a static
+ * device array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one copy per
+ * GPU, held until the process ends.
+ *   Limit: moe_workspace_size(desc, MOE_WS_PERMUTE) must not exceed
+ *   MOE_NOALLOC_SCRATCH_BYTES (for example T <= 131072 at E = 256, T <= 262144
+ *   at E = 128); a larger problem gets MOE_ERR_WORKSPACE and nothing is
+ *   enqueued.
+ *   The call never calls hipMalloc/hipFree or any allocating routine; the
+ *   first call on a device looks the array's address up once
+ *   (hipGetSymbolAddress on the current device; `stream` must belong to it).
+ *   Every call on one GPU shares that one array and leaves its contents
+ *   behind: calls that overlap in time on the same GPU (other streams, other
+ *   threads) race on it and must be serialised by the caller.  Nothing in the
+ *   array has to start at zero (every scratch entry is written before it is
+ *   read in each call). */
+#define MOE_NOALLOC_SCRATCH_BYTES (2u << 20)
+moe_status moe_permute_noalloc(const moe_desc* desc, const int32_t* topk_ids, int32_t* counts,
+                               int32_t* offsets, int32_t* raw_counts, int32_t* perm_token,
+                               int32_t* inv_slot, void* stream);
+
 /* Step 6: H[s,:] = silu(X[perm_token[s]] W_gate[e]) * (X[perm_token[s]] W_up[e])
  * for every slot s of expert e (rows gathered from X inside the GEMM; no
  * gathered copy of X is made).  offsets/perm_token as moe_permute writes them.

@@ -23,7 +23,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 23
+    assert len(names) == 24
     lib = moe.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -269,3 +269,32 @@ def test_atomic_expert_descriptor_checks():
         moe.MOE_ERR_INVALID_ARG
     zero = moe.make_omni_desc(0, 1024, 4, 4, 2)
     assert lib.moe_omni_forward(ctypes.byref(zero), A, A, A, A, A, A, A, 0, None) == moe.MOE_OK
+
+
+def test_allocation_free_permutation_rejects_problems_beyond_its_scratch():
+    """moe_permute_noalloc keeps its scratch in a static device array of
+    MOE_NOALLOC_SCRATCH_BYTES: a problem whose permutation needs more gets
+    MOE_ERR_WORKSPACE before anything is enqueued (so no GPU is needed)."""
+    lib = moe.lib()
+    A = ctypes.c_void_p(1 << 20)          # aligned fake pointers: never dereferenced
+    fits = moe.make_desc(131072, 128, 256, 8, 128)
+    assert moe.moe_workspace_size(fits, moe.MOE_WS_PERMUTE) <= moe.MOE_NOALLOC_SCRATCH_BYTES
+    big = moe.make_desc(262144, 128, 256, 8, 128)
+    assert moe.moe_workspace_size(big, moe.MOE_WS_PERMUTE) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_permute_noalloc(ctypes.byref(big), A, A, A, None, A, A, None) == \
+        moe.MOE_ERR_WORKSPACE
+    assert b"MOE_NOALLOC_SCRATCH_BYTES" in lib.moe_last_error()
+    also_big = moe.make_desc(262144 * 2, 128, 128, 2, 128)
+    assert lib.moe_permute_noalloc(ctypes.byref(also_big), A, A, A, None, A, A, None) == \
+        moe.MOE_ERR_WORKSPACE
+    # argument errors come first, as for moe_permute
+    small = moe.make_desc(64, 128, 8, 2, 128)
+    assert lib.moe_permute_noalloc(ctypes.byref(small), None, A, A, None, A, A, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    U = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.moe_permute_noalloc(ctypes.byref(small), A, A, A, U, A, A, None) == \
+        moe.MOE_ERR_ALIGNMENT
+    # T = 0 is a no-op
+    zero = moe.make_desc(0, 128, 8, 2, 128)
+    assert lib.moe_permute_noalloc(ctypes.byref(zero), None, None, None, None, None, None, None) == \
+        moe.MOE_OK

@@ -5,7 +5,7 @@ Argument marshalling only.  Every step of the layer runs in the HIP kernels of
 library has not been built, every call raises (there is no fallback path).
 
 Low-level functions carry the C names (``moe_route``, ``moe_permute``,
-``moe_grouped_gemm_up``, ``moe_grouped_gemm_down``, ``moe_grouped_ffn``,
+``moe_permute_noalloc``, ``moe_grouped_gemm_up``, ``moe_grouped_gemm_down``, ``moe_grouped_ffn``,
 ``moe_round_tokens``, ``moe_combine``, ``moe_forward``, ``moe_forward_train``,
 ``moe_backward`` and the host-only queries) and take torch tensors.
 ``route``, ``permute``, ``round_tokens``, ``grouped_ffn``, ``combine``,
@@ -40,6 +40,7 @@ MOE_FLAG_TILE_TABLE_READY = 1
 MOE_FLAG_GEMM_TILED = 2
 MOE_FLAG_GEMM_SKINNY = 4
 MOE_FLAG_TOKEN_ROUNDING = 8
+MOE_NOALLOC_SCRATCH_BYTES = 2 << 20
 
 
 class MoeError(RuntimeError):
@@ -118,6 +119,7 @@ _SIGNATURES = {
     "moe_forward": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "moe_saved_layout_of": [_DP, ctypes.POINTER(MoeSavedLayout)],
     "moe_round_tokens": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "moe_permute_noalloc": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "moe_omni_validate": [ctypes.c_void_p],
     "moe_omni_workspace_size": [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
     "moe_omni_route": [ctypes.c_void_p, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
@@ -225,6 +227,12 @@ def moe_permute(desc, ids, counts, offsets, raw_counts, perm_token, inv_slot, ws
     _check(lib().moe_permute(ctypes.byref(desc), _p(ids), _p(counts), _p(offsets), _p(raw_counts),
                              _p(perm_token), _p(inv_slot), _p(ws), ws.numel() * ws.element_size(),
                              _stream(stream)), "moe_permute")
+
+
+def moe_permute_noalloc(desc, ids, counts, offsets, raw_counts, perm_token, inv_slot, stream=None):
+    _check(lib().moe_permute_noalloc(ctypes.byref(desc), _p(ids), _p(counts), _p(offsets),
+                                     _p(raw_counts), _p(perm_token), _p(inv_slot),
+                                     _stream(stream)), "moe_permute_noalloc")
 
 
 def moe_round_tokens(desc, ids, gates, counts, offsets, perm_token, inv_slot, ws, stream=None):

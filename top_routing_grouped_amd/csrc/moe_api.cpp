@@ -489,6 +489,29 @@ moe_status moe_permute(const moe_desc* desc, const int32_t* topk_ids, int32_t* c
                      static_cast<unsigned char*>(ws), nullptr, (hipStream_t)stream);
 }
 
+static_assert(moe::kNoallocScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "scratch size in moe.h");
+
+moe_status moe_permute_noalloc(const moe_desc* desc, const int32_t* topk_ids, int32_t* counts,
+                               int32_t* offsets, int32_t* raw_counts, int32_t* perm_token,
+                               int32_t* inv_slot, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc));
+  if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
+  MOE_TRY(check_ptrs({{topk_ids, "topk_ids"}, {counts, "counts"}, {offsets, "offsets"},
+                      {perm_token, "perm_token"}, {inv_slot, "inv_slot"}},
+                     {{raw_counts, "raw_counts"}}));
+  const moe::Problem p = make_problem(desc);
+  if (permute_ws_bytes(p) > moe::kNoallocScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_permute_noalloc: the permutation needs " + std::to_string(permute_ws_bytes(p)) +
+                    " bytes of scratch, above the static MOE_NOALLOC_SCRATCH_BYTES (" +
+                    std::to_string(moe::kNoallocScratchBytes) + "); use moe_permute with a workspace");
+  void* scratch = nullptr;
+  MOE_TRY(hip_status(moe::noalloc_scratch(&scratch), "static scratch address"));
+  return run_permute(p, topk_ids, counts, offsets, raw_counts, perm_token, inv_slot,
+                     static_cast<unsigned char*>(scratch), nullptr, (hipStream_t)stream);
+}
+
 moe_status moe_round_tokens(const moe_desc* desc, const int32_t* topk_ids, const float* topk_gates,
                             int32_t* counts, int32_t* offsets, int32_t* perm_token,
                             int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream) {

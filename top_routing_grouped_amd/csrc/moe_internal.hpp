@@ -97,6 +97,12 @@ hipError_t launch_permute_one_block(const Problem& p, const int32_t* ids, int32_
                                    int32_t* counts, int32_t* offsets, int32_t* table,
                                    int32_t* perm, int32_t* inv, hipStream_t s);
 
+// Static device scratch of the allocation-free permutation entry point
+// (permute.hip): its address on the current device, looked up once per
+// device with hipGetSymbolAddress and kept.
+constexpr size_t kNoallocScratchBytes = (size_t)2 << 20;
+hipError_t noalloc_scratch(void** out);
+
 // Hpre (bf16 only, may be NULL): also store the pre-activations [rows][2n]
 // (x W_gate | x W_up) for the backward.
 hipError_t launch_gemm_up(const Problem& p, const void* X, const int32_t* perm,

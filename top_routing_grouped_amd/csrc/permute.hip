@@ -22,7 +22,38 @@
 // and one launch (decode batches: 18 -> 10 us at T = 64).
 #include "moe_internal.hpp"
 
+#include <mutex>
+
+// Scratch of the allocation-free entry point (moe_permute_noalloc): the
+// per-block histogram, block bases and raw counts that moe_permute keeps in
+// the caller's workspace.  Each GPU the library runs on holds its own copy
+// at its own address until the process ends.  In host code this name is
+// only a stand-in for the symbol; the device address comes from
+// noalloc_scratch() below and is the only form ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[moe::kNoallocScratchBytes];
+
 namespace moe {
+
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kB = kPermuteBlock;        // tokens per block (== threads)
