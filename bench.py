@@ -9,7 +9,10 @@ scratch buffer is rewritten so that neither L2 nor the 256 MB MALL holds the
 inputs (cold cache); each step is bracketed by HIP events on the stream the
 kernels run on, and `value` = T / median step time.  Each step is followed
 by the same work through the step-wise entry points with events between the
-stages (per-stage medians, same kernels); then the up GEMM alone is timed
+stages (moe_route_permute, up GEMM, down GEMM, combine: the kernels
+moe_forward runs; per-stage medians), and by the router alone plus the
+standalone permutation (moe_route_ws, moe_permute), each after its own cache
+flush; then the up GEMM alone is timed
 for the roofline, and everything is repeated without the flush (warm,
 labelled as such).  For bf16 workloads the training step (moe_forward_train
 then moe_backward on a seeded dY) is timed the same way and reported under
@@ -249,6 +252,7 @@ def main():
     O = torch.empty((rows, d), dtype=dev["X"].dtype, device="cuda")
     Y = torch.empty((T, d), dtype=dev["X"].dtype, device="cuda")
     ws_r = moe.workspace(desc, moe.MOE_WS_ROUTE)
+    ws_rp = moe.workspace(desc, moe.MOE_WS_ROUTE_PERMUTE)
     ws_p = moe.workspace(desc, moe.MOE_WS_PERMUTE)
     ws_f = moe.workspace(desc, moe.MOE_WS_GROUPED_FFN)
     ws_fwd = moe.workspace(desc, moe.MOE_WS_FORWARD)
@@ -260,17 +264,26 @@ def main():
                         dev["W_down"], Y, ws_fwd)
 
     def stepwise(ev):
+        # the stages moe_forward runs: route + fused permutation, up, down, combine
+        ev[0].record(stream)
+        moe.moe_route_permute(desc, dev["X"], dev["W_r"], dev["bias"], None, ids, gates, counts,
+                              offsets, None, perm, inv, ws_rp)
+        ev[1].record(stream)
+        moe.moe_grouped_gemm_up(desc, dev["X"], offsets, perm, dev["W_gate"], dev["W_up"], H, ws_f)
+        ev[2].record(stream)
+        moe.moe_grouped_gemm_down(desc_ready, H, offsets, dev["W_down"], O, ws_f)
+        ev[3].record(stream)
+        moe.moe_combine(desc, O, gates, inv, Y)
+        ev[4].record(stream)
+
+    def route_parts(ev):
+        # the router alone (moe_route_ws) and the standalone three-launch
+        # permutation from its ids (moe_permute)
         ev[0].record(stream)
         moe.moe_route_ws(desc, dev["X"], dev["W_r"], dev["bias"], None, ids, gates, ws_r)
         ev[1].record(stream)
         moe.moe_permute(desc, ids, counts, offsets, None, perm, inv, ws_p)
         ev[2].record(stream)
-        moe.moe_grouped_gemm_up(desc, dev["X"], offsets, perm, dev["W_gate"], dev["W_up"], H, ws_f)
-        ev[3].record(stream)
-        moe.moe_grouped_gemm_down(desc_ready, H, offsets, dev["W_down"], O, ws_f)
-        ev[4].record(stream)
-        moe.moe_combine(desc, O, gates, inv, Y)
-        ev[5].record(stream)
 
     def flush(i):
         scratch.fill_(float(i))
@@ -279,7 +292,8 @@ def main():
         return torch.cuda.Event(enable_timing=True)
 
     for i in range(args.warmup):
-        stepwise([ev() for _ in range(6)])
+        stepwise([ev() for _ in range(5)])
+        route_parts([ev() for _ in range(3)])
         fused()
     torch.cuda.synchronize()
     N = int(offsets[E].item())            # kept (token, expert) rows: fixed by the inputs
@@ -290,20 +304,25 @@ def main():
         step-wise entry points (interleaved, so both see the same clocks and
         temperatures); with `cold`, the cache flush precedes each of them."""
         fev = [(ev(), ev()) for _ in range(args.steps)]
-        sev = [[ev() for _ in range(6)] for _ in range(args.steps)]
+        sev = [[ev() for _ in range(5)] for _ in range(args.steps)]
+        rev = [[ev() for _ in range(3)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
             if cold:
-                flush(2 * i)
+                flush(3 * i)
             fev[i][0].record(stream)
             fused()
             fev[i][1].record(stream)
             if cold:
-                flush(2 * i + 1)
+                flush(3 * i + 1)
             stepwise(sev[i])
+            if cold:
+                flush(3 * i + 2)
+            route_parts(rev[i])
         torch.cuda.synchronize()
         return ([a.elapsed_time(b) for a, b in fev],
-                [[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in sev])
+                [[e[j].elapsed_time(e[j + 1]) for j in range(4)] +
+                 [r[0].elapsed_time(r[1]), r[1].elapsed_time(r[2])] for e, r in zip(sev, rev)])
 
     def run_up_kernel(cold: bool):
         """The up-projection GEMM alone (its tile table already built by the
@@ -423,12 +442,12 @@ def main():
     omni = None if args.forward_only else run_omni(cold)
 
     med = statistics.median(fused_ms)
-    names = ["route", "permute", "gemm_up", "gemm_down", "combine"]
+    names = ["route_permute", "gemm_up", "gemm_down", "combine", "route", "permute"]
     stage_med = {nm: statistics.median(x[j] for x in stage_ms) for j, nm in enumerate(names)}
     warm_stage_med = {nm: statistics.median(x[j] for x in warm_stage_ms) for j, nm in enumerate(names)}
 
     # ---- algorithmic work (no padding, no pre-gather, active experts only)
-    t_route, t_perm, t_up, t_down, t_comb = (stage_med[k] * 1e-3 for k in names)
+    t_rp, t_up, t_down, t_comb, t_route, t_perm = (stage_med[k] * 1e-3 for k in names)
     route_bytes = T * d * s + d * E * s + T * K * 8
     perm_bytes = T * K * 4 + N * 4 + T * K * 4 + 2 * E * 4
     comb_bytes = N * d * s + T * K * 8 + T * d * s
@@ -486,15 +505,16 @@ def main():
                  "stage_us": {k: v * 1e3 for k, v in warm_stage_med.items()}},
         "wall_s_timed_region": wall,
         "stage_us": {k: v * 1e3 for k, v in stage_med.items()},
-        "stepwise_ms_per_step": sum(stage_med.values()),
+        "stepwise_ms_per_step": sum(stage_med[k] for k in names[:4]),
         "grouped_gemm_mfma_util": mfma_util,
         "gemm_up_tflops": up_tflops,
         "gemm_down_tflops": down_flops / t_down / 1e12,
         "route_GBps": route_bytes / t_route / 1e9,
         "permute_GBps": perm_bytes / t_perm / 1e9,
-        "route_permute_GBps": (route_bytes + perm_bytes) / (t_route + t_perm) / 1e9,
+        "route_permute_GBps": (route_bytes + perm_bytes) / t_rp / 1e9,
         "combine_GBps": comb_bytes / t_comb / 1e9,
         "hbm_frac": {"route": route_bytes / t_route / 1e9 / PEAK_HBM_GBPS,
+                     "route_permute": (route_bytes + perm_bytes) / t_rp / 1e9 / PEAK_HBM_GBPS,
                      "combine": comb_bytes / t_comb / 1e9 / PEAK_HBM_GBPS},
         "roofline": roofline,
         "gemm_path": "weight-streaming" if skinny else "tiled",

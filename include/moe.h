@@ -109,7 +109,8 @@ enum {
   MOE_WS_ROUTE = 3,
   MOE_WS_SAVED = 4,
   MOE_WS_BACKWARD = 5,
-  MOE_WS_ROUND = 6
+  MOE_WS_ROUND = 6,
+  MOE_WS_ROUTE_PERMUTE = 7
 };
 
 /* Byte offsets of the fields of the saved state (the `saved` buffer of
@@ -189,6 +190,20 @@ moe_status moe_route_ws(const moe_desc* desc, const void* X, const void* W_r, co
 moe_status moe_permute(const moe_desc* desc, const int32_t* topk_ids, int32_t* counts,
                        int32_t* offsets, int32_t* raw_counts, int32_t* perm_token,
                        int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream);
+
+/* Steps 1-5 in two launches ("算子与编译器：MoE 路由与稀疏 Kernel" §3: the
+ * counting and prefix sums of the permutation; SonicMoE article §11: the
+ * metadata triple): the router of moe_route_ws, whose selection also counts
+ * each token block's choices per expert, then one permutation launch that
+ * sums the counts of the blocks before each 256-token workgroup and ranks
+ * that workgroup's tokens.  Outputs are exactly those of moe_route_ws
+ * followed by moe_permute (same arguments; logits and raw_counts may be
+ * NULL).  ws: MOE_WS_ROUTE_PERMUTE bytes.  moe_forward runs this path. */
+moe_status moe_route_permute(const moe_desc* desc, const void* X, const void* W_r,
+                             const float* bias, float* logits, int32_t* topk_ids,
+                             float* topk_gates, int32_t* counts, int32_t* offsets,
+                             int32_t* raw_counts, int32_t* perm_token, int32_t* inv_slot,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* Allocation-free moe_permute, for callers that cannot allocate device memory
  * or hand in a workspace: code under HIP graph capture, tight serving loops,

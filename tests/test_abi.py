@@ -23,7 +23,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 24
+    assert len(names) == 25
     lib = moe.lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -298,3 +298,23 @@ def test_allocation_free_permutation_rejects_problems_beyond_its_scratch():
     zero = moe.make_desc(0, 128, 8, 2, 128)
     assert lib.moe_permute_noalloc(ctypes.byref(zero), None, None, None, None, None, None, None) == \
         moe.MOE_OK
+
+
+def test_route_permute_workspace_and_argument_checks():
+    lib = moe.lib()
+    A = ctypes.c_void_p(1 << 20)
+    for T, E in ((64, 8), (16384, 128), (3000, 128), (32768, 256)):
+        desc = moe.make_desc(T, 256, E, 4, 128)
+        need = moe.moe_workspace_size(desc, moe.MOE_WS_ROUTE_PERMUTE)
+        assert need >= moe.moe_workspace_size(desc, moe.MOE_WS_ROUTE)
+        assert need % 256 == 0
+    desc = moe.make_desc(64, 128, 8, 2, 128)
+    p = ctypes.byref(desc)
+    # missing workspace, then a null required pointer, then T = 0 as a no-op
+    assert lib.moe_route_permute(p, A, A, None, None, A, A, A, A, None, A, A, A, 16, None) == \
+        moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route_permute(p, A, A, None, None, None, A, A, A, None, A, A, A, 1 << 20, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    zero = moe.make_desc(0, 128, 8, 2, 128)
+    assert lib.moe_route_permute(ctypes.byref(zero), None, None, None, None, None, None, None, None,
+                                 None, None, None, None, 0, None) == moe.MOE_OK

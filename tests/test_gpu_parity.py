@@ -102,6 +102,45 @@ def test_route_with_and_without_k_split(T, d, E, K):
         check_routing({"ids": ids, "gates": gates, "logits": logits}, inp, K)
 
 
+ROUTE_PERMUTE = [
+    # T, d, E, K, dtype, cf, bias
+    (3000, 512, 128, 6, "bf16", 0.0, None),      # split-k router: 16-token count blocks, 3 workgroups
+    (1500, 256, 256, 8, "bf16", 1.0, "zipf"),    # E = 256, capacity drops, 2 workgroups
+    (1024, 128, 8, 2, "bf16", 0.0, None),        # exactly one workgroup
+    (1025, 128, 8, 2, "bf16", 0.0, None),        # a second workgroup with one token
+    (5000, 256, 5, 3, "bf16", 0.5, "zipf"),      # E % 8 != 0 (register-staged router), drops
+    (9000, 256, 64, 4, "bf16", 1.25, "zipf"),    # 64-token count blocks (no k split), 9 workgroups
+    (200, 64, 40, 20, "bf16", 0.0, None),        # K above 16
+    (2100, 128, 8, 2, "fp32", 0.7, None),        # fp32 router
+]
+
+
+@pytest.mark.parametrize("T,d,E,K,dtype,cf,bias", ROUTE_PERMUTE)
+def test_route_permute_equals_route_then_permute(T, d, E, K, dtype, cf, bias):
+    """moe_route_permute (router counting per block + one fused permutation
+    launch) gives exactly the outputs of moe_route_ws then moe_permute, and
+    the permutation is the oracle's on the device's logits."""
+    print(f"route_permute T={T} d={d} E={E} K={K} {dtype} cf={cf} bias={bias}", flush=True)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    inp = mi.draw(T, d, E, 64, tdt, seed=41, bias=bias)
+    dev = device_inputs(inp)
+    desc = moe.make_desc(T, d, E, K, 64, dtype, cf)
+    fused = moe.route_permute(dev["X"], dev["W_r"], K, desc, bias=dev["bias"], want_logits=True)
+    ids, gates, logits = moe.route(dev["X"], dev["W_r"], K, bias=dev["bias"], want_logits=True, n=64)
+    meta = moe.permute(desc, ids)
+    torch.cuda.synchronize()
+    assert torch.equal(fused["logits"], logits)
+    assert torch.equal(fused["ids"], ids) and torch.equal(fused["gates"], gates)
+    for key in ("counts", "offsets", "raw_counts", "inv_slot"):
+        assert torch.equal(fused[key], meta[key]), key
+    N = int(meta["offsets"][E].item())
+    assert torch.equal(fused["perm_token"][:N], meta["perm_token"][:N])
+    res = {"ids": ids, "gates": gates, "logits": logits}
+    res.update(fused)
+    _, ids_ref, _ = check_routing(res, inp, K)
+    check_permutation(res, ids_ref, E, mo.capacity(T, K, E, cf))
+
+
 def test_gemm_paths_agree_on_skewed_decode():
     """Decode-sized batch with one expert taking most rows (several 64-row
     passes in the weight-streaming kernel): both kernels against the oracle
@@ -262,6 +301,12 @@ def _full_size_check(name):
     L_gpu, ids, gates = check_routing(res, inp, w.K)
     C = mo.capacity(w.T, w.K, w.E, w.capacity_factor)
     ref = check_permutation(res, ids, w.E, C)
+    fused = moe.route_permute(dev["X"], dev["W_r"], w.K, res["desc"], bias=dev["bias"])
+    torch.cuda.synchronize()
+    for key in ("ids", "gates", "counts", "offsets", "raw_counts", "inv_slot"):
+        assert torch.equal(fused[key], res[key]), key
+    N = int(ref["offsets"][-1])
+    assert torch.equal(fused["perm_token"][:N], res["perm_token"][:N])
     worst = check_outputs_streamed(inp, ref, gates, res["H"], res["O"], res["Y"], TOL[w.dtype],
                                    label=name)
     print(f"workload {name}: {worst}", flush=True)

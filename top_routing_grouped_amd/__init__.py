@@ -5,7 +5,7 @@ Argument marshalling only.  Every step of the layer runs in the HIP kernels of
 library has not been built, every call raises (there is no fallback path).
 
 Low-level functions carry the C names (``moe_route``, ``moe_permute``,
-``moe_permute_noalloc``, ``moe_grouped_gemm_up``, ``moe_grouped_gemm_down``, ``moe_grouped_ffn``,
+``moe_permute_noalloc``, ``moe_route_permute``, ``moe_grouped_gemm_up``, ``moe_grouped_gemm_down``, ``moe_grouped_ffn``,
 ``moe_round_tokens``, ``moe_combine``, ``moe_forward``, ``moe_forward_train``,
 ``moe_backward`` and the host-only queries) and take torch tensors.
 ``route``, ``permute``, ``round_tokens``, ``grouped_ffn``, ``combine``,
@@ -36,6 +36,7 @@ MOE_WS_ROUTE = 3
 MOE_WS_SAVED = 4
 MOE_WS_BACKWARD = 5
 MOE_WS_ROUND = 6
+MOE_WS_ROUTE_PERMUTE = 7
 MOE_FLAG_TILE_TABLE_READY = 1
 MOE_FLAG_GEMM_TILED = 2
 MOE_FLAG_GEMM_SKINNY = 4
@@ -120,6 +121,8 @@ _SIGNATURES = {
     "moe_saved_layout_of": [_DP, ctypes.POINTER(MoeSavedLayout)],
     "moe_round_tokens": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "moe_permute_noalloc": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "moe_route_permute": [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                          ctypes.c_size_t, _VP],
     "moe_omni_validate": [ctypes.c_void_p],
     "moe_omni_workspace_size": [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
     "moe_omni_route": [ctypes.c_void_p, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
@@ -229,6 +232,14 @@ def moe_permute(desc, ids, counts, offsets, raw_counts, perm_token, inv_slot, ws
                              _stream(stream)), "moe_permute")
 
 
+def moe_route_permute(desc, X, W_r, bias, logits, ids, gates, counts, offsets, raw_counts,
+                      perm_token, inv_slot, ws, stream=None):
+    _check(lib().moe_route_permute(ctypes.byref(desc), _p(X), _p(W_r), _p(bias), _p(logits),
+                                   _p(ids), _p(gates), _p(counts), _p(offsets), _p(raw_counts),
+                                   _p(perm_token), _p(inv_slot), _p(ws), _nbytes(ws),
+                                   _stream(stream)), "moe_route_permute")
+
+
 def moe_permute_noalloc(desc, ids, counts, offsets, raw_counts, perm_token, inv_slot, stream=None):
     _check(lib().moe_permute_noalloc(ctypes.byref(desc), _p(ids), _p(counts), _p(offsets),
                                      _p(raw_counts), _p(perm_token), _p(inv_slot),
@@ -322,6 +333,28 @@ def route(X, W_r, K, bias=None, want_logits=False, n=64, split=True):
     else:
         moe_route(desc, X, W_r, bias, logits, ids, gates)
     return ids, gates, logits
+
+
+def route_permute(X, W_r, K, desc: MoeDesc, bias=None, want_logits=False):
+    """Steps 1-5 through moe_route_permute.  Returns dict(ids, gates, logits or
+    None, counts, offsets, raw_counts, perm_token, inv_slot)."""
+    import torch
+    dev = X.device
+    T, E = desc.T, desc.E
+    out = {
+        "ids": torch.empty((T, K), dtype=torch.int32, device=dev),
+        "gates": torch.empty((T, K), dtype=torch.float32, device=dev),
+        "logits": torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None,
+        "counts": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "raw_counts": torch.empty(E, dtype=torch.int32, device=dev),
+        "perm_token": torch.full((max(1, T * K),), -1, dtype=torch.int32, device=dev),
+        "inv_slot": torch.empty((T, K), dtype=torch.int32, device=dev),
+    }
+    moe_route_permute(desc, X, W_r, bias, out["logits"], out["ids"], out["gates"], out["counts"],
+                      out["offsets"], out["raw_counts"], out["perm_token"], out["inv_slot"],
+                      workspace(desc, MOE_WS_ROUTE_PERMUTE, dev))
+    return out
 
 
 def permute(desc: MoeDesc, ids):

@@ -101,6 +101,30 @@ PermuteWs carve_permute(const moe::Problem& p, unsigned char* base) {
           reinterpret_cast<int32_t*>(base + 2 * nbe)};
 }
 
+// Workspace of moe_route_permute: split-k partial scores (or none), the
+// per-block expert counts, raw counts.
+struct RoutePermuteWs {
+  float* route_partial;
+  int32_t* blockcnt;
+  int32_t* raw;
+  size_t bytes;
+};
+RoutePermuteWs carve_route_permute(const moe::Problem& p, unsigned char* base) {
+  RoutePermuteWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    unsigned char* ptr = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return ptr;
+  };
+  const size_t rp = moe::route_partial_bytes(p);
+  w.route_partial = rp ? reinterpret_cast<float*>(take(rp)) : nullptr;
+  w.blockcnt = reinterpret_cast<int32_t*>(take(moe::route_count_bytes(p, true)));
+  w.raw = reinterpret_cast<int32_t*>(take((size_t)p.E * 4));
+  w.bytes = off;
+  return w;
+}
+
 struct ForwardWs {
   float* route_partial;
   int32_t* ids;
@@ -109,7 +133,8 @@ struct ForwardWs {
   int32_t* perm;
   int32_t* counts;
   int32_t* offsets;
-  unsigned char* permute;
+  int32_t* raw;
+  int32_t* blockcnt;
   int32_t* table;
   void* H;
   void* O;
@@ -133,7 +158,8 @@ ForwardWs carve_forward(const moe::Problem& p, unsigned char* base) {
   w.perm = reinterpret_cast<int32_t*>(take(tk * 4));
   w.counts = reinterpret_cast<int32_t*>(take((size_t)p.E * 4));
   w.offsets = reinterpret_cast<int32_t*>(take((size_t)(p.E + 1) * 4));
-  w.permute = take(permute_ws_bytes(p));
+  w.raw = reinterpret_cast<int32_t*>(take((size_t)p.E * 4));
+  w.blockcnt = reinterpret_cast<int32_t*>(take(moe::route_count_bytes(p, true)));
   w.table = reinterpret_cast<int32_t*>(take(moe::tile_table_bytes(p)));
   w.H = take((size_t)p.rows_max * p.n * elem(p));
   w.O = take((size_t)p.rows_max * p.d * elem(p));
@@ -221,6 +247,22 @@ moe_status run_permute(const moe::Problem& p, const int32_t* ids, int32_t* count
                      "scan launch"));
   return hip_status(moe::launch_scatter(p, ids, w.blockbase, offsets, perm, inv, s),
                     "scatter launch");
+}
+
+// Steps 1-5 of moe_forward / moe_forward_train: the router, which also
+// writes per-block expert counts, then the fused permutation (one launch).
+moe_status run_route_permute(const moe::Problem& p, const void* X, const void* W_r,
+                             const float* bias, float* logits, int32_t* ids, float* gates,
+                             float* partial, int32_t* blockcnt, int32_t* counts, int32_t* offsets,
+                             int32_t* raw, int32_t* perm, int32_t* inv, int32_t* table,
+                             hipStream_t s) {
+  const bool split = partial != nullptr;
+  MOE_TRY(hip_status(moe::launch_route(p, X, W_r, bias, logits, ids, gates, partial, s, blockcnt),
+                     "route launch"));
+  return hip_status(moe::launch_permute_fused(p, ids, blockcnt, moe::route_count_block(p, split),
+                                              moe::route_count_ld(p, split), raw, counts, offsets,
+                                              table, perm, inv, s),
+                    "permutation launch");
 }
 
 moe_status check_omni(const moe_omni_desc* d) {
@@ -416,6 +458,9 @@ moe_status moe_workspace_size(const moe_desc* desc, int32_t entry, size_t* bytes
     case MOE_WS_ROUND:
       *bytes = moe::round_ws_bytes(p, nullptr, nullptr);
       return MOE_OK;
+    case MOE_WS_ROUTE_PERMUTE:
+      *bytes = carve_route_permute(p, nullptr).bytes;
+      return MOE_OK;
     default:
       return fail(MOE_ERR_INVALID_ARG, "unknown workspace selector");
   }
@@ -487,6 +532,27 @@ moe_status moe_permute(const moe_desc* desc, const int32_t* topk_ids, int32_t* c
     return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_PERMUTE)");
   return run_permute(p, topk_ids, counts, offsets, raw_counts, perm_token, inv_slot,
                      static_cast<unsigned char*>(ws), nullptr, (hipStream_t)stream);
+}
+
+moe_status moe_route_permute(const moe_desc* desc, const void* X, const void* W_r,
+                             const float* bias, float* logits, int32_t* topk_ids,
+                             float* topk_gates, int32_t* counts, int32_t* offsets,
+                             int32_t* raw_counts, int32_t* perm_token, int32_t* inv_slot,
+                             void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_TRY(check_desc(desc));
+  if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
+  MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {topk_ids, "topk_ids"}, {topk_gates, "topk_gates"},
+                      {counts, "counts"}, {offsets, "offsets"}, {perm_token, "perm_token"},
+                      {inv_slot, "inv_slot"}, {ws, "ws"}},
+                     {{bias, "bias"}, {logits, "logits"}, {raw_counts, "raw_counts"}}));
+  const moe::Problem p = make_problem(desc);
+  if (ws_bytes < carve_route_permute(p, nullptr).bytes)
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_ROUTE_PERMUTE)");
+  const RoutePermuteWs w = carve_route_permute(p, static_cast<unsigned char*>(ws));
+  return run_route_permute(p, X, W_r, bias, logits, topk_ids, topk_gates, w.route_partial,
+                           w.blockcnt, counts, offsets, raw_counts ? raw_counts : w.raw,
+                           perm_token, inv_slot, nullptr, (hipStream_t)stream);
 }
 
 static_assert(moe::kNoallocScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "scratch size in moe.h");
@@ -629,11 +695,10 @@ moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, con
     return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_FORWARD)");
   hipStream_t s = (hipStream_t)stream;
   ForwardWs w = carve_forward(p, static_cast<unsigned char*>(ws));
-  MOE_TRY(hip_status(moe::launch_route(p, X, W_r, bias, nullptr, w.ids, w.gates, w.route_partial, s),
-                     "route launch"));
   const bool rounding = (desc->flags & MOE_FLAG_TOKEN_ROUNDING) != 0;
-  MOE_TRY(run_permute(p, w.ids, w.counts, w.offsets, nullptr, w.perm, w.inv, w.permute,
-                      rounding ? nullptr : w.table, s));
+  MOE_TRY(run_route_permute(p, X, W_r, bias, nullptr, w.ids, w.gates, w.route_partial, w.blockcnt,
+                            w.counts, w.offsets, w.raw, w.perm, w.inv, rounding ? nullptr : w.table,
+                            s));
   if (rounding) {
     moe::RoundWs rw;
     moe::round_ws_bytes(p, &rw, w.round);
@@ -676,11 +741,9 @@ moe_status moe_forward_train(const moe_desc* desc, const void* X, const void* W_
   hipStream_t s = (hipStream_t)stream;
   const Saved sv = carve_saved(p, static_cast<unsigned char*>(saved));
   const ForwardWs w = carve_forward(p, static_cast<unsigned char*>(ws));
-  MOE_TRY(hip_status(moe::launch_route(p, X, W_r, bias, sv.logits, sv.ids, sv.gates,
-                                       w.route_partial, s),
-                     "route launch"));
-  MOE_TRY(run_permute(p, sv.ids, sv.counts, sv.offsets, nullptr, sv.perm, sv.inv, w.permute,
-                      sv.table, s));
+  MOE_TRY(run_route_permute(p, X, W_r, bias, sv.logits, sv.ids, sv.gates, w.route_partial,
+                            w.blockcnt, sv.counts, sv.offsets, w.raw, sv.perm, sv.inv, sv.table,
+                            s));
   MOE_TRY(hip_status(moe::launch_gemm_up(p, X, sv.perm, sv.table, W_gate, W_up, w.H, s, sv.Hpre),
                      "grouped GEMM (up) launch"));
   MOE_TRY(hip_status(moe::launch_gemm_down(p, w.H, sv.table, W_down, w.O, s),

@@ -71,9 +71,31 @@ inline size_t route_partial_bytes(const Problem& p) {
   return (size_t)ks * (size_t)p.T * (size_t)(32 * route_nbw(p.E)) * sizeof(float);
 }
 
+// Per-block expert counts written by the router for the fused permutation:
+// tokens per count block (the selecting workgroup's token block: 64, or 16
+// for the split-k finish at more than 64 padded experts), blocks, and the
+// row length of the expert-major array blockcnt[E][ld] (a multiple of 4, so
+// that rows can be read as 16-byte vectors).  `split` says whether the
+// router may split k (moe_route_ws / moe_forward).
+inline int route_count_block(const Problem& p, bool split) {
+  return (split && route_ksplit(p) > 1 && route_nbw(p.E) >= 4) ? 16 : 64;
+}
+inline int64_t route_count_blocks(const Problem& p, bool split) {
+  const int cb = route_count_block(p, split);
+  return (p.T + cb - 1) / cb;
+}
+inline int64_t route_count_ld(const Problem& p, bool split) {
+  return (route_count_blocks(p, split) + 3) / 4 * 4;
+}
+inline size_t route_count_bytes(const Problem& p, bool split) {
+  return (size_t)p.E * (size_t)route_count_ld(p, split) * sizeof(int32_t);
+}
+
 // partial: route_partial_bytes(p) of workspace, or NULL (no k split).
+// blockcnt (or NULL): receives the per-block expert counts described above.
 hipError_t launch_route(const Problem& p, const void* X, const void* W_r, const float* bias,
-                        float* logits, int32_t* ids, float* gates, float* partial, hipStream_t s);
+                        float* logits, int32_t* ids, float* gates, float* partial, hipStream_t s,
+                        int32_t* blockcnt = nullptr);
 // The fp32 scores X W1 and X W2 of the same bf16 tokens in one launch (no
 // bias, no selection); both widths must be multiples of 8 and at most 256.
 bool route_pair_supported(int E1, int E2);
@@ -96,6 +118,18 @@ hipError_t launch_tile_table(const Problem& p, const int32_t* offsets, int32_t* 
 hipError_t launch_permute_one_block(const Problem& p, const int32_t* ids, int32_t* raw,
                                    int32_t* counts, int32_t* offsets, int32_t* table,
                                    int32_t* perm, int32_t* inv, hipStream_t s);
+
+// The whole permutation after a router that wrote per-block expert counts
+// (blockcnt, cb tokens per block, row length ld): one launch of 256-token
+// workgroups, each reducing the counts of the blocks before it (no global
+// atomics) and ranking its own tokens with an LDS bitmask.  Outputs are
+// those of histogram + scan + scatter.  With T <= 256 blockcnt is not read
+// (may be NULL).  table may be NULL.
+constexpr int kFusedPermuteTokens = 256;
+hipError_t launch_permute_fused(const Problem& p, const int32_t* ids, const int32_t* blockcnt,
+                                int cb, int64_t ld, int32_t* raw, int32_t* counts,
+                                int32_t* offsets, int32_t* table, int32_t* perm, int32_t* inv,
+                                hipStream_t s);
 
 // Static device scratch of the allocation-free permutation entry point
 // (permute.hip): its address on the current device, looked up once per

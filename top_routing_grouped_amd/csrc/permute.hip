@@ -323,6 +323,224 @@ __global__ __launch_bounds__(kB) void permute_one_block_kernel(
   }
 }
 
+// The fused permutation (after a router that wrote per-block expert counts).
+// One workgroup of 1024 threads per 256 tokens:
+//   1. every wave sums whole rows of the router's expert-major counts
+//      blockcnt[E][ld] (64 lanes x 16-byte loads = 256 blocks per load, eight
+//      rows in flight), split at this workgroup's first token: base[e] =
+//      assignments to e from earlier tokens, total[e] = all of them;
+//   2. counts = min(total, C), offsets = exclusive scan (workgroup 0 writes
+//      raw counts, counts, offsets and the tile table);
+//   3. the first 256 threads (one token each) set bits in an LDS bitmask per
+//      expert (256 bits = 8 words), an 8-lane scan turns the words' popcounts
+//      into exclusive prefixes, and a token's rank inside expert e is base[e]
+//      plus the prefix of its word plus the popcount of the lower bits of its
+//      word.  A workgroup's kept tokens of expert e fill one contiguous run of
+//      slots, so (for K <= 32) the tokens are staged in LDS by expert and each
+//      run is stored by consecutive lanes instead of one 4-byte store per
+//      (token, k) to a random slot.
+// Same definitions as histogram + scan + scatter, so the same outputs.
+constexpr int kFT = kFusedPermuteTokens;   // tokens per workgroup
+constexpr int kFThreads = 1024;
+constexpr int kFWords = kFT / 32;
+constexpr int kFRows = 8;                  // rows of counts in flight per wave
+constexpr int kFStageK = 32;               // largest K whose slots are staged in LDS
+
+// Sum over the 64 lanes of a wave, returned to every lane: DPP steps inside
+// each 16-lane row (lane pairs, quads, half-row mirror, row mirror), then the
+// four row sums read out with readlane (no LDS round trips).
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int wave_sum(int x) {
+  x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);   // row_half_mirror
+  x += dpp_mov<0x140>(x);   // row_mirror
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+         __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
+}
+
+__global__ __launch_bounds__(kFThreads) void permute_fused_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ blockcnt, int cb, int64_t ld,
+    int64_t nbc, int32_t* __restrict__ raw, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ table, int64_t max_tiles,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int64_t T, int E, int K, int64_t C) {
+  __shared__ uint32_t bits[256 * kFWords];
+  __shared__ int pre[256 * kFWords];
+  __shared__ int base_s[256];
+  __shared__ int tot_s[256];
+  __shared__ int offs_s[256];
+  __shared__ int lst_s[256];                // start of each expert's run in stage[]
+  __shared__ int tmp[256];
+  __shared__ int stage[kFT * kFStageK];     // kept tokens, grouped by expert
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  constexpr int kWaves = kFThreads / 64;
+  const int64_t t0 = (int64_t)blockIdx.x * kFT;
+  int Ep = 1;
+  while (Ep < E) Ep <<= 1;
+  for (int j = tid; j < Ep * kFWords; j += kFThreads) bits[j] = 0u;
+
+  // 1. counts of the blocks before this workgroup, and of all blocks, per expert
+  if (gridDim.x > 1) {
+    using i4 = int __attribute__((ext_vector_type(4)));
+    const int64_t bfirst = t0 / cb;           // a multiple of 4
+    const int64_t nchunk = (nbc + 255) / 256;
+    for (int e0 = wave; e0 < E; e0 += kWaves * kFRows) {
+      int bef[kFRows], tot[kFRows];
+#pragma unroll
+      for (int r = 0; r < kFRows; ++r) bef[r] = tot[r] = 0;
+      for (int64_t c = 0; c < nchunk; ++c) {
+        const int64_t q = c * 256 + 4 * lane;
+        i4 v[kFRows];
+#pragma unroll
+        for (int r = 0; r < kFRows; ++r) {
+          const int e = e0 + kWaves * r;
+          v[r] = (e < E && q < nbc) ? *reinterpret_cast<const i4*>(blockcnt + (int64_t)e * ld + q)
+                                    : i4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int r = 0; r < kFRows; ++r)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int x = (q + j < nbc) ? v[r][j] : 0;   // entries past nbc are not counts
+            tot[r] += x;
+            if (q + j < bfirst) bef[r] += x;
+          }
+      }
+#pragma unroll
+      for (int r = 0; r < kFRows; ++r) {
+        const int e = e0 + kWaves * r;
+        const int sb = wave_sum(bef[r]), st = wave_sum(tot[r]);
+        if (lane == 0 && e < E) {
+          base_s[e] = sb;
+          tot_s[e] = st;
+        }
+      }
+    }
+  } else if (tid < 256) {
+    base_s[tid] = 0;
+  }
+
+  // 3a. bitmask of this workgroup's tokens per expert
+  const int64_t t = t0 + tid;
+  const bool valid = tid < kFT && t < T;
+  const int w = (tid >> 5) & (kFWords - 1);
+  const uint32_t bit = 1u << (tid & 31);
+  __syncthreads();                            // bits zeroed
+  // the first kChunk ids stay in registers for the ranking pass
+  int e_first[kChunk];
+#pragma unroll
+  for (int c = 0; c < kChunk; ++c) e_first[c] = (valid && c < K) ? ids[t * K + c] : -1;
+  if (valid)
+    for (int k0 = 0; k0 < K; k0 += kChunk) {
+      int ee[kChunk];
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c)
+        ee[c] = (k0 == 0) ? e_first[c] : ((k0 + c < K) ? ids[t * K + k0 + c] : -1);
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c)
+        if (ee[c] >= 0 && ee[c] < E) atomicOr(&bits[ee[c] * kFWords + w], bit);
+    }
+  __syncthreads();
+  // 3b. exclusive prefix of the words' popcounts, per expert (8-lane segments)
+  for (int j = tid; j < Ep * kFWords; j += kFThreads) {
+    const int c = __popc(bits[j]);
+    int x = c;
+#pragma unroll
+    for (int off = 1; off < kFWords; off <<= 1) {
+      const int y = __shfl_up(x, off, kFWords);
+      if ((j & (kFWords - 1)) >= off) x += y;
+    }
+    pre[j] = x - c;
+  }
+  __syncthreads();
+  int mytot = 0, mine = 0;                    // mine: this workgroup's assignments to expert tid
+  if (tid < E) {
+    mine = pre[tid * kFWords + kFWords - 1] + __popc(bits[tid * kFWords + kFWords - 1]);
+    mytot = (gridDim.x > 1) ? tot_s[tid] : mine;
+  }
+  const bool staged = K <= kFStageK;
+  if (staged) {
+    int nst = 0;
+    const int ls = block_exscan256(mine, E, tmp, &nst);
+    if (tid < E) lst_s[tid] = ls;
+  }
+
+  // 2. capped counts, offsets (and, in workgroup 0, the metadata and tile table)
+  int kept = 0;
+  if (tid < E) kept = ((int64_t)mytot < C) ? mytot : (int)C;
+  int total = 0;
+  const int off = block_exscan256(kept, E, tmp, &total);
+  if (tid < E) offs_s[tid] = off;
+  if (blockIdx.x == 0) {
+    if (tid < E) {
+      raw[tid] = mytot;
+      counts[tid] = kept;
+      offsets[tid] = off;
+    }
+    if (tid == 0) offsets[E] = total;
+    if (table) {
+      const int nt = (tid < E) ? (kept + kGemmBM - 1) / kGemmBM : 0;
+      int ntiles = 0;
+      const int start = block_exscan256(nt, E, tmp, &ntiles);
+      if (tid < E) write_tiles(tid, off, kept, start, max_tiles, table);
+      if (tid == 0) {
+        table[0] = (int64_t)ntiles < max_tiles ? ntiles : (int)max_tiles;
+        table[1] = table[2] = table[3] = 0;
+      }
+    }
+  }
+  __syncthreads();                            // base_s, offs_s, lst_s complete
+
+  // 3c. ranks and slots (perm_token through the staging runs, or directly)
+  if (valid)
+    for (int k0 = 0; k0 < K; k0 += kChunk) {
+      int ee[kChunk];
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c)
+        ee[c] = (k0 == 0) ? e_first[c] : ((k0 + c < K) ? ids[t * K + k0 + c] : -1);
+      int32_t slot[kChunk];
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) {
+        const int e = ee[c];
+        slot[c] = -1;
+        if (k0 + c < K && e >= 0 && e < E) {
+          const int jw = e * kFWords + w;
+          const int within = pre[jw] + __popc(bits[jw] & (bit - 1u));
+          const int64_t rank = (int64_t)base_s[e] + within;
+          if (rank < C) {
+            slot[c] = (int32_t)(offs_s[e] + rank);
+            if (staged) stage[lst_s[e] + within] = (int32_t)t;
+            else perm[slot[c]] = (int32_t)t;
+          }
+        }
+      }
+      if ((K & 3) == 0 && k0 + kChunk <= K) {   // whole 16-byte pieces of the token's row
+        using i4 = int __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int c = 0; c < kChunk; c += 4)
+          *reinterpret_cast<i4*>(inv + t * K + k0 + c) = i4{slot[c], slot[c + 1], slot[c + 2], slot[c + 3]};
+      } else {
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c)
+          if (k0 + c < K) inv[t * K + k0 + c] = slot[c];
+      }
+    }
+  if (!staged) return;
+  __syncthreads();
+  // each expert's kept run: consecutive lanes store consecutive slots
+  for (int e = wave; e < E; e += kWaves) {
+    const int n = pre[e * kFWords + kFWords - 1] + __popc(bits[e * kFWords + kFWords - 1]);
+    const int64_t room = C - (int64_t)base_s[e];          // ranks below C are kept
+    const int nk = room <= 0 ? 0 : (room < n ? (int)room : n);
+    const int64_t dst = (int64_t)offs_s[e] + base_s[e];
+    for (int i = lane; i < nk; i += 64) perm[dst + i] = stage[lst_s[e] + i];
+  }
+}
+
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ table,
                                                          int64_t max_tiles, int64_t rows_max,
@@ -378,6 +596,20 @@ hipError_t launch_permute_one_block(const Problem& p, const int32_t* ids, int32_
                                    int32_t* perm, int32_t* inv, hipStream_t s) {
   hipLaunchKernelGGL(permute_one_block_kernel, dim3(1), dim3(kB), 0, s, ids, raw, counts, offsets,
                      table, max_row_tiles(p, kGemmBM), perm, inv, p.T, p.E, p.K, p.C);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_fused(const Problem& p, const int32_t* ids, const int32_t* blockcnt,
+                                int cb, int64_t ld, int32_t* raw, int32_t* counts,
+                                int32_t* offsets, int32_t* table, int32_t* perm, int32_t* inv,
+                                hipStream_t s) {
+  const int64_t nwg = (p.T + kFT - 1) / kFT;
+  if (nwg > 1 && (blockcnt == nullptr || kFT % cb != 0 || (kFT / cb) % 4 != 0))
+    return hipErrorInvalidValue;
+  const int64_t nbc = (p.T + cb - 1) / cb;
+  hipLaunchKernelGGL(permute_fused_kernel, dim3((unsigned)nwg), dim3(kFThreads), 0, s, ids, blockcnt, cb,
+                     ld, nbc, raw, counts, offsets, table, max_row_tiles(p, kGemmBM), perm, inv,
+                     p.T, p.E, p.K, p.C);
   return hipGetLastError();
 }
 

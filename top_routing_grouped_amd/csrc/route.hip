@@ -123,7 +123,8 @@ __device__ __forceinline__ void sort_desc(int64_t* v) {
 // back into the token's own LDS row (no longer read) for the gate pass.
 template <int V, int R = 4>
 __device__ __forceinline__ void topk_from_lds(float* L, int S, int64_t t0, int64_t T, int E, int K,
-                                              int32_t* __restrict__ ids, float* __restrict__ gates) {
+                                              int32_t* __restrict__ ids, float* __restrict__ gates,
+                                              int* cntl = nullptr) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int q = lane >> 4;
@@ -177,7 +178,10 @@ __device__ __forceinline__ void topk_from_lds(float* L, int S, int64_t t0, int64
       for (int r = 0; r < R; ++r) {
         const int tl = 4 * R * w + R * q + r;
         L[tl * S + k] = key_value(m[r]);
-        if (t0 + tl < T) ids[(t0 + tl) * K + k] = cand[r];
+        if (t0 + tl < T) {
+          ids[(t0 + tl) * K + k] = cand[r];
+          if (cntl) atomicAdd(&cntl[cand[r]], 1);
+        }
       }
     }
   }
@@ -204,7 +208,7 @@ __device__ __forceinline__ void topk_from_lds(float* L, int S, int64_t t0, int64
 template <int V, bool PREPPED = false>
 __device__ __forceinline__ void route_tail(float* L, int S, int64_t t0, int64_t T, int E, int K, int Epad,
                            const float* __restrict__ bias, float* __restrict__ logits,
-                           int32_t* __restrict__ ids, float* __restrict__ gates) {
+                           int32_t* __restrict__ ids, float* __restrict__ gates, int* cntl) {
   if (!PREPPED) {
     for (int idx = threadIdx.x; idx < kTok * Epad; idx += kThreads) {
       const int r = idx / Epad, e = idx - (idx / Epad) * Epad;
@@ -225,7 +229,20 @@ __device__ __forceinline__ void route_tail(float* L, int S, int64_t t0, int64_t 
     }
     __syncthreads();  // selection rewrites the rows being exported
   }
-  topk_from_lds<V>(L, S, t0, T, E, K, ids, gates);
+  topk_from_lds<V>(L, S, t0, T, E, K, ids, gates, cntl);
+}
+
+// Per-block expert counts for the permutation: the selection above adds each
+// chosen expert of the block's tokens to an LDS array (zeroed by
+// count_zero before the selection), which is then stored expert-major,
+// blockcnt[e * ldc + block] (every expert's entry, zeros included).
+__device__ __forceinline__ void count_zero(int* cntl, int nthreads) {
+  for (int e = threadIdx.x; e < 256; e += nthreads) cntl[e] = 0;
+}
+__device__ __forceinline__ void count_store(const int* cntl, int32_t* __restrict__ blockcnt,
+                                            int64_t ldc, int64_t block, int E, int nthreads) {
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += nthreads) blockcnt[e * ldc + block] = cntl[e];
 }
 
 // ---------------------------------------------------------------- bf16 router (MFMA)
@@ -236,8 +253,9 @@ template <int NBW, bool VEC>
 __global__ __launch_bounds__(kThreads, (NBW >= 8) ? 1 : 2) void route_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
-    int d, int E, int K) {
+    int d, int E, int K, int32_t* __restrict__ blockcnt, int64_t ldc) {
   constexpr int Epad = 32 * NBW;
+  __shared__ int cntl[256];
   // X stages held in registers (prefetch depth); fewer when the weight tile is wide
   constexpr int kPF = (NBW >= 8) ? 4 : 6;
   constexpr int R = Epad + 16;            // bf16 elements per LDS weight row (padded)
@@ -375,8 +393,10 @@ __global__ __launch_bounds__(kThreads, (NBW >= 8) ? 1 : 2) void route_bf16_kerne
         const int col = wn * 16 * NBW + nb * 16 + (lane & 15);
         L[row * S + col] = acc[rb][nb][r];
       }
+  if (blockcnt) count_zero(cntl, kThreads);
   __syncthreads();
-  route_tail<2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates);
+  route_tail<2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates, blockcnt ? cntl : nullptr);
+  if (blockcnt) count_store(cntl, blockcnt, ldc, blockIdx.x, E, kThreads);
 }
 
 // ---------------------------------------------------------------- bf16 router, staged copies
@@ -417,7 +437,9 @@ struct RouteGeo {
   static constexpr int kW = kBK * Epad * 2;          // W_r tile bytes
   static constexpr int kStage = kX + kW;
   static constexpr int S = Epad + 16;                // floats per score row
-  static constexpr int kLds = (NST * kStage > kTok * S * 4) ? NST * kStage : kTok * S * 4;
+  // per-block expert counts (256 ints) after the score rows, in the idle stage space
+  static constexpr int kCnt = kTok * S * 4;
+  static constexpr int kLds = (NST * kStage > kCnt + 1024) ? NST * kStage : kCnt + 1024;
   static_assert(kLds <= 160 * 1024, "one workgroup's LDS");
   static constexpr int kXInstr = kX / 1024 / NW;     // copies per wave per tile
   static constexpr int kWInstr = kW / 1024 / NW;
@@ -444,7 +466,7 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
     int d, int E, int K, int ksplit, float* __restrict__ partial, const uint16_t* __restrict__ Wr2,
-    float* __restrict__ logits2, int E2, int nblk) {
+    float* __restrict__ logits2, int E2, int nblk, int32_t* __restrict__ blockcnt, int64_t ldc) {
   using G = RouteGeo<NBW>;
   constexpr int Epad = G::Epad, NST = G::NST, CPR = G::CPR;
   constexpr int XI = G::kXInstr, WI = G::kWInstr, CBW = G::CBW;
@@ -464,6 +486,7 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
     logits = logits2;
     E = E2;
     ids = nullptr;
+    blockcnt = nullptr;
   }
   const int64_t t0 = (int64_t)bx * kTok;
   const int KT_all = d / kBK;
@@ -599,6 +622,8 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
     bcol[nb] = (col < E) ? (bias ? bias[col] : 0.f) : -__builtin_inff();
   }
   __syncthreads();
+  int* cntl = reinterpret_cast<int*>(smem + G::kCnt);
+  if (blockcnt) count_zero(cntl, G::kThreads);
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -619,7 +644,9 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
     }
     __syncthreads();  // selection rewrites the rows being exported
   }
-  if (ids) topk_from_lds<2 * NBW, kTok / (4 * G::NW)>(L, G::S, t0, T, E, K, ids, gates);
+  if (ids) topk_from_lds<2 * NBW, kTok / (4 * G::NW)>(L, G::S, t0, T, E, K, ids, gates,
+                                                       blockcnt ? cntl : nullptr);
+  if (blockcnt) count_store(cntl, blockcnt, ldc, bx, E, G::kThreads);
 }
 
 // Split-k finish, part 1: partial[0] = sum over ks of partial[ks], in ks
@@ -656,16 +683,20 @@ struct SelGeo {
   static constexpr int Epad = 32 * NBW, S = Epad + 16;
   static constexpr int TW = (NBW >= 4) ? 16 : kTok;
   static constexpr int R = TW / 16;
-  static constexpr int kLds = TW * S * 4;
+  static constexpr int kCnt = TW * S * 4;            // per-block expert counts after the rows
+  static constexpr int kLds = kCnt + 1024;
 };
 template <int NBW>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const float* __restrict__ scores, const float* __restrict__ bias, float* __restrict__ logits,
-    int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T, int E, int K) {
+    int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T, int E, int K,
+    int32_t* __restrict__ blockcnt, int64_t ldc) {
   using G = SelGeo<NBW>;
   constexpr int Epad = G::Epad, S = G::S, TW = G::TW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   float* L = reinterpret_cast<float*>(smem);
+  int* cntl = reinterpret_cast<int*>(smem + G::kCnt);
+  if (blockcnt) count_zero(cntl, kThreads);
   const int64_t t0 = (int64_t)blockIdx.x * TW;
   // Each thread owns one 4-column group and kPer rows of it: all of its
   // 16-byte loads are issued before the first is used (one at a time, the
@@ -704,7 +735,8 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
     }
     __syncthreads();  // selection rewrites the rows being exported
   }
-  topk_from_lds<2 * NBW, G::R>(L, S, t0, T, E, K, ids, gates);
+  topk_from_lds<2 * NBW, G::R>(L, S, t0, T, E, K, ids, gates, blockcnt ? cntl : nullptr);
+  if (blockcnt) count_store(cntl, blockcnt, ldc, blockIdx.x, E, kThreads);
 }
 
 // ---------------------------------------------------------------- fp32 router (plain FMA)
@@ -712,10 +744,12 @@ template <int NBW>
 __global__ __launch_bounds__(kThreads) void route_f32_kernel(
     const float* __restrict__ X, const float* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
-    int d, int E, int K) {
+    int d, int E, int K, int32_t* __restrict__ blockcnt, int64_t ldc) {
   constexpr int Epad = 32 * NBW;
   constexpr int S = Epad + 16;
   __shared__ float L[kTok * S];
+  __shared__ int cntl[256];
+  if (blockcnt) count_zero(cntl, kThreads);
   const int64_t t0 = (int64_t)blockIdx.x * kTok;
   for (int idx = threadIdx.x; idx < kTok * Epad; idx += kThreads) {
     const int r = idx / Epad, e = idx - (idx / Epad) * Epad;
@@ -727,13 +761,15 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
     L[r * S + e] = s;
   }
   __syncthreads();
-  route_tail<2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates);
+  route_tail<2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates, blockcnt ? cntl : nullptr);
+  if (blockcnt) count_store(cntl, blockcnt, ldc, blockIdx.x, E, kThreads);
 }
 
 template <int NBW>
 hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, const float* bias,
                             float* logits, int32_t* ids, float* gates, float* partial,
-                            hipStream_t s) {
+                            int32_t* blockcnt, hipStream_t s) {
+  const int64_t ldc = blockcnt ? route_count_ld(p, partial != nullptr) : 0;
   const dim3 grid((unsigned)((p.T + kTok - 1) / kTok));
   if (p.bf16) {
     if (p.E % 8 == 0) {
@@ -746,7 +782,8 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
       hipLaunchKernelGGL(kern, dim3(grid.x, (unsigned)ksplit), dim3(RouteGeo<NBW>::kThreads),
                          (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)W_r,
                          bias, logits, ids, gates, p.T, p.d, p.E, p.K, ksplit, partial,
-                         (const uint16_t*)nullptr, (float*)nullptr, 0, (int)grid.x);
+                         (const uint16_t*)nullptr, (float*)nullptr, 0, (int)grid.x,
+                         ksplit > 1 ? nullptr : blockcnt, ldc);
       if (ksplit > 1) {
         err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -761,15 +798,17 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kSelLds);
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(sel, dim3((unsigned)((p.T + TW - 1) / TW)), dim3(kThreads),
-                           (size_t)kSelLds, s, partial, bias, logits, ids, gates, p.T, p.E, p.K);
+                           (size_t)kSelLds, s, partial, bias, logits, ids, gates, p.T, p.E, p.K,
+                           blockcnt, ldc);
       }
     } else
       hipLaunchKernelGGL((route_bf16_kernel<NBW, false>), grid, dim3(kThreads), 0, s,
                          (const uint16_t*)X, (const uint16_t*)W_r, bias, logits, ids, gates, p.T,
-                         p.d, p.E, p.K);
+                         p.d, p.E, p.K, blockcnt, ldc);
   } else {
     hipLaunchKernelGGL((route_f32_kernel<NBW>), grid, dim3(kThreads), 0, s, (const float*)X,
-                       (const float*)W_r, bias, logits, ids, gates, p.T, p.d, p.E, p.K);
+                       (const float*)W_r, bias, logits, ids, gates, p.T, p.d, p.E, p.K, blockcnt,
+                       ldc);
   }
   return hipGetLastError();
 }
@@ -789,7 +828,8 @@ hipError_t launch_logits_pair_nbw(int64_t T, int d, int E1, int E2, const void* 
   hipLaunchKernelGGL(kern, dim3(2 * nblk, 1), dim3(RouteGeo<NBW>::kThreads),
                      (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)W1,
                      (const float*)nullptr, logits1, (int32_t*)nullptr, (float*)nullptr, T, d, E1,
-                     1, 1, (float*)nullptr, (const uint16_t*)W2, logits2, E2, (int)nblk);
+                     1, 1, (float*)nullptr, (const uint16_t*)W2, logits2, E2, (int)nblk,
+                     (int32_t*)nullptr, (int64_t)0);
   return hipGetLastError();
 }
 }  // namespace
@@ -810,12 +850,13 @@ hipError_t launch_logits_pair(int64_t T, int d, int E1, int E2, const void* X, c
 }
 
 hipError_t launch_route(const Problem& p, const void* X, const void* W_r, const float* bias,
-                        float* logits, int32_t* ids, float* gates, float* partial, hipStream_t s) {
+                        float* logits, int32_t* ids, float* gates, float* partial,
+                        hipStream_t s, int32_t* blockcnt) {
   const int nbw = route_nbw(p.E);
-  if (nbw <= 1) return launch_route_nbw<1>(p, X, W_r, bias, logits, ids, gates, partial, s);
-  if (nbw <= 2) return launch_route_nbw<2>(p, X, W_r, bias, logits, ids, gates, partial, s);
-  if (nbw <= 4) return launch_route_nbw<4>(p, X, W_r, bias, logits, ids, gates, partial, s);
-  return launch_route_nbw<8>(p, X, W_r, bias, logits, ids, gates, partial, s);
+  if (nbw <= 1) return launch_route_nbw<1>(p, X, W_r, bias, logits, ids, gates, partial, blockcnt, s);
+  if (nbw <= 2) return launch_route_nbw<2>(p, X, W_r, bias, logits, ids, gates, partial, blockcnt, s);
+  if (nbw <= 4) return launch_route_nbw<4>(p, X, W_r, bias, logits, ids, gates, partial, blockcnt, s);
+  return launch_route_nbw<8>(p, X, W_r, bias, logits, ids, gates, partial, blockcnt, s);
 }
 
 }  // namespace moe
