@@ -34,6 +34,14 @@ Extra modes (used for profiler runs):
                          of the forward GEMMs: the training forward's up GEMM
                          also writes the pre-activations, the rounded forward's
                          GEMMs see fewer rows); --no-train is the same switch.
+    --pmc-kernel NAME    kernel-name substring that --pmc-summary averages
+                         (default: the tiled up GEMM).
+    --gather-study MODE  only time the up GEMM on the workload's routing, K cold
+                         launches: MODE "gathered" reads token rows of X through
+                         perm_token (the product path), "pregathered" reads a
+                         contiguous copy X[perm_token] built beforehand with
+                         torch (a measurement baseline, never a product path),
+                         "both" interleaves the two.  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -75,6 +83,8 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=4, default=None)
     ap.add_argument("--warm", action="store_true")
     ap.add_argument("--forward-only", "--no-train", dest="forward_only", action="store_true")
+    ap.add_argument("--pmc-kernel", default=None)
+    ap.add_argument("--gather-study", choices=["gathered", "pregathered", "both"], default=None)
     return ap.parse_args()
 
 
@@ -103,9 +113,11 @@ def _pmc_per_dispatch(directory: str, counter: str, name_has: str | None):
     return out
 
 
-def pmc_summary(fetch_dir, write_dir, calib_fetch_dir, calib_write_dir, workload):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the up GEMM, scaled by
-    what the same counters read for a plain copy of known size."""
+def pmc_summary(fetch_dir, write_dir, calib_fetch_dir, calib_write_dir, workload, kernel=None):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the up GEMM (or the
+    kernel named by `kernel`), scaled by what the same counters read for a
+    plain copy of known size."""
+    kname = kernel or UP_KERNEL
     cf = _pmc_per_dispatch(calib_fetch_dir, "FETCH_SIZE", None)
     cw = _pmc_per_dispatch(calib_write_dir, "WRITE_SIZE", None)
     # the calibration run copies FLUSH_BYTES (--calib-copy 1073741824): the
@@ -114,11 +126,11 @@ def pmc_summary(fetch_dir, write_dir, calib_fetch_dir, calib_write_dir, workload
     copy_write = max(v for _, v in cw.values()) * 1024.0
     f_scale = FLUSH_BYTES / copy_fetch
     w_scale = FLUSH_BYTES / copy_write
-    fu = [v for _, v in _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", UP_KERNEL).values()]
-    wu = [v for _, v in _pmc_per_dispatch(write_dir, "WRITE_SIZE", UP_KERNEL).values()]
+    fu = [v for _, v in _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", kname).values()]
+    wu = [v for _, v in _pmc_per_dispatch(write_dir, "WRITE_SIZE", kname).values()]
     fetch = statistics.mean(fu) * 1024.0 * f_scale
     write = statistics.mean(wu) * 1024.0 * w_scale
-    rec = {"workload": workload, "kernel": "grouped_gemm_bf16<up>", "dispatches": [len(fu), len(wu)],
+    rec = {"workload": workload, "kernel": kname, "dispatches": [len(fu), len(wu)],
            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
            "traffic_bytes_per_launch": fetch + write,
            "fetch_scale": f_scale, "write_scale": w_scale,
@@ -209,11 +221,51 @@ def pct(xs, q):
     return s[i]
 
 
+def gather_study(args, moe, dev, desc, desc_ready, offsets, perm, H, ws_f, flush, ev, stream, w,
+                 N):
+    """The up GEMM on the workload's routing with the token rows gathered
+    through perm_token (the product path) and, as a baseline, on a
+    contiguous pre-gathered copy X[perm_token[:N]] with the identity
+    permutation: same kernel, same tile table, same weights and flops; only
+    where the A rows come from differs."""
+    import torch
+    Xg = dev["X"].index_select(0, perm[:N].long()).contiguous()
+    ident = torch.arange(max(1, perm.numel()), dtype=torch.int32, device="cuda")
+    modes = ["gathered", "pregathered"] if args.gather_study == "both" else [args.gather_study]
+    src = {"gathered": (dev["X"], perm), "pregathered": (Xg, ident)}
+    # build the tile table once from the offsets (the launches below reuse it)
+    moe.moe_grouped_gemm_up(desc, dev["X"], offsets, perm, dev["W_gate"], dev["W_up"], H, ws_f)
+    for i in range(args.warmup):
+        for m in modes:
+            flush(i)
+            moe.moe_grouped_gemm_up(desc_ready, src[m][0], offsets, src[m][1], dev["W_gate"],
+                                    dev["W_up"], H, ws_f)
+    times = {m: [] for m in modes}
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        for m in modes:
+            flush(i)
+            a, b = ev(), ev()
+            a.record(stream)
+            moe.moe_grouped_gemm_up(desc_ready, src[m][0], offsets, src[m][1], dev["W_gate"],
+                                    dev["W_up"], H, ws_f)
+            b.record(stream)
+            torch.cuda.synchronize()
+            times[m].append(a.elapsed_time(b) * 1e3)
+    flops = 4.0 * N * w.d * w.n
+    out = {"gather_study": w.name, "kept_rows": N,
+           "a_rows_bytes": {"gathered_X": w.T * w.d * 2, "pregathered_copy": N * w.d * 2}}
+    for m in modes:
+        out[m] = {"us_mean": statistics.mean(times[m]), "us_median": statistics.median(times[m]),
+                  "tflops": flops / (statistics.mean(times[m]) * 1e-6) / 1e12}
+    print(json.dumps(out))
+
+
 # ---------------------------------------------------------------- main
 def main():
     args = parse()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary, args.workload)
+        pmc_summary(*args.pmc_summary, args.workload, args.pmc_kernel)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -338,6 +390,11 @@ def main():
             evs[i][1].record(stream)
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in evs]
+
+    if args.gather_study:
+        gather_study(args, moe, dev, desc, desc_ready, offsets, perm, H, ws_f, flush, ev, stream,
+                     w, N)
+        return
 
     train = w.dtype == "bf16" and not args.forward_only
     if train:
