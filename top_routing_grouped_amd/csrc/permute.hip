@@ -124,12 +124,51 @@ __device__ void write_tiles(int e, int off, int cnt, int start, int64_t max_tile
   }
 }
 
+// First table entry of each expert's row tiles.  The grouped GEMMs give each
+// XCD a contiguous range of the table, so in expert order the most loaded
+// experts of a skewed router would all fall to the first XCDs (the Zipf-biased
+// layer: the nine experts capped at 640 rows on two of eight).  Instead the
+// experts, sorted by tile count (descending; ties by id), are dealt in a snake
+// over 8 lanes (0..7, 7..0, ...), and the table lists lane 0's experts, then
+// lane 1's, ...: every XCD's range gets a similar mix of heavy and light
+// experts, heavy ones first, while each expert's tiles stay contiguous.
+// All threads of the workgroup (at least 256) must call it; threads below E
+// pass their expert's tile count and get its first entry; *ntiles = total.
+__device__ int tile_starts(int nt, int E, int* cnt_s, int* ord_s, int* pref_s, int* tmp,
+                           int* ntiles) {
+  const int tid = threadIdx.x;
+  if (tid < 256) {
+    cnt_s[tid] = (tid < E) ? nt : 0;
+    ord_s[tid] = -1;
+  }
+  __syncthreads();
+  int key = 0;
+  if (tid < E) {
+    int rank = 0;
+    for (int j = 0; j < E; ++j) {
+      const int c = cnt_s[j];
+      rank += (c > nt) || (c == nt && j < tid);
+    }
+    const int round = rank >> 3, pos = rank & 7;
+    const int lane = (round & 1) ? 7 - pos : pos;
+    key = lane * 32 + round;                  // rounds <= 32 for E <= 256
+    ord_s[key] = tid;
+  }
+  __syncthreads();
+  const int v = (tid < 256 && ord_s[tid] >= 0) ? cnt_s[ord_s[tid]] : 0;
+  const int pref = block_exscan256(v, 256, tmp, ntiles);
+  if (tid < 256) pref_s[tid] = pref;
+  __syncthreads();
+  return (tid < E) ? pref_s[key] : 0;
+}
+
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t* __restrict__ blockcnt, int32_t* __restrict__ blockbase,
     int32_t* __restrict__ raw, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ table, int64_t max_tiles, int NB, int E, int64_t C) {
   __shared__ int part[kScanThreads];
   __shared__ int tmp[256];
+  __shared__ int tcnt_s[256], tord_s[256], tpref_s[256];   // tile_starts scratch
   int Ep = 1;
   while (Ep < E) Ep <<= 1;
   const int P = kScanThreads / Ep;            // block ranges per expert
@@ -180,7 +219,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   if (table) {
     const int nt = (tid < E) ? (kept + kGemmBM - 1) / kGemmBM : 0;
     int ntiles = 0;
-    const int start = block_exscan256(nt, E, tmp, &ntiles);
+    const int start = tile_starts(nt, E, tcnt_s, tord_s, tpref_s, tmp, &ntiles);
     if (tid < E) write_tiles(tid, off, kept, start, max_tiles, table);
     if (tid == 0) {
       table[0] = (int64_t)ntiles < max_tiles ? ntiles : (int)max_tiles;
@@ -257,6 +296,7 @@ __global__ __launch_bounds__(kB) void permute_one_block_kernel(
   __shared__ int cnt[256];
   __shared__ int offs[256];
   __shared__ int tmp[256];
+  __shared__ int tcnt_s[256], tord_s[256], tpref_s[256];   // tile_starts scratch
   const int tid = threadIdx.x;
   for (int j = tid; j < E * kWords; j += kB) bits[j] = 0u;
   if (tid < 256) cnt[tid] = 0;
@@ -291,7 +331,7 @@ __global__ __launch_bounds__(kB) void permute_one_block_kernel(
   if (table) {
     const int nt = (tid < E) ? (kept + kGemmBM - 1) / kGemmBM : 0;
     int ntiles = 0;
-    const int start = block_exscan256(nt, E, tmp, &ntiles);
+    const int start = tile_starts(nt, E, tcnt_s, tord_s, tpref_s, tmp, &ntiles);
     if (tid < E) write_tiles(tid, off, kept, start, max_tiles, table);
     if (tid == 0) {
       table[0] = (int64_t)ntiles < max_tiles ? ntiles : (int)max_tiles;
@@ -374,6 +414,7 @@ __global__ __launch_bounds__(kFThreads) void permute_fused_kernel(
   __shared__ int offs_s[256];
   __shared__ int lst_s[256];                // start of each expert's run in stage[]
   __shared__ int tmp[256];
+  __shared__ int tcnt_s[256], tord_s[256], tpref_s[256];   // tile_starts scratch
   __shared__ int stage[kFT * kFStageK];     // kept tokens, grouped by expert
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -485,7 +526,7 @@ __global__ __launch_bounds__(kFThreads) void permute_fused_kernel(
     if (table) {
       const int nt = (tid < E) ? (kept + kGemmBM - 1) / kGemmBM : 0;
       int ntiles = 0;
-      const int start = block_exscan256(nt, E, tmp, &ntiles);
+      const int start = tile_starts(nt, E, tcnt_s, tord_s, tpref_s, tmp, &ntiles);
       if (tid < E) write_tiles(tid, off, kept, start, max_tiles, table);
       if (tid == 0) {
         table[0] = (int64_t)ntiles < max_tiles ? ntiles : (int)max_tiles;
@@ -546,6 +587,7 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restri
                                                          int64_t max_tiles, int64_t rows_max,
                                                          int E) {
   __shared__ int tmp[256];
+  __shared__ int tcnt_s[256], tord_s[256], tpref_s[256];   // tile_starts scratch
   const int tid = threadIdx.x;
   int off = 0, cnt = 0;
   if (tid < E) {
@@ -557,7 +599,7 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restri
   }
   const int nt = (cnt + kGemmBM - 1) / kGemmBM;
   int ntiles = 0;
-  const int start = block_exscan256(nt, E, tmp, &ntiles);
+  const int start = tile_starts(nt, E, tcnt_s, tord_s, tpref_s, tmp, &ntiles);
   if (tid < E) write_tiles(tid, off, cnt, start, max_tiles, table);
   if (tid == 0) {
     table[0] = (int64_t)ntiles < max_tiles ? ntiles : (int)max_tiles;
