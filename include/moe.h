@@ -151,13 +151,16 @@ moe_status moe_workspace_size(const moe_desc* desc, int32_t entry, size_t* bytes
 moe_status moe_saved_layout_of(const moe_desc* desc, moe_saved_layout* out);
 
 /* Static description of a status code. */
-const char* moe_status_str(int32_t status);
+const char* moe_status_str(moe_status status);
 
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* moe_last_error(void);
 
 /* ---------------------------------------------------------------- device
- * Steps 1-2 (router GEMM, softmax, top-K, renormalised gates).
+ * Steps 1-2 (router GEMM, softmax, top-K, renormalised gates; page "MoE 的两个
+ * 上游创新：Routing-Free 与 OmniMoE" §1.1 (Router -> Softmax -> TopK) and
+ * "AI芯片如何支持MoE架构" §4.2-§4.3 (gating as dense dot products, top-K with
+ * a run-time K)).
  *   X[T,d] dtype, W_r[d,E] dtype, bias[E] fp32 or NULL,
  *   logits[T,E] fp32 or NULL (when given, receives the exact scores the
  *   selection was made on), topk_ids[T,K] int32, topk_gates[T,K] fp32.
@@ -166,7 +169,7 @@ const char* moe_last_error(void);
 moe_status moe_route(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
                      float* logits, int32_t* topk_ids, float* topk_gates, void* stream);
 
-/* moe_route with a workspace (MOE_WS_ROUTE bytes; may be 0, then ws may be
+/* moe_route with a workspace (same passages as moe_route; MOE_WS_ROUTE bytes; may be 0, then ws may be
  * NULL).  For batches whose 64-token blocks cannot fill the GPU (bf16, E a
  * multiple of 8) the router's k range is split over several workgroups per
  * block, whose fp32 partial scores go to ws and are summed in a fixed order
@@ -177,7 +180,11 @@ moe_status moe_route_ws(const moe_desc* desc, const void* X, const void* W_r, co
                         float* logits, int32_t* topk_ids, float* topk_gates, void* ws,
                         size_t ws_bytes, void* stream);
 
-/* Steps 3-5 (histogram, capacity cut in token order, exclusive scan, scatter).
+/* Steps 3-5 (histogram, capacity cut in token order, exclusive scan, scatter;
+ * SonicMoE article §11 (the metadata triple and its counting / prefix-sum /
+ * scatter-index steps), "算子与编译器：MoE 路由与稀疏 Kernel" §3-§4
+ * (permutation as counting + prefix sums; the capacity factor), OmniMoE page
+ * §2.3 (slots ordered by expert, then token)).
  *   topk_ids[T,K] int32 with distinct ids in [0,E) per token (as moe_route writes;
  *   other ids are ignored and marked dropped),
  *   counts[E] kept per expert, offsets[E+1] exclusive scan of counts,
@@ -229,7 +236,9 @@ moe_status moe_permute_noalloc(const moe_desc* desc, const int32_t* topk_ids, in
                                int32_t* offsets, int32_t* raw_counts, int32_t* perm_token,
                                int32_t* inv_slot, void* stream);
 
-/* Step 6: H[s,:] = silu(X[perm_token[s]] W_gate[e]) * (X[perm_token[s]] W_up[e])
+/* Step 6 (SonicMoE article §3 pipeline steps 3-4, §6.2 gather fused into the
+ * operand load, §6.3 SwiGLU in the epilogue):
+ * H[s,:] = silu(X[perm_token[s]] W_gate[e]) * (X[perm_token[s]] W_up[e])
  * for every slot s of expert e (rows gathered from X inside the GEMM; no
  * gathered copy of X is made).  offsets/perm_token as moe_permute writes them.
  *   H has moe_max_rows rows of n; ws: MOE_WS_GROUPED_FFN bytes. */
@@ -237,7 +246,8 @@ moe_status moe_grouped_gemm_up(const moe_desc* desc, const void* X, const int32_
                                const int32_t* perm_token, const void* W_gate, const void* W_up,
                                void* H, void* ws, size_t ws_bytes, void* stream);
 
-/* Step 7: O[s,:] = H[s,:] W_down[e] for every slot s of expert e.
+/* Step 7 (SonicMoE article §3 pipeline step 5): O[s,:] = H[s,:] W_down[e] for
+ * every slot s of expert e.
  *   O has moe_max_rows rows of d; ws: MOE_WS_GROUPED_FFN bytes. */
 moe_status moe_grouped_gemm_down(const moe_desc* desc, const void* H, const int32_t* offsets,
                                  const void* W_down, void* O, void* ws, size_t ws_bytes,
@@ -258,19 +268,23 @@ moe_status moe_round_tokens(const moe_desc* desc, const int32_t* topk_ids, const
                             int32_t* counts, int32_t* offsets, int32_t* perm_token,
                             int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream);
 
-/* Steps 6-7 in one call (moe_grouped_gemm_up then moe_grouped_gemm_down). */
+/* Steps 6-7 in one call (moe_grouped_gemm_up then moe_grouped_gemm_down;
+ * SonicMoE article §3). */
 moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* offsets,
                            const int32_t* perm_token, const void* W_gate, const void* W_up,
                            const void* W_down, void* H, void* O, void* ws, size_t ws_bytes,
                            void* stream);
 
-/* Step 8: Y[t,:] = sum over k with inv_slot[t,k] >= 0, in k order, of
+/* Step 8 (SonicMoE article §1: y = sum over the selected experts of gate x
+ * expert output; §6.1: the aggregation back to token order):
+ * Y[t,:] = sum over k with inv_slot[t,k] >= 0, in k order, of
  * topk_gates[t,k] * O[inv_slot[t,k],:], accumulated in fp32; a token whose
  * K assignments were all dropped gets a zero row.  No atomics. */
 moe_status moe_combine(const moe_desc* desc, const void* O, const float* topk_gates,
                        const int32_t* inv_slot, void* Y, void* stream);
 
-/* Steps 1-8 in one call; every intermediate lives in ws (MOE_WS_FORWARD bytes).
+/* Steps 1-8 in one call (the SonicMoE article §3 GPU pipeline, forward
+ * half); every intermediate lives in ws (MOE_WS_FORWARD bytes).
  * Flags: MOE_FLAG_GEMM_TILED / MOE_FLAG_GEMM_SKINNY, MOE_FLAG_TOKEN_ROUNDING. */
 moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
                        const void* W_gate, const void* W_up, const void* W_down, void* Y,

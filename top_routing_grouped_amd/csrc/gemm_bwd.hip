@@ -410,12 +410,6 @@ __global__ __launch_bounds__(kThreads, 1) void alpha_gemm(
 // so a tile has few k-steps.  NST stages of BK rows: on the Qwen3-shaped
 // layer two 64-row stages ran fastest (dW_gate|dW_up 1.31 ms); four or five
 // 32-row stages (more bytes in flight, twice the barriers) were 5-11% slower.
-#ifndef MOE_BETA_NST
-#define MOE_BETA_NST 2
-#endif
-#ifndef MOE_BETA_BK
-#define MOE_BETA_BK 64
-#endif
 template <int NST, int BK>
 struct BetaGeo {
   static constexpr int kOpBytes = BK * kTile * 2;        // one operand tile of a stage
@@ -830,7 +824,8 @@ hipError_t allow_lds(Kern* k, int bytes = kLds) {
 
 int pad64(int E) { return (E + 63) / 64 * 64; }
 
-constexpr int kBNst = MOE_BETA_NST, kBBk = MOE_BETA_BK;
+// two 64-row stages (the measured best; see the stage note at BetaGeo)
+constexpr int kBNst = 2, kBBk = 64;
 constexpr int kBLds = BetaGeo<kBNst, kBBk>::kLds;
 
 }  // namespace

@@ -39,13 +39,8 @@ using f32x4 = float __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;             // 4 waves
 constexpr int kBK = 64;                   // k per stage
-#ifndef SKINNY_NST
-#define SKINNY_NST 4
-#endif
-constexpr int kNST = SKINNY_NST;          // LDS stages
-#ifndef SKINNY_COLS
-#define SKINNY_COLS 256
-#endif
+constexpr int kNST = 4;                   // LDS stages (3 to 8 measured alike)
+constexpr int kSkinnyCols = 256;          // weight columns per workgroup (128-column blocks were slower)
 
 // ROWS rows per pass (ROWS/16 MFMA row blocks): 64, or 32 for batches with at
 // most 16 rows per expert on average (a smaller token tile leaves more LDS to
@@ -270,7 +265,7 @@ template <bool UP, int ROWS>
 hipError_t launch_rows(const Problem& p, const uint16_t* A, const int32_t* perm,
                        const int32_t* offsets, const uint16_t* B0, const uint16_t* B1,
                        uint16_t* C, hipStream_t s) {
-  constexpr int kCols = SKINNY_COLS;
+  constexpr int kCols = kSkinnyCols;
   auto* kern = skinny_gemm_bf16<UP, ROWS, kCols>;
   constexpr int kLds = SkinnyGeo<ROWS, kCols>::kLds;
   const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -473,7 +473,7 @@ moe_status moe_saved_layout_of(const moe_desc* desc, moe_saved_layout* out) {
   return MOE_OK;
 }
 
-const char* moe_status_str(int32_t status) {
+const char* moe_status_str(moe_status status) {
   switch (status) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
