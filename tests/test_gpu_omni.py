@@ -85,6 +85,32 @@ def test_tied_columns_take_the_best_rows_lowest_columns():
     assert np.allclose(f32np(gates), 1.0 / K, atol=GATE_ATOL)
 
 
+def test_hot_experts_are_ranked_by_token_mask():
+    """Every token's strongest row and column are row 3 and column 7, so the
+    atomic expert (3, 7) is chosen by all T tokens and its row and column
+    neighbours by many: segments far longer than 64 entries, ranked through
+    the token mask.  Routing, permutation and Y against the oracle."""
+    T, d, Nr, Nc, K = 3000, 128, 16, 16, 8
+    inp = mi.draw_omni(T, d, Nr, Nc, K, seed=13)
+    X = inp["X"].float()
+    X[:, 0] = 4.0
+    inp["X"] = X.to(torch.bfloat16)
+    for key, col in (("W_r", 3), ("W_c", 7)):
+        W = inp[key].float()
+        W[0, col] = 2.0
+        inp[key] = W.to(torch.bfloat16)
+    dev, ids, gates, ls_r, ls_c, meta, Y = _run(inp, K)
+    lr, lc, rid = _check_route_and_permutation(inp, K, ids, gates, ls_r, ls_c, meta)
+    counts = intnp(meta["counts"])
+    assert counts[3 * Nc + 7] == T
+    assert int((counts > 64).sum()) >= 3
+    a = {k: f32np(inp[k]) for k in ("X", "W_r", "W_c", "W_in", "W_out")}
+    ref = om.forward(a["X"], a["W_r"], a["W_c"], a["W_in"], a["W_out"], K, scores=(lr, lc))
+    Yg = f32np(Y)
+    assert mo.rel_l2(Yg, ref["Y"]) <= TOL["bf16"]
+    assert float(mo.rel_l2_rows(Yg, ref["Y"]).max()) <= TOL["bf16"]
+
+
 def test_repeat_runs_are_bitwise_identical():
     inp = mi.draw_omni(500, 128, 32, 32, 16, seed=4)
     dev, *_, Y1 = _run(inp, 16)

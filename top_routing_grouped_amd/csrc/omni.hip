@@ -392,24 +392,75 @@ __global__ __launch_bounds__(kThreads) void omni_scatter_kernel(const int32_t* _
 
 // One wave per expert: each entry's final place is its rank among the
 // segment's (token*K + k) keys (distinct), i.e. ascending token order.
+// Segments of at most 64 entries: each lane counts the smaller keys directly
+// (c compares per lane).  Longer ones, when T fits the wave's LDS mask
+// (mask_words = ceil(T/32) > 0): an expert occurs at most once per token, so
+// the wave sets one bit per token in a T-bit mask, takes exclusive prefix
+// popcounts over the mask words, and an entry's rank is the prefix of its
+// token's word plus the popcount of the lower bits: O(T/32 + c) per expert
+// instead of O(c^2/64) (a hot expert chosen by most of 32768 tokens would
+// otherwise serialise ~16M loads on one wave).
+constexpr int kRankDirect = 64;
 __global__ __launch_bounds__(kThreads) void omni_rank_kernel(const int32_t* __restrict__ offsets,
                                                              const int32_t* __restrict__ tmp_tk,
                                                              int32_t* __restrict__ perm,
                                                              int32_t* __restrict__ inv, int N,
-                                                             int K) {
+                                                             int K, int mask_words) {
+  extern __shared__ uint32_t rank_lds[];
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int wv = threadIdx.x >> 6;
+  const int e = blockIdx.x * kWaves + wv;
   if (e >= N) return;
   const int off = offsets[e], c = offsets[e + 1] - off;
-  for (int i0 = 0; i0 < c; i0 += 64) {
-    const int i = i0 + lane;
-    const int mine = i < c ? tmp_tk[off + i] : 0x7FFFFFFF;
-    int rank = 0;
-    for (int j = 0; j < c; ++j) rank += tmp_tk[off + j] < mine ? 1 : 0;
-    if (i < c) {
-      perm[off + rank] = mine / K;
-      inv[mine] = off + rank;
+  if (c <= kRankDirect || mask_words == 0) {
+    for (int i0 = 0; i0 < c; i0 += 64) {
+      const int i = i0 + lane;
+      const int mine = i < c ? tmp_tk[off + i] : 0x7FFFFFFF;
+      int rank = 0;
+      for (int j = 0; j < c; ++j) rank += tmp_tk[off + j] < mine ? 1 : 0;
+      if (i < c) {
+        perm[off + rank] = mine / K;
+        inv[mine] = off + rank;
+      }
     }
+    return;
+  }
+  uint32_t* mask = rank_lds + (size_t)wv * 2 * mask_words;
+  uint32_t* pre = mask + mask_words;
+  for (int j = lane; j < mask_words; j += 64) mask[j] = 0u;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  for (int i = lane; i < c; i += 64) {
+    const int t = tmp_tk[off + i] / K;
+    atomicOr(&mask[t >> 5], 1u << (t & 31));
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  // lane l owns words [l*chunk, (l+1)*chunk): its popcount total, a wave
+  // exclusive scan of the totals, then the per-word prefixes
+  const int chunk = (mask_words + 63) / 64;
+  const int w0 = lane * chunk, w1 = (w0 + chunk < mask_words) ? w0 + chunk : mask_words;
+  int own = 0;
+  for (int j = w0; j < w1; ++j) own += __popc(mask[j]);
+  int x = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    x += lane >= o ? y : 0;
+  }
+  int run = x - own;
+  for (int j = w0; j < w1; ++j) {
+    pre[j] = (uint32_t)run;
+    run += __popc(mask[j]);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  for (int i = lane; i < c; i += 64) {
+    const int key = tmp_tk[off + i];
+    const int t = key / K;
+    const int rank = (int)pre[t >> 5] + __popc(mask[t >> 5] & ((1u << (t & 31)) - 1u));
+    perm[off + rank] = t;
+    inv[key] = off + rank;
   }
 }
 
@@ -641,8 +692,13 @@ hipError_t launch_omni_permute(const OmniProblem& p, const int32_t* ids, int32_t
   hipLaunchKernelGGL(omni_scatter_kernel, dim3(gTK), dim3(kThreads), 0, s, ids, w.cursor,
                      w.tmp_tk, TK);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  // the token mask of long segments: 2 * ceil(T/32) words per wave, used
+  // while it keeps a workgroup within 64 KB of LDS (T <= 65536)
+  int mask_words = (int)((p.T + 31) / 32);
+  if ((size_t)kWaves * 2 * mask_words * sizeof(uint32_t) > 64 * 1024) mask_words = 0;
   hipLaunchKernelGGL(omni_rank_kernel, dim3((unsigned)((N + kWaves - 1) / kWaves)),
-                     dim3(kThreads), 0, s, offsets, w.tmp_tk, perm, inv, N, p.K);
+                     dim3(kThreads), (size_t)kWaves * 2 * mask_words * sizeof(uint32_t), s, offsets,
+                     w.tmp_tk, perm, inv, N, p.K, mask_words);
   return hipGetLastError();
 }
 
