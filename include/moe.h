@@ -87,9 +87,14 @@ typedef struct {
  * per expert (T*K <= 64*E, e.g. decode) runs the weight-streaming kernels --
  * one workgroup per expert and column block, reading each active expert's
  * weights once per 64 rows -- and larger batches run the 256x256-tiled
- * kernels.  Both give results within the documented tolerance of each other
- * (they round the same fp32 sums; summation order differs).  The skinny
- * kernels need no tile table: MOE_FLAG_TILE_TABLE_READY is then ignored. */
+ * kernels, whose launch also computes every expert of at most 64 rows with a
+ * weight-streaming block instead of its mostly empty tile (a skewed router
+ * leaves many such experts beside a few full ones).  MOE_FLAG_GEMM_TILED
+ * runs every expert by tiles; MOE_FLAG_GEMM_SKINNY every expert by weight
+ * streaming.  All give results within the documented tolerance of each
+ * other (they round the same fp32 sums; summation order differs).  The
+ * skinny kernels need no tile table: MOE_FLAG_TILE_TABLE_READY is then
+ * ignored. */
 #define MOE_FLAG_GEMM_TILED 2u
 #define MOE_FLAG_GEMM_SKINNY 4u
 

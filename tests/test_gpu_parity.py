@@ -154,6 +154,53 @@ def test_gemm_paths_agree_on_skewed_decode():
     assert mo.rel_l2(f32np(res_s["O"])[:N], f32np(res_t["O"])[:N]) <= TOL["bf16"]
 
 
+# Expert sizes set by hand around the bound up to which a tiled launch hands an
+# expert to a weight-streaming block (64 rows): empty, 1, 2, 33, 63, 64 (all
+# streamed), 65 (one partial tile), 256, 257, 300, 512 (one and more tiles).
+STREAM_COUNTS = [64, 65, 0, 1, 63, 300, 256, 257, 33, 512, 2, 64]
+
+
+@pytest.mark.parametrize("d,n", [(256, 320), (512, 192)])
+def test_tiled_launch_streams_small_experts(d, n):
+    """moe_grouped_ffn with default flags on hand-made metadata: every expert
+    segment of H and O against the oracle; experts above 64 rows bit-equal to
+    the tiles-only launch (MOE_FLAG_GEMM_TILED), experts of at most 64 rows
+    bit-equal to the weight-streaming launch (MOE_FLAG_GEMM_SKINNY: the same
+    per-element MFMA sums, on 4 instead of 8 waves)."""
+    T, K, E = 700, 3, len(STREAM_COUNTS)
+    print(f"case streamed experts T={T} d={d} E={E} K={K} n={n}", flush=True)
+    inp = mi.draw(T, d, E, n, torch.bfloat16, seed=23)
+    rng = np.random.default_rng(23)
+    offsets = np.concatenate([[0], np.cumsum(STREAM_COUNTS)]).astype(np.int32)
+    perm = np.concatenate([np.sort(rng.choice(T, size=c, replace=False)) for c in STREAM_COUNTS])
+    assert offsets[-1] <= T * K and T * K > 64 * E      # tiled launch by default
+    dev = device_inputs(inp)
+    off_d = torch.from_numpy(offsets).cuda()
+    perm_d = torch.from_numpy(perm.astype(np.int32)).cuda()
+    outs = {}
+    for path in ("auto", "tiled", "skinny"):
+        desc = moe.make_desc(T, d, E, K, n, "bf16", 0.0, flags=GEMM_PATHS[path])
+        outs[path] = moe.grouped_ffn(desc, dev["X"], off_d, perm_d, dev["W_gate"], dev["W_up"],
+                                     dev["W_down"])
+    torch.cuda.synchronize()
+    X32 = f32np(inp["X"])
+    Wg, Wu, Wd = (f32np(inp[k]) for k in ("W_gate", "W_up", "W_down"))
+    H, O = (t.cpu() for t in outs["auto"])
+    for e, c in enumerate(STREAM_COUNTS):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if c == 0:
+            continue
+        h, o = mo.expert_ffn(X32[perm[lo:hi]], Wg[e], Wu[e], Wd[e])
+        for name, got, want in (("H", H[lo:hi], h), ("O", O[lo:hi], o)):
+            rows = mo.rel_l2_rows(got.to(torch.float64).numpy(), want)
+            assert rows.max() <= TOL["bf16"], f"{name} expert {e} ({c} rows): {rows.max():.3e}"
+        other = "skinny" if c <= 64 else "tiled"
+        for i, name in enumerate(("H", "O")):
+            ref_rows = outs[other][i][lo:hi].cpu()
+            got = (H, O)[i][lo:hi]
+            assert torch.equal(got, ref_rows), f"{name} expert {e} ({c} rows) differs from {other}"
+
+
 def test_zero_router_gives_lowest_ids_and_uniform_gates():
     inp = mi.draw(300, 128, 16, 128, torch.bfloat16, seed=1)
     inp["W_r"] = torch.zeros_like(inp["W_r"])

@@ -40,7 +40,7 @@
 //   it about 2% and 6% faster).
 // * Workgroup ids are remapped so that consecutive tiles (same expert, same
 //   token rows) run on the same XCD and share its L2.
-#include "moe_internal.hpp"
+#include "gemm_stream.hpp"
 
 namespace moe {
 namespace {
@@ -89,6 +89,12 @@ constexpr int kWGM = 2, kWGN = 4, kWTB = 4, kWCB = 2;
 constexpr int kNST = 2, kBK = 64;
 using ProdGeo = Geo<kWGM, kWGN, kWTB, kWCB, kNST, kBK>;
 static_assert(ProdGeo::BM == kGemmBM, "tile table rows must match the kernel tile");
+// Weight-streaming blocks appended to a launch: passes of kStreamRows rows,
+// kStreamCols weight columns per block, the tile kernel's 8 waves.
+constexpr int kStreamRows = 64, kStreamCols = 256;
+using StreamGeo = wstream::Geo<kStreamRows, kStreamCols, kWGM * kWGN>;
+static_assert(StreamGeo::kThreads == ProdGeo::kThreads, "one workgroup size for both kinds");
+static_assert(kMaxStreamRows <= kGemmBM, "a streamed expert must be a single tile");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -126,7 +132,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_bf16(
     const uint16_t* __restrict__ B1,      // up: W_up
     uint16_t* __restrict__ C,             // up: H [rows][N]; down: O [rows][N]
     uint16_t* __restrict__ Hpre,          // up, or NULL: pre-activations [rows][2N] (gate | up)
-    int64_t T, int Kd, int N, int NT) {
+    int64_t T, int Kd, int N, int NT,
+    const int32_t* __restrict__ offsets,  // [E+1] expert row ranges (weight-streaming blocks)
+    int64_t rows_max, int stream_rows, int stream_base) {
   using G = Geo<WGM, WGN, WTB, WCB, NST, BK>;
   constexpr int kCpr = G::kCpr, kSh = G::kSh, kRowsPerCopy = 64 / kCpr;
   constexpr int KS = BK / 16;              // 16-deep MFMA sub-steps per stage
@@ -135,6 +143,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_bf16(
   constexpr int kStages = NST;
   constexpr int kHalf = WCB / 2;           // up: gate blocks (then as many up blocks)
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+  // Workgroups from stream_base on are weight-streaming blocks: expert
+  // bid / NB, column block bid % NB, for the experts with 1..stream_rows
+  // rows (the tiles of those experts exit below).  They come after every
+  // tile, so the dispatcher starts them on the CUs that tiles leave free.
+  if (stream_rows > 0 && (int)blockIdx.x >= stream_base) {
+    constexpr int kCols = UP ? kStreamCols / 2 : kStreamCols;
+    const int NB = (N + kCols - 1) / kCols;
+    const int idx = (int)blockIdx.x - stream_base;
+    wstream::stream_block<UP, kStreamRows, kStreamCols, WGM * WGN>(
+        A, perm, offsets, B0, B1, C, T, Kd, N, rows_max, stream_rows, idx / NB, idx - (idx / NB) * NB,
+        smem);
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,6 +194,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_bf16(
   const int32_t* ent = table + 4 * (mt + 1);
   const int e = tile_expert((uint32_t)ent[0]), row0 = ent[1];
   const int nrows = ent[2] - row0;
+  // an expert of at most stream_rows rows (one tile) is a weight-streaming block's
+  if (c == 1 && nrows <= stream_rows) return;
   const int ncol0 = nt * (UP ? BN / 2 : BN);   // first output column of the tile
   // 32-row token blocks of this wave that hold any valid row (uniform per wave)
   int ntb = (nrows - wm * (WTB * 32) + 31) / 32;
@@ -433,17 +457,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_bf16(
   }
 }
 
+// stream_rows > 0 (needs offsets): experts with 1..stream_rows rows run as
+// weight-streaming blocks appended to the grid, E * NB of them.
 template <bool UP>
 hipError_t launch_bf16(const uint16_t* A, const int32_t* perm, const int32_t* table,
                        const uint16_t* B0, const uint16_t* B1, uint16_t* C, uint16_t* Hpre,
-                       int64_t T, int Kd, int N, int64_t mtiles, hipStream_t s) {
+                       int64_t T, int Kd, int N, int64_t mtiles, int E, const int32_t* offsets,
+                       int64_t rows_max, int stream_rows, hipStream_t s) {
+  if (stream_rows < 0 || stream_rows > kMaxStreamRows || (stream_rows > 0 && !offsets))
+    return hipErrorInvalidValue;
   const int NT = (N + (UP ? BN / 2 : BN) - 1) / (UP ? BN / 2 : BN);
+  const int64_t tiles = mtiles * NT;
+  const int NB = (N + (UP ? kStreamCols / 2 : kStreamCols) - 1) / (UP ? kStreamCols / 2 : kStreamCols);
+  const int64_t grid = tiles + (stream_rows > 0 ? (int64_t)E * NB : 0);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const int lds = (stream_rows > 0 && StreamGeo::kLds > ProdGeo::kLds) ? StreamGeo::kLds : ProdGeo::kLds;
   auto* kern = grouped_gemm_bf16<UP, kWGM, kWGN, kWTB, kWCB, kNST, kBK>;
   hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, ProdGeo::kLds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(mtiles * NT)), dim3(ProdGeo::kThreads),
-                     (size_t)ProdGeo::kLds, s, A, perm, table, B0, B1, C, Hpre, T, Kd, N, NT);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(ProdGeo::kThreads), (size_t)lds, s, A, perm,
+                     table, B0, B1, C, Hpre, T, Kd, N, NT, offsets, rows_max, stream_rows,
+                     (int)tiles);
   return hipGetLastError();
 }
 
@@ -528,12 +563,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
 
 hipError_t launch_gemm_up(const Problem& p, const void* X, const int32_t* perm,
                           const int32_t* table, const void* W_gate, const void* W_up, void* H,
-                          hipStream_t s, void* Hpre) {
+                          hipStream_t s, void* Hpre, const int32_t* offsets, int stream_rows) {
   const int64_t mtiles = max_row_tiles(p, kGemmBM);
-  if (p.bf16)
+  if (p.bf16) {
+    if (Hpre && stream_rows) return hipErrorInvalidValue;   // streamed rows store no pre-activations
     return launch_bf16<true>((const uint16_t*)X, perm, table, (const uint16_t*)W_gate,
                              (const uint16_t*)W_up, (uint16_t*)H, (uint16_t*)Hpre, p.T, p.d, p.n,
-                             mtiles, s);
+                             mtiles, p.E, offsets, p.rows_max, stream_rows, s);
+  }
   if (Hpre) return hipErrorNotSupported;      // the training path is bf16 only
   const int NT = (p.n + 63) / 64;
   hipLaunchKernelGGL(grouped_gemm_f32<true>, dim3((unsigned)(mtiles * kF32Sub * NT)), dim3(256), 0, s,
@@ -543,11 +580,13 @@ hipError_t launch_gemm_up(const Problem& p, const void* X, const int32_t* perm,
 }
 
 hipError_t launch_gemm_down(const Problem& p, const void* H, const int32_t* table,
-                            const void* W_down, void* O, hipStream_t s) {
+                            const void* W_down, void* O, hipStream_t s, const int32_t* offsets,
+                            int stream_rows) {
   const int64_t mtiles = max_row_tiles(p, kGemmBM);
   if (p.bf16)
     return launch_bf16<false>((const uint16_t*)H, nullptr, table, (const uint16_t*)W_down,
-                              nullptr, (uint16_t*)O, nullptr, p.T, p.n, p.d, mtiles, s);
+                              nullptr, (uint16_t*)O, nullptr, p.T, p.n, p.d, mtiles, p.E, offsets,
+                              p.rows_max, stream_rows, s);
   const int NT = (p.d + 63) / 64;
   hipLaunchKernelGGL(grouped_gemm_f32<false>, dim3((unsigned)(mtiles * kF32Sub * NT)), dim3(256), 0, s,
                      (const float*)H, nullptr, table, (const float*)W_down, nullptr, (float*)O,

@@ -69,6 +69,13 @@ bool skinny(const moe::Problem& p, const moe_desc* d) {
   return moe::use_skinny(p, d->flags, MOE_FLAG_GEMM_TILED, MOE_FLAG_GEMM_SKINNY);
 }
 
+// Rows up to which an expert of a tiled bf16 launch is computed by a
+// weight-streaming block instead of its tile (0: every expert by tiles, as
+// MOE_FLAG_GEMM_TILED asks).
+int stream_rows(const moe::Problem& p, const moe_desc* d) {
+  return (p.bf16 && !(d->flags & MOE_FLAG_GEMM_TILED)) ? moe::kMaxStreamRows : 0;
+}
+
 moe::Problem make_problem(const moe_desc* d) {
   moe::Problem p;
   p.T = d->T;
@@ -617,7 +624,8 @@ moe_status moe_grouped_gemm_up(const moe_desc* desc, const void* X, const int32_
   int32_t* table = static_cast<int32_t*>(ws);
   if (!(desc->flags & MOE_FLAG_TILE_TABLE_READY))
     MOE_TRY(hip_status(moe::launch_tile_table(p, offsets, table, s), "tile table launch"));
-  return hip_status(moe::launch_gemm_up(p, X, perm_token, table, W_gate, W_up, H, s),
+  return hip_status(moe::launch_gemm_up(p, X, perm_token, table, W_gate, W_up, H, s, nullptr,
+                                        offsets, stream_rows(p, desc)),
                     "grouped GEMM (up) launch");
 }
 
@@ -638,7 +646,8 @@ moe_status moe_grouped_gemm_down(const moe_desc* desc, const void* H, const int3
   int32_t* table = static_cast<int32_t*>(ws);
   if (!(desc->flags & MOE_FLAG_TILE_TABLE_READY))
     MOE_TRY(hip_status(moe::launch_tile_table(p, offsets, table, s), "tile table launch"));
-  return hip_status(moe::launch_gemm_down(p, H, table, W_down, O, s), "grouped GEMM (down) launch");
+  return hip_status(moe::launch_gemm_down(p, H, table, W_down, O, s, offsets, stream_rows(p, desc)),
+                    "grouped GEMM (down) launch");
 }
 
 moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* offsets,
@@ -664,9 +673,12 @@ moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* o
   int32_t* table = static_cast<int32_t*>(ws);
   if (!(desc->flags & MOE_FLAG_TILE_TABLE_READY))
     MOE_TRY(hip_status(moe::launch_tile_table(p, offsets, table, s), "tile table launch"));
-  MOE_TRY(hip_status(moe::launch_gemm_up(p, X, perm_token, table, W_gate, W_up, H, s),
+  const int sr = stream_rows(p, desc);
+  MOE_TRY(hip_status(moe::launch_gemm_up(p, X, perm_token, table, W_gate, W_up, H, s, nullptr,
+                                         offsets, sr),
                      "grouped GEMM (up) launch"));
-  return hip_status(moe::launch_gemm_down(p, H, table, W_down, O, s), "grouped GEMM (down) launch");
+  return hip_status(moe::launch_gemm_down(p, H, table, W_down, O, s, offsets, sr),
+                    "grouped GEMM (down) launch");
 }
 
 moe_status moe_combine(const moe_desc* desc, const void* O, const float* topk_gates,
@@ -714,9 +726,11 @@ moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, con
     MOE_TRY(hip_status(moe::launch_gemm_down_skinny(p, w.H, w.offsets, W_down, w.O, s),
                        "grouped GEMM (down, weight-streaming) launch"));
   } else {
-    MOE_TRY(hip_status(moe::launch_gemm_up(p, X, w.perm, w.table, W_gate, W_up, w.H, s),
+    const int sr = stream_rows(p, desc);
+    MOE_TRY(hip_status(moe::launch_gemm_up(p, X, w.perm, w.table, W_gate, W_up, w.H, s, nullptr,
+                                           w.offsets, sr),
                        "grouped GEMM (up) launch"));
-    MOE_TRY(hip_status(moe::launch_gemm_down(p, w.H, w.table, W_down, w.O, s),
+    MOE_TRY(hip_status(moe::launch_gemm_down(p, w.H, w.table, W_down, w.O, s, w.offsets, sr),
                        "grouped GEMM (down) launch"));
   }
   return hip_status(moe::launch_combine(p, w.O, w.gates, w.inv, Y, s), "combine launch");

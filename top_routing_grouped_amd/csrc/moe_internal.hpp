@@ -138,12 +138,18 @@ constexpr size_t kNoallocScratchBytes = (size_t)2 << 20;
 hipError_t noalloc_scratch(void** out);
 
 // Hpre (bf16 only, may be NULL): also store the pre-activations [rows][2n]
-// (x W_gate | x W_up) for the backward.
+// (x W_gate | x W_up) for the backward.  stream_rows (bf16 only, 0 or
+// 1..kMaxStreamRows, needs offsets; not with Hpre): the experts with at most
+// that many rows are computed by weight-streaming blocks in the same launch
+// instead of by their (single, mostly empty) tile.
+constexpr int kMaxStreamRows = 64;
 hipError_t launch_gemm_up(const Problem& p, const void* X, const int32_t* perm,
                           const int32_t* table, const void* W_gate, const void* W_up, void* H,
-                          hipStream_t s, void* Hpre = nullptr);
+                          hipStream_t s, void* Hpre = nullptr, const int32_t* offsets = nullptr,
+                          int stream_rows = 0);
 hipError_t launch_gemm_down(const Problem& p, const void* H, const int32_t* table,
-                            const void* W_down, void* O, hipStream_t s);
+                            const void* W_down, void* O, hipStream_t s,
+                            const int32_t* offsets = nullptr, int stream_rows = 0);
 
 // Weight-streaming grouped GEMMs for few rows per expert (one workgroup per
 // expert and column block; no tile table).
