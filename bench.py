@@ -65,7 +65,8 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "MoE-layer fwd tokens/s; grouped-GEMM MFMA util; permute/combine HBM GB/s"
 DEFAULT_WORKLOAD = "qwen3_bf16"
 FLUSH_BYTES = 1 << 30
-GEMM_SOURCES = ("top_routing_grouped_amd/csrc/gemm.hip", "top_routing_grouped_amd/csrc/moe_internal.hpp")
+GEMM_SOURCES = ("top_routing_grouped_amd/csrc/gemm.hip", "top_routing_grouped_amd/csrc/gemm_stream.hpp",
+                "top_routing_grouped_amd/csrc/moe_internal.hpp")
 TRAFFIC_FILE = "profiles/gemm_up_traffic_{workload}.json"
 UP_KERNEL = "grouped_gemm_bf16<true"
 
