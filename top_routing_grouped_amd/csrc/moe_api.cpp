@@ -408,11 +408,14 @@ moe_status moe_omni_forward(const moe_omni_desc* desc, const void* X, const void
   hipStream_t s = (hipStream_t)stream;
   moe::OmniRouteWs rw;
   moe::omni_route_ws_bytes(p, &rw, w.route);
-  MOE_TRY(hip_status(moe::launch_omni_route(p, X, W_r, W_c, nullptr, nullptr, w.ids, w.gates, rw, s),
+  // the selection counts the entries per expert, so the permutation does not
+  MOE_TRY(hip_status(moe::launch_omni_route(p, X, W_r, W_c, nullptr, nullptr, w.ids, w.gates, rw, s,
+                                            w.counts),
                      "atomic-expert router launch"));
   moe::OmniPermuteWs pw;
   moe::omni_permute_ws_bytes(p, &pw, w.permute);
-  MOE_TRY(hip_status(moe::launch_omni_permute(p, w.ids, w.counts, w.offsets, w.perm, w.inv, pw, s),
+  MOE_TRY(hip_status(moe::launch_omni_permute(p, w.ids, w.counts, w.offsets, w.perm, w.inv, pw, s,
+                                              true),
                      "atomic-expert permutation launch"));
   return hip_status(moe::launch_omni_experts(p, X, W_in, W_out, w.ids, w.gates, w.offsets, w.perm,
                                              w.inv, w.a, Y, s),

@@ -98,9 +98,13 @@ hipError_t launch_route(const Problem& p, const void* X, const void* W_r, const 
                         int32_t* blockcnt = nullptr);
 // The fp32 scores X W1 and X W2 of the same bf16 tokens in one launch (no
 // bias, no selection); both widths must be multiples of 8 and at most 256.
+// When the token blocks alone would leave CUs idle, each axis wider than 128
+// is computed by two groups of workgroups (128 columns each).  zero
+// (optional): zero_n int32s that the launch also clears.
 bool route_pair_supported(int E1, int E2);
 hipError_t launch_logits_pair(int64_t T, int d, int E1, int E2, const void* X, const void* W1,
-                              const void* W2, float* logits1, float* logits2, hipStream_t s);
+                              const void* W2, float* logits1, float* logits2, hipStream_t s,
+                              int32_t* zero = nullptr, int zero_n = 0);
 
 hipError_t launch_histogram(const Problem& p, const int32_t* ids, int32_t* blockcnt,
                             hipStream_t s);
@@ -188,16 +192,18 @@ struct OmniRouteWs {
 struct OmniPermuteWs {
   int32_t* cursor;      // [N] fill position of each expert's segment
   int32_t* tmp_tk;      // [T*K] entries in arrival order
-  int32_t* bsum;        // [64] per-workgroup count sums of the scan
 };
 size_t omni_route_ws_bytes(const OmniProblem& p, OmniRouteWs* w, unsigned char* base);
 size_t omni_permute_ws_bytes(const OmniProblem& p, OmniPermuteWs* w, unsigned char* base);
+// counts (optional): the selection also counts each expert's entries into
+// it (cleared first), so that the permutation can skip its own count
+// (launch_omni_permute with counted = true).
 hipError_t launch_omni_route(const OmniProblem& p, const void* X, const void* W_r, const void* W_c,
                              float* ls_r, float* ls_c, int32_t* ids, float* gates,
-                             const OmniRouteWs& w, hipStream_t s);
+                             const OmniRouteWs& w, hipStream_t s, int32_t* counts = nullptr);
 hipError_t launch_omni_permute(const OmniProblem& p, const int32_t* ids, int32_t* counts,
                                int32_t* offsets, int32_t* perm, int32_t* inv,
-                               const OmniPermuteWs& w, hipStream_t s);
+                               const OmniPermuteWs& w, hipStream_t s, bool counted = false);
 hipError_t launch_omni_experts(const OmniProblem& p, const void* X, const void* W_in,
                                const void* W_out, const int32_t* ids, const float* gates,
                                const int32_t* offsets, const int32_t* perm, const int32_t* inv,

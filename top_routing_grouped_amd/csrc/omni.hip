@@ -219,7 +219,7 @@ __device__ __forceinline__ void wave_top(const uint32_t* k, const int* id, int r
 __global__ __launch_bounds__(kThreads) void omni_select_kernel(
     const float* __restrict__ p_r, const float* __restrict__ p_c, float* __restrict__ ls_r,
     float* __restrict__ ls_c, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
-    int Nr, int Nc, int K) {
+    int Nr, int Nc, int K, int32_t* __restrict__ counts) {
   __shared__ int ckey[kWaves][kMaxCand];
   __shared__ int cid[kWaves][kMaxCand];
   __shared__ int tk[kWaves][128];
@@ -284,6 +284,7 @@ __global__ __launch_bounds__(kThreads) void omni_select_kernel(
   if (lane < K) {
     ids[t * K + lane] = sid;
     gates[t * K + lane] = ex / z;
+    if (counts) atomicAdd(&counts[sid], 1);   // the permutation's counts (cleared by the router launch)
   }
 }
 
@@ -300,18 +301,20 @@ __global__ __launch_bounds__(kThreads) void omni_count_kernel(const int32_t* __r
   if (i < TK) atomicAdd(&counts[ids[i]], 1);
 }
 
-// Exclusive scan over N <= 65536 counts in two launches of N/1024
-// workgroups: block sums, then each block adds the sums before it and scans
-// its own 1024 counts (thread q owns 4 consecutive ones: coalesced 16-byte
-// accesses).
-constexpr int kScanBlock = 4 * kThreads;
-__device__ __forceinline__ void load4(const int32_t* p, int base, int N, int v[4]) {
-  if (base + 3 < N) {
-    const int4 q = *reinterpret_cast<const int4*>(p + base);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+// Exclusive scan over N counts in one launch without any wait between
+// workgroups: workgroup b owns counts [4096b, 4096b + 4096), four per thread
+// (16-byte loads; a wave reads 1 KB contiguous).  It sums every count before
+// its range itself (at most 240 KB of L2 reads at N = 65536, spread over its
+// 1024 threads), then scans its own counts: wave scans of the threads' sums,
+// the 16 wave totals through LDS.  The last workgroup also writes offsets[N].
+constexpr int kScanThreads = 1024, kScanWaves = kScanThreads / 64, kScanBlock = 4 * kScanThreads;
+__device__ __forceinline__ void load4(const int32_t* p, int i, int N, int v[4]) {
+  if (i + 3 < N) {
+    const int4 c = *reinterpret_cast<const int4*>(p + i);
+    v[0] = c.x; v[1] = c.y; v[2] = c.z; v[3] = c.w;
   } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = base + r < N ? p[base + r] : 0;
+    for (int r = 0; r < 4; ++r) v[r] = (i + r < N) ? p[i + r] : 0;
   }
 }
 __device__ __forceinline__ int wave_sum_i(int x) {
@@ -319,33 +322,23 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
-
-__global__ __launch_bounds__(kThreads) void omni_blocksum_kernel(const int32_t* __restrict__ counts,
-                                                                 int32_t* __restrict__ bsum, int N) {
-  __shared__ int tmp[kWaves];
-  int v[4];
-  load4(counts, blockIdx.x * kScanBlock + 4 * threadIdx.x, N, v);
-  const int s = wave_sum_i(v[0] + v[1] + v[2] + v[3]);
-  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) bsum[blockIdx.x] = (tmp[0] + tmp[1]) + (tmp[2] + tmp[3]);
-}
-
-__global__ __launch_bounds__(kThreads) void omni_scan_kernel(const int32_t* __restrict__ counts,
-                                                             const int32_t* __restrict__ bsum,
-                                                             int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ cursor, int N) {
-  __shared__ int tmp[kWaves];
-  __shared__ int carry_sh;
+__global__ __launch_bounds__(kScanThreads) void omni_scan_kernel(const int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ cursor, int N) {
+  __shared__ int part[kScanWaves], wtot[kScanWaves];
   const int q = threadIdx.x, lane = q & 63, w = q >> 6;
-  const int b = blockIdx.x;
-  if (w == 0) {                                   // blocks before this one (b <= 64)
-    const int c = wave_sum_i(lane < b ? bsum[lane] : 0);
-    if (lane == 0) carry_sh = c;
+  const int b = blockIdx.x, i0 = b * kScanBlock;
+  // counts before this workgroup's range
+  int pre = 0;
+  for (int j = 0; j < b; ++j) {
+    int v[4];
+    load4(counts, j * kScanBlock + 4 * q, N, v);
+    pre += (v[0] + v[1]) + (v[2] + v[3]);
   }
-  const int base = b * kScanBlock + 4 * q;
+  pre = wave_sum_i(pre);
+  // this range
   int v[4];
-  load4(counts, base, N, v);
+  load4(counts, i0 + 4 * q, N, v);
   const int mine = (v[0] + v[1]) + (v[2] + v[3]);
   int x = mine;
 #pragma unroll
@@ -353,31 +346,40 @@ __global__ __launch_bounds__(kThreads) void omni_scan_kernel(const int32_t* __re
     const int y = __shfl_up(x, o);
     x += lane >= o ? y : 0;
   }
-  if (lane == 63) tmp[w] = x;
+  if (lane == 63) {
+    part[w] = pre;
+    wtot[w] = x;
+  }
   __syncthreads();
-  int before = carry_sh, total = 0;
+  int run = x - mine, total = 0;
 #pragma unroll
-  for (int j = 0; j < kWaves; ++j) {
-    total += tmp[j];
-    before += j < w ? tmp[j] : 0;
+  for (int j = 0; j < kScanWaves; ++j) {
+    run += part[j] + (j < w ? wtot[j] : 0);
+    total += wtot[j];
   }
   int o[4];
-  o[0] = before + x - mine;
+  o[0] = run;
   o[1] = o[0] + v[0];
   o[2] = o[1] + v[1];
   o[3] = o[2] + v[2];
-  if (base + 3 < N) {
-    *reinterpret_cast<int4*>(offsets + base) = int4{o[0], o[1], o[2], o[3]};
-    *reinterpret_cast<int4*>(cursor + base) = int4{o[0], o[1], o[2], o[3]};
+  const int i = i0 + 4 * q;
+  if (i + 3 < N) {
+    *reinterpret_cast<int4*>(offsets + i) = int4{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<int4*>(cursor + i) = int4{o[0], o[1], o[2], o[3]};
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (base + r < N) {
-        offsets[base + r] = o[r];
-        cursor[base + r] = o[r];
+      if (i + r < N) {
+        offsets[i + r] = o[r];
+        cursor[i + r] = o[r];
       }
   }
-  if (b == (int)gridDim.x - 1 && q == 0) offsets[N] = carry_sh + total;
+  if (b == (int)gridDim.x - 1 && q == 0) {
+    int all = 0;
+#pragma unroll
+    for (int j = 0; j < kScanWaves; ++j) all += part[j];
+    offsets[N] = all + total;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void omni_scatter_kernel(const int32_t* __restrict__ ids,
@@ -642,14 +644,14 @@ size_t omni_permute_ws_bytes(const OmniProblem& p, OmniPermuteWs* w, unsigned ch
   OmniPermuteWs ws{};
   ws.cursor = reinterpret_cast<int32_t*>(take((size_t)p.Nr * p.Nc * 4));
   ws.tmp_tk = reinterpret_cast<int32_t*>(take((size_t)p.T * p.K * 4));
-  ws.bsum = reinterpret_cast<int32_t*>(take(64 * 4));
   if (w) *w = ws;
   return off;
 }
 
 hipError_t launch_omni_route(const OmniProblem& p, const void* X, const void* W_r, const void* W_c,
                              float* ls_r, float* ls_c, int32_t* ids, float* gates,
-                             const OmniRouteWs& w, hipStream_t s) {
+                             const OmniRouteWs& w, hipStream_t s, int32_t* counts) {
+  const int N = p.Nr * p.Nc;
   // the two axis projections: the router GEMM with fp32 logits out.  Both in
   // one launch where the widths allow it (twice the workgroups of one axis,
   // which alone fills a quarter of the chip at T = 4096); otherwise one
@@ -657,9 +659,16 @@ hipError_t launch_omni_route(const OmniProblem& p, const void* X, const void* W_
   // (no k split: its extra selection pass costs more than it saves here)
   hipError_t err;
   if (route_pair_supported(p.Nr, p.Nc)) {
-    err = launch_logits_pair(p.T, p.d, p.Nr, p.Nc, X, W_r, W_c, w.p_r, w.p_c, s);
+    // the launch also clears the counts that the selection below adds to
+    err = launch_logits_pair(p.T, p.d, p.Nr, p.Nc, X, W_r, W_c, w.p_r, w.p_c, s, counts,
+                             counts ? N : 0);
     if (err != hipSuccess) return err;
   } else {
+    if (counts) {
+      hipLaunchKernelGGL(omni_zero_kernel, dim3((unsigned)((N + kThreads - 1) / kThreads)),
+                         dim3(kThreads), 0, s, counts, (int64_t)N);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
     err = launch_route(axis_problem(p, p.Nr), X, W_r, nullptr, w.p_r, w.ids1, w.gates1, nullptr, s);
     if (err != hipSuccess) return err;
     err = launch_route(axis_problem(p, p.Nc), X, W_c, nullptr, w.p_c, w.ids1, w.gates1, nullptr, s);
@@ -667,27 +676,26 @@ hipError_t launch_omni_route(const OmniProblem& p, const void* X, const void* W_
   }
   hipLaunchKernelGGL(omni_select_kernel, dim3((unsigned)((p.T + kWaves - 1) / kWaves)),
                      dim3(kThreads), 0, s, w.p_r, w.p_c, ls_r, ls_c, ids, gates, p.T, p.Nr, p.Nc,
-                     p.K);
+                     p.K, counts);
   return hipGetLastError();
 }
 
 hipError_t launch_omni_permute(const OmniProblem& p, const int32_t* ids, int32_t* counts,
                                int32_t* offsets, int32_t* perm, int32_t* inv,
-                               const OmniPermuteWs& w, hipStream_t s) {
+                               const OmniPermuteWs& w, hipStream_t s, bool counted) {
   const int N = p.Nr * p.Nc;
   const int64_t TK = p.T * (int64_t)p.K;
   const unsigned gN = (unsigned)((N + kThreads - 1) / kThreads);
   const unsigned gTK = (unsigned)((TK + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(omni_zero_kernel, dim3(gN), dim3(kThreads), 0, s, counts, (int64_t)N);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(omni_count_kernel, dim3(gTK), dim3(kThreads), 0, s, ids, counts, TK);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  const unsigned nb = (unsigned)((N + kScanBlock - 1) / kScanBlock);
-  hipLaunchKernelGGL(omni_blocksum_kernel, dim3(nb), dim3(kThreads), 0, s, counts, w.bsum, N);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(omni_scan_kernel, dim3(nb), dim3(kThreads), 0, s, counts, w.bsum, offsets,
-                     w.cursor, N);
+  hipError_t err;
+  if (!counted) {
+    hipLaunchKernelGGL(omni_zero_kernel, dim3(gN), dim3(kThreads), 0, s, counts, (int64_t)N);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(omni_count_kernel, dim3(gTK), dim3(kThreads), 0, s, ids, counts, TK);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(omni_scan_kernel, dim3((unsigned)((N + kScanBlock - 1) / kScanBlock)),
+                     dim3(kScanThreads), 0, s, counts, offsets, w.cursor, N);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(omni_scatter_kernel, dim3(gTK), dim3(kThreads), 0, s, ids, w.cursor,
                      w.tmp_tk, TK);

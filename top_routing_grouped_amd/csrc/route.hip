@@ -461,12 +461,32 @@ __device__ __forceinline__ void wait_stages(int pending) {
 // block (for batches too small to fill the chip): each writes its raw fp32
 // partial scores to partial[ks][T][Epad]; route_sum_kernel and
 // route_select_kernel finish.
+// Router matrices over the same tokens that share one launch (fp32 scores
+// only, no bias or selection): job j takes workgroups j*nblk .. (j+1)*nblk-1,
+// multiplying X by E[j] columns of a matrix whose rows (and score rows) are
+// ld[j] wide.  n = 0: the launch is one ordinary router.  zero (optional):
+// zero_n int32s cleared by the launch, a slice per workgroup.
+struct RouteJobs {
+  const uint16_t* W[4];
+  float* logits[4];
+  int E[4];
+  int ld[4];
+  int n;
+  int nblk;
+  int32_t* zero;
+  int zero_n;
+};
+template <typename V>
+__device__ __forceinline__ V pick4(const V (&a)[4], int j) {
+  return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
+}
+
 template <int NBW>
 __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
-    int d, int E, int K, int ksplit, float* __restrict__ partial, const uint16_t* __restrict__ Wr2,
-    float* __restrict__ logits2, int E2, int nblk, int32_t* __restrict__ blockcnt, int64_t ldc) {
+    int d, int E, int K, int ksplit, float* __restrict__ partial, RouteJobs jobs,
+    int32_t* __restrict__ blockcnt, int64_t ldc) {
   using G = RouteGeo<NBW>;
   constexpr int Epad = G::Epad, NST = G::NST, CPR = G::CPR;
   constexpr int XI = G::kXInstr, WI = G::kWInstr, CBW = G::CBW;
@@ -477,16 +497,22 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / G::WN, wn = w - (w / G::WN) * G::WN;
-  // A second router matrix over the same tokens may share the launch
-  // (logits only, no selection): workgroups nblk.. take it.
   int bx = blockIdx.x;
-  if (bx >= nblk) {
-    bx -= nblk;
-    Wr = Wr2;
-    logits = logits2;
-    E = E2;
+  int ld = E;                                 // row stride of W_r and of the score rows
+  if (jobs.n > 0) {
+    const int j = bx / jobs.nblk;
+    bx -= j * jobs.nblk;
+    Wr = pick4(jobs.W, j);
+    logits = pick4(jobs.logits, j);
+    E = pick4(jobs.E, j);
+    ld = pick4(jobs.ld, j);
     ids = nullptr;
     blockcnt = nullptr;
+  }
+  if (jobs.zero) {
+    const int per = (jobs.zero_n + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int z1 = min(jobs.zero_n, ((int)blockIdx.x + 1) * per);
+    for (int i = (int)blockIdx.x * per + tid; i < z1; i += G::kThreads) jobs.zero[i] = 0;
   }
   const int64_t t0 = (int64_t)bx * kTok;
   const int KT_all = d / kBK;
@@ -515,7 +541,7 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
     const int r = (w * WI + i) * G::kWRows + lane / CPR;
     int c = (lane % CPR) ^ wr_swizzle<CPR>(r);
     if (c * 8 >= E) c = 0;
-    wsrc[i] = Wr + (int64_t)r * E + c * 8;
+    wsrc[i] = Wr + (int64_t)r * ld + c * 8;
   }
   // Every workgroup reads all of W_r; starting each one at a different
   // k-step (rotated by its position among the workgroups of its XCD) spreads
@@ -534,7 +560,7 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
     for (int i = 0; i < XI; ++i) dev::lds_copy16_stream(xsrc[i] + kk * kBK, base + (w * XI + i) * 1024);
 #pragma unroll
     for (int i = 0; i < WI; ++i)
-      dev::lds_copy16(wsrc[i] + (int64_t)kk * kBK * E, base + G::kX + (w * WI + i) * 1024);
+      dev::lds_copy16(wsrc[i] + (int64_t)kk * kBK * ld, base + G::kX + (w * WI + i) * 1024);
   };
 
   // fragment offsets.  X (16x16x32 A operand): lane -> token row lane%16,
@@ -640,7 +666,7 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
   if (logits) {
     for (int idx = tid; idx < kTok * E; idx += G::kThreads) {
       const int r = idx / E, e = idx - (idx / E) * E;
-      if (t0 + r < T) logits[(t0 + r) * E + e] = L[r * G::S + e];
+      if (t0 + r < T) logits[(t0 + r) * ld + e] = L[r * G::S + e];
     }
     __syncthreads();  // selection rewrites the rows being exported
   }
@@ -782,8 +808,7 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
       hipLaunchKernelGGL(kern, dim3(grid.x, (unsigned)ksplit), dim3(RouteGeo<NBW>::kThreads),
                          (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)W_r,
                          bias, logits, ids, gates, p.T, p.d, p.E, p.K, ksplit, partial,
-                         (const uint16_t*)nullptr, (float*)nullptr, 0, (int)grid.x,
-                         ksplit > 1 ? nullptr : blockcnt, ldc);
+                         RouteJobs{}, ksplit > 1 ? nullptr : blockcnt, ldc);
       if (ksplit > 1) {
         err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -817,21 +842,24 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
 
 namespace {
 template <int NBW>
-hipError_t launch_logits_pair_nbw(int64_t T, int d, int E1, int E2, const void* X, const void* W1,
-                                  const void* W2, float* logits1, float* logits2, hipStream_t s) {
+hipError_t launch_jobs_nbw(int64_t T, int d, const RouteJobs& jobs, const void* X, hipStream_t s) {
   auto* kern = route_staged_kernel<NBW>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        RouteGeo<NBW>::kLds);
   if (err != hipSuccess) return err;
-  const unsigned nblk = (unsigned)((T + kTok - 1) / kTok);
-  hipLaunchKernelGGL(kern, dim3(2 * nblk, 1), dim3(RouteGeo<NBW>::kThreads),
-                     (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)W1,
-                     (const float*)nullptr, logits1, (int32_t*)nullptr, (float*)nullptr, T, d, E1,
-                     1, 1, (float*)nullptr, (const uint16_t*)W2, logits2, E2, (int)nblk,
-                     (int32_t*)nullptr, (int64_t)0);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(jobs.n * jobs.nblk), 1), dim3(RouteGeo<NBW>::kThreads),
+                     (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)nullptr,
+                     (const float*)nullptr, (float*)nullptr, (int32_t*)nullptr, (float*)nullptr, T,
+                     d, 0, 1, 1, (float*)nullptr, jobs, (int32_t*)nullptr, (int64_t)0);
   return hipGetLastError();
 }
+
+// Token blocks below which a launch of the two axes leaves CUs idle (one
+// workgroup per CU): the axes wider than 128 columns are then cut in two
+// halves of their own workgroups.  The atomic-expert router (T = 4096, two
+// 256-wide axes): 128 -> 256 workgroups.
+constexpr int64_t kRouteFillBlocks = 256;
 }  // namespace
 
 bool route_pair_supported(int E1, int E2) {
@@ -839,14 +867,36 @@ bool route_pair_supported(int E1, int E2) {
 }
 
 hipError_t launch_logits_pair(int64_t T, int d, int E1, int E2, const void* X, const void* W1,
-                              const void* W2, float* logits1, float* logits2, hipStream_t s) {
+                              const void* W2, float* logits1, float* logits2, hipStream_t s,
+                              int32_t* zero, int zero_n) {
   if (!route_pair_supported(E1, E2)) return hipErrorInvalidValue;
   if (T == 0) return hipSuccess;
-  const int nbw = route_nbw(E1 > E2 ? E1 : E2);
-  if (nbw <= 1) return launch_logits_pair_nbw<1>(T, d, E1, E2, X, W1, W2, logits1, logits2, s);
-  if (nbw <= 2) return launch_logits_pair_nbw<2>(T, d, E1, E2, X, W1, W2, logits1, logits2, s);
-  if (nbw <= 4) return launch_logits_pair_nbw<4>(T, d, E1, E2, X, W1, W2, logits1, logits2, s);
-  return launch_logits_pair_nbw<8>(T, d, E1, E2, X, W1, W2, logits1, logits2, s);
+  RouteJobs jobs{};
+  jobs.nblk = (int)((T + kTok - 1) / kTok);
+  jobs.zero = zero_n > 0 ? zero : nullptr;
+  jobs.zero_n = zero_n;
+  const bool halves = 2 * (int64_t)jobs.nblk < kRouteFillBlocks;
+  const uint16_t* Ws[2] = {(const uint16_t*)W1, (const uint16_t*)W2};
+  float* Ls[2] = {logits1, logits2};
+  const int Es[2] = {E1, E2};
+  int widest = 0;
+  for (int a = 0; a < 2; ++a) {
+    const int cut = (halves && Es[a] > 128) ? 128 : Es[a];
+    for (int c0 = 0; c0 < Es[a]; c0 += cut) {
+      const int w = (Es[a] - c0 < cut) ? Es[a] - c0 : cut;
+      jobs.W[jobs.n] = Ws[a] + c0;
+      jobs.logits[jobs.n] = Ls[a] + c0;
+      jobs.E[jobs.n] = w;
+      jobs.ld[jobs.n] = Es[a];
+      ++jobs.n;
+      widest = w > widest ? w : widest;
+    }
+  }
+  const int nbw = route_nbw(widest);
+  if (nbw <= 1) return launch_jobs_nbw<1>(T, d, jobs, X, s);
+  if (nbw <= 2) return launch_jobs_nbw<2>(T, d, jobs, X, s);
+  if (nbw <= 4) return launch_jobs_nbw<4>(T, d, jobs, X, s);
+  return launch_jobs_nbw<8>(T, d, jobs, X, s);
 }
 
 hipError_t launch_route(const Problem& p, const void* X, const void* W_r, const float* bias,
