@@ -761,7 +761,8 @@ __global__ __launch_bounds__(64 * kTokWaves) void token_backward_kernel(
         const int k = k0 + u < K ? k0 + u : K - 1;
         const int s = s_slot[wv][k];
         ok[u] = (k0 + u < K) && s >= 0;
-        o[u] = *reinterpret_cast<const u32x4*>(dXs + (int64_t)(ok[u] ? s : 0) * d + c * 8);
+        o[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(dXs + (int64_t)(ok[u] ? s : 0) * d + c * 8));
       }
 #pragma unroll
       for (int u = 0; u < KG; ++u)
@@ -793,7 +794,7 @@ __global__ __launch_bounds__(64 * kTokWaves) void token_backward_kernel(
     u32x4 out;
 #pragma unroll
     for (int h = 0; h < 4; ++h) out[h] = dev::pack_bf16x2(acc[2 * h], acc[2 * h + 1]);
-    *reinterpret_cast<u32x4*>(dX + t * (int64_t)d + c * 8) = out;
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(dX + t * (int64_t)d + c * 8));
   }
 }
 
