@@ -104,6 +104,16 @@ typedef struct {
  * round_tokens -> grouped_ffn -> combine. */
 #define MOE_FLAG_TOKEN_ROUNDING 8u
 
+/* desc->flags bit for moe_route / moe_route_ws / moe_route_permute /
+ * moe_forward / moe_forward_train: select the K experts of each token by
+ * threshold bisection ("AI芯片如何支持MoE架构" §4.3, threshold-based
+ * selection: try a threshold, count the scores above it, move it) instead of
+ * the default sort-and-extract selection.  Both are exact: ids, their order
+ * and the gates are bit-identical either way; only the kernel's work differs
+ * (the bisection runs a fixed number of counting steps whatever K is, the
+ * default K extraction rounds). */
+#define MOE_FLAG_TOPK_THRESHOLD 16u
+
 /* Workspace selectors for moe_workspace_size.  MOE_WS_SAVED is the state
  * that moe_forward_train keeps for moe_backward (see moe_saved_layout);
  * MOE_WS_BACKWARD is moe_backward's scratch. */
@@ -300,7 +310,8 @@ moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, con
  * cannot cheaply recompute: the routing metadata and the pre-activations
  * x W_gate | x W_up; the SwiGLU activation A and the expert outputs O are
  * never stored for the backward.  Both calls need desc->dtype == MOE_BF16
- * (MOE_ERR_UNSUPPORTED otherwise) and take flags 0 or MOE_FLAG_GEMM_TILED:
+ * (MOE_ERR_UNSUPPORTED otherwise) and take flags 0 or MOE_FLAG_GEMM_TILED
+ * (plus MOE_FLAG_TOPK_THRESHOLD, which only moe_forward_train's router uses):
  * the training path always runs the 256x256-tiled GEMMs. */
 
 /* Forward that also fills `saved` (MOE_WS_SAVED bytes, layout in

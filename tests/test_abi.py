@@ -48,14 +48,14 @@ def test_validate_cases():
         (moe.make_desc(16, 100, 8, 2, 256), moe.MOE_ERR_UNSUPPORTED),          # d % 64
         (moe.make_desc(16, 128, 8, 2, 96), moe.MOE_ERR_UNSUPPORTED),           # n % 64
         (moe.make_desc(16, 128, 8, 2, 256, flags=6), moe.MOE_ERR_INVALID_ARG),  # both GEMM paths
-        (moe.make_desc(16, 128, 8, 2, 256, flags=16), moe.MOE_ERR_INVALID_ARG),  # undefined bit
+        (moe.make_desc(16, 128, 8, 2, 256, flags=32), moe.MOE_ERR_INVALID_ARG),  # undefined bit
         (moe.make_desc(16, 128, 8, 2, 256, capacity_factor=float("nan")), moe.MOE_ERR_INVALID_ARG),
         (moe.make_desc(16, 128, 8, 2, 256, capacity_factor=float("inf")), moe.MOE_ERR_INVALID_ARG),
         (moe.make_desc(2 ** 30, 128, 8, 2, 256), moe.MOE_ERR_UNSUPPORTED),     # T*K >= 2^31
     ]
     for desc, want in bad:
         assert moe.moe_validate(desc) == want
-    for f in (1, 2, 4, 5, 8, 10):                             # defined bits are valid
+    for f in (1, 2, 4, 5, 8, 10, 16, 26):                     # defined bits are valid
         assert moe.moe_validate(moe.make_desc(16, 128, 8, 2, 256, flags=f)) == moe.MOE_OK
     d = moe.make_desc(16, 128, 8, 2, 256)
     d.dtype = 7
@@ -154,10 +154,19 @@ def test_gemm_path_flags_are_checked_per_entry_point():
     ws = moe.moe_workspace_size(T0(0), moe.MOE_WS_FORWARD) + 256
     assert lib.moe_forward(ctypes.byref(T0(moe.MOE_FLAG_GEMM_SKINNY)), A, A, None, A, A, A, A, A, ws,
                            None) == moe.MOE_OK
-    # the tile-table bit belongs to the grouped entry points only; route takes no flags
+    # the tile-table bit belongs to the grouped entry points only; route takes
+    # only the selection bit, which the grouped GEMMs and the permutation refuse
     assert lib.moe_forward(ctypes.byref(T0(moe.MOE_FLAG_TILE_TABLE_READY)), A, A, None, A, A, A, A,
                            A, ws, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_route(ctypes.byref(T0(moe.MOE_FLAG_GEMM_TILED)), A, A, None, None, A, A, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    thr = moe.MOE_FLAG_TOPK_THRESHOLD
+    assert lib.moe_route(ctypes.byref(T0(thr)), A, A, None, None, A, A, None) == moe.MOE_OK
+    assert lib.moe_forward(ctypes.byref(T0(thr | moe.MOE_FLAG_GEMM_TILED)), A, A, None, A, A, A, A,
+                           A, ws, None) == moe.MOE_OK
+    assert lib.moe_grouped_ffn(ctypes.byref(T0(thr)), A, A, A, A, A, A, A, A, A, 1 << 20, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(ctypes.byref(T0(thr)), A, A, A, A, A, A, None, 0, None) == \
         moe.MOE_ERR_INVALID_ARG
 
 

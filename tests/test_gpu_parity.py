@@ -233,6 +233,85 @@ def test_quantised_logits_with_many_exact_ties():
     assert ties > T // 2
 
 
+def _router_case(kind, T, d, E, seed, dtype=torch.bfloat16):
+    """Router inputs with or without exact ties among the logits."""
+    inp = mi.draw(T, d, E, 64, dtype, seed=seed, bias="zipf" if kind == "zipf" else None)
+    g = torch.Generator().manual_seed(seed)
+    if kind == "zero":
+        inp["W_r"] = torch.zeros_like(inp["W_r"])
+    elif kind == "dup":
+        inp["W_r"][:, E - 1] = inp["W_r"][:, 0]
+        inp["W_r"][:, E // 2] = inp["W_r"][:, 1]
+    elif kind == "quant":
+        inp["X"] = torch.randint(-1, 2, (T, d), generator=g).to(dtype)
+        inp["W_r"] = (torch.randint(-1, 2, (d, E), generator=g).float() / 8).to(dtype)
+    return inp
+
+
+THRESHOLD_CASES = [
+    # kind, T, d, E, K, dtype
+    ("plain", 700, 512, 128, 8, "bf16"),
+    ("zipf", 1000, 256, 256, 8, "bf16"),
+    ("plain", 300, 128, 3, 3, "bf16"),       # K = E, E not a multiple of 8 (register-staged router)
+    ("plain", 200, 64, 40, 20, "bf16"),      # K above 16
+    ("plain", 130, 128, 64, 64, "bf16"),     # K = E = 64: every expert of every token
+    ("zero", 300, 128, 16, 5, "bf16"),       # every logit tied
+    ("dup", 400, 256, 12, 12, "bf16"),       # duplicated columns
+    ("quant", 600, 128, 32, 4, "bf16"),      # many exact ties, ties cut at the threshold
+    ("quant", 500, 128, 256, 8, "bf16"),
+    ("plain", 64, 4096, 256, 8, "bf16"),     # decode size: k-split router + selection kernel
+    ("plain", 256, 128, 8, 2, "fp32"),
+    ("quant", 300, 64, 40, 7, "fp32"),
+]
+
+
+@pytest.mark.parametrize("kind,T,d,E,K,dtype", THRESHOLD_CASES)
+def test_threshold_selection_matches_default(kind, T, d, E, K, dtype):
+    """MOE_FLAG_TOPK_THRESHOLD: ids, their order and gates bit-equal to the
+    default selection's (both router paths), and ids equal to the oracle's
+    on the device's logits."""
+    print(f"case threshold {kind} T={T} d={d} E={E} K={K} {dtype}", flush=True)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    inp = _router_case(kind, T, d, E, seed=31, dtype=tdt)
+    dev = device_inputs(inp)
+    for split in (True, False):
+        base = moe.route(dev["X"], dev["W_r"], K, bias=dev["bias"], want_logits=True, split=split)
+        thr = moe.route(dev["X"], dev["W_r"], K, bias=dev["bias"], want_logits=True, split=split,
+                        flags=moe.MOE_FLAG_TOPK_THRESHOLD)
+        torch.cuda.synchronize()
+        assert torch.equal(thr[2], base[2]), "logits differ"
+        assert torch.equal(thr[0], base[0]), f"ids differ (split={split})"
+        assert torch.equal(thr[1], base[1]), f"gates differ (split={split})"
+        check_routing({"ids": thr[0], "gates": thr[1], "logits": thr[2]}, inp, K)
+
+
+@pytest.mark.parametrize("kind,T,d,E,K,cf", [("zipf", 3000, 512, 128, 6, 1.0), ("quant", 2000, 128, 64, 4, 0.0),
+                                             ("plain", 200, 64, 40, 20, 0.0)])
+def test_threshold_selection_in_fused_paths(kind, T, d, E, K, cf):
+    """moe_route_permute and moe_forward with MOE_FLAG_TOPK_THRESHOLD give
+    exactly the default flags' outputs."""
+    print(f"case threshold fused {kind} T={T} d={d} E={E} K={K} cf={cf}", flush=True)
+    inp = _router_case(kind, T, d, E, seed=37)
+    n = 128
+    inp.update({k: v for k, v in mi.draw(T, d, E, n, torch.bfloat16, seed=38).items()
+                if k in ("W_gate", "W_up", "W_down")})
+    dev = device_inputs(inp)
+    outs = []
+    for flags in (0, moe.MOE_FLAG_TOPK_THRESHOLD):
+        desc = moe.make_desc(T, d, E, K, n, "bf16", cf, flags=flags)
+        rp = moe.route_permute(dev["X"], dev["W_r"], K, desc, bias=dev["bias"], want_logits=True)
+        Y = moe.forward(dev["X"], dev["W_r"], dev["W_gate"], dev["W_up"], dev["W_down"], K, cf,
+                        bias=dev["bias"], flags=flags)
+        outs.append((rp, Y))
+    torch.cuda.synchronize()
+    (rp0, Y0), (rp1, Y1) = outs
+    N = int(rp0["offsets"][E].item())
+    for key in ("ids", "gates", "logits", "counts", "offsets", "raw_counts", "inv_slot"):
+        assert torch.equal(rp1[key], rp0[key]), key
+    assert torch.equal(rp1["perm_token"][:N], rp0["perm_token"][:N])
+    assert torch.equal(Y1, Y0)
+
+
 def test_capacity_one_keeps_each_experts_first_token():
     inp = mi.draw(257, 128, 8, 128, torch.bfloat16, seed=4)
     cf = 1e-6                                    # C = 1

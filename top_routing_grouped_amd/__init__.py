@@ -41,6 +41,7 @@ MOE_FLAG_TILE_TABLE_READY = 1
 MOE_FLAG_GEMM_TILED = 2
 MOE_FLAG_GEMM_SKINNY = 4
 MOE_FLAG_TOKEN_ROUNDING = 8
+MOE_FLAG_TOPK_THRESHOLD = 16
 MOE_NOALLOC_SCRATCH_BYTES = 2 << 20
 
 
@@ -317,14 +318,15 @@ def workspace(desc: MoeDesc, entry: int, device="cuda"):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def route(X, W_r, K, bias=None, want_logits=False, n=64, split=True):
+def route(X, W_r, K, bias=None, want_logits=False, n=64, split=True, flags=0):
     """Steps 1-2.  Returns (ids [T,K] int32, gates [T,K] fp32, logits [T,E] fp32 or None).
     split=True goes through moe_route_ws (k split for small batches, as
-    moe_forward does); split=False through moe_route."""
+    moe_forward does); split=False through moe_route.  flags may carry
+    MOE_FLAG_TOPK_THRESHOLD (the threshold selection)."""
     import torch
     T, d = X.shape
     E = W_r.shape[1]
-    desc = make_desc(T, d, E, K, n, "bf16" if X.dtype == torch.bfloat16 else "fp32")
+    desc = make_desc(T, d, E, K, n, "bf16" if X.dtype == torch.bfloat16 else "fp32", flags=flags)
     ids = torch.empty((T, K), dtype=torch.int32, device=X.device)
     gates = torch.empty((T, K), dtype=torch.float32, device=X.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=X.device) if want_logits else None

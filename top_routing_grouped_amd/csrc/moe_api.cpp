@@ -63,7 +63,7 @@ moe_status check_desc(const moe_desc* d, uint32_t allowed_flags = 0) {
 
 constexpr uint32_t kGemmFlags = MOE_FLAG_TILE_TABLE_READY | MOE_FLAG_GEMM_TILED | MOE_FLAG_GEMM_SKINNY;
 // every defined bit (host-only queries accept them all)
-constexpr uint32_t kAllFlags = kGemmFlags | MOE_FLAG_TOKEN_ROUNDING;
+constexpr uint32_t kAllFlags = kGemmFlags | MOE_FLAG_TOKEN_ROUNDING | MOE_FLAG_TOPK_THRESHOLD;
 
 bool skinny(const moe::Problem& p, const moe_desc* d) {
   return moe::use_skinny(p, d->flags, MOE_FLAG_GEMM_TILED, MOE_FLAG_GEMM_SKINNY);
@@ -88,6 +88,7 @@ moe::Problem make_problem(const moe_desc* d) {
   const int64_t tk = d->T * (int64_t)d->K;
   const int64_t ec = (int64_t)d->E * p.C;
   p.rows_max = tk < ec ? tk : ec;
+  p.sel = (d->flags & MOE_FLAG_TOPK_THRESHOLD) ? 1 : 0;
   return p;
 }
 
@@ -500,7 +501,7 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 moe_status moe_route(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
                      float* logits, int32_t* topk_ids, float* topk_gates, void* stream) {
   g_last_error.clear();
-  MOE_TRY(check_desc(desc));
+  MOE_TRY(check_desc(desc, MOE_FLAG_TOPK_THRESHOLD));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
   MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {topk_ids, "topk_ids"}, {topk_gates, "topk_gates"}},
                      {{bias, "bias"}, {logits, "logits"}}));
@@ -514,7 +515,7 @@ moe_status moe_route_ws(const moe_desc* desc, const void* X, const void* W_r, co
                         float* logits, int32_t* topk_ids, float* topk_gates, void* ws,
                         size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  MOE_TRY(check_desc(desc));
+  MOE_TRY(check_desc(desc, MOE_FLAG_TOPK_THRESHOLD));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
   MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {topk_ids, "topk_ids"}, {topk_gates, "topk_gates"}},
                      {{bias, "bias"}, {logits, "logits"}, {ws, "ws"}}));
@@ -550,7 +551,7 @@ moe_status moe_route_permute(const moe_desc* desc, const void* X, const void* W_
                              int32_t* raw_counts, int32_t* perm_token, int32_t* inv_slot,
                              void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  MOE_TRY(check_desc(desc));
+  MOE_TRY(check_desc(desc, MOE_FLAG_TOPK_THRESHOLD));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
   MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {topk_ids, "topk_ids"}, {topk_gates, "topk_gates"},
                       {counts, "counts"}, {offsets, "offsets"}, {perm_token, "perm_token"},
@@ -699,7 +700,8 @@ moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, con
                        const void* W_gate, const void* W_up, const void* W_down, void* Y,
                        void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_GEMM_SKINNY | MOE_FLAG_TOKEN_ROUNDING));
+  MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_GEMM_SKINNY | MOE_FLAG_TOKEN_ROUNDING |
+                               MOE_FLAG_TOPK_THRESHOLD));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
   MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {W_gate, "W_gate"}, {W_up, "W_up"},
                       {W_down, "W_down"}, {Y, "Y"}},
@@ -744,7 +746,7 @@ moe_status moe_forward_train(const moe_desc* desc, const void* X, const void* W_
                              const void* W_down, void* Y, void* saved, size_t saved_bytes,
                              void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED));
+  MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_TOPK_THRESHOLD));
   if (desc->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the training path is bf16 only");
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
   MOE_TRY(check_ptrs({{X, "X"}, {W_r, "W_r"}, {W_gate, "W_gate"}, {W_up, "W_up"},
@@ -773,7 +775,7 @@ moe_status moe_backward(const moe_desc* desc, const void* X, const void* W_r, co
                         size_t saved_bytes, void* dX, float* dW_r, float* dW_gate, float* dW_up,
                         float* dW_down, void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED));
+  MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_TOPK_THRESHOLD));  // the latter: no effect here
   if (desc->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the training path is bf16 only");
   MOE_TRY(check_ptrs({{dW_r, "dW_r"}, {dW_gate, "dW_gate"}, {dW_up, "dW_up"}, {dW_down, "dW_down"}},
                      {}));

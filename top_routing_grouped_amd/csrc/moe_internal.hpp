@@ -16,6 +16,7 @@ struct Problem {
   bool bf16;          // element type of X, weights, H, O, Y (else fp32)
   int64_t C;          // per-expert cap
   int64_t rows_max;   // upper bound on kept assignments: min(T*K, E*C)
+  int sel = 0;        // top-K selection: 0 sorted lanes + row maxima, 1 threshold bisection
 };
 
 // Token block of the permutation kernels (one workgroup of threads, one

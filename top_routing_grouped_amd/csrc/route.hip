@@ -203,12 +203,196 @@ __device__ __forceinline__ void topk_from_lds(float* L, int S, int64_t t0, int64
   }
 }
 
+__device__ __forceinline__ int row_sum16i(int x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  return x;
+}
+
+// The same top-K by threshold selection ("AI芯片如何支持MoE架构" §4.3: guess a
+// threshold, count the scores above it, raise or lower it), with the same
+// token layout as topk_from_lds and exactly its results:
+// * the K-th largest key th is found by bisection over the 32-bit
+//   order-preserving key: each step tries th | bit and keeps the bit when at
+//   least K keys of the token's row reach it (a DPP row sum of per-lane
+//   counts).  It starts below the highest bit where the row's largest and
+//   smallest keys differ.
+// * ties at th, when not all fit, go to the lowest ids: the same bisection
+//   over the 8-bit ids of the tied entries.
+// * the K winners are compacted into the token's LDS row slot by slot (lane
+//   i, slot j is expert i + 16 j, so positions follow ascending ids), and a
+//   winner's rank is the number of row keys above its own plus the equal
+//   keys at lower positions: the order (score desc, id asc).
+template <int V, int R = 4>
+__device__ __forceinline__ void topk_threshold_from_lds(float* L, int S, int64_t t0, int64_t T,
+                                                        int E, int K, int32_t* __restrict__ ids,
+                                                        float* __restrict__ gates, int* cntl) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int q = lane >> 4;
+  const int i = lane & 15;
+  uint32_t uk[R][V];
+  float val[R][V];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float* row = L + (4 * R * w + R * q + r) * S;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      val[r][j] = row[i + 16 * j];
+      uk[r][j] = (uint32_t)sort_key(val[r][j]) ^ 0x80000000u;
+    }
+  }
+  // threshold: the K-th largest key of each token.  The R tokens of a row
+  // run their bisections side by side (independent DPP chains), over the
+  // wave's widest range of bits; a token skips the bits above its own range.
+  uint32_t th[R];
+  int top[R], hb[R];
+  int hbw = -1;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int mx = (int)0x80000000, mn = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      mx = max(mx, (int)(uk[r][j] ^ 0x80000000u));
+      mn = min(mn, (int)(uk[r][j] ^ 0x80000000u));
+    }
+    mx = row_max16(mx);
+    mn = row_min16(mn);
+    top[r] = mx;                              // largest sort key (signed order)
+    const uint32_t kmax = (uint32_t)mx ^ 0x80000000u, kmin = (uint32_t)mn ^ 0x80000000u;
+    const uint32_t diff = kmax ^ kmin;
+    hb[r] = diff ? 31 - __builtin_clz(diff) : -1;
+    th[r] = (hb[r] >= 0) ? (kmax & ~((2u << hb[r]) - 1u)) : kmax;
+    hbw = max(hbw, hb[r]);
+  }
+  hbw = max(max(__builtin_amdgcn_readlane(hbw, 0), __builtin_amdgcn_readlane(hbw, 16)),
+            max(__builtin_amdgcn_readlane(hbw, 32), __builtin_amdgcn_readlane(hbw, 48)));
+  for (int bit = hbw; bit >= 0; --bit) {
+    int c[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t cand = th[r] | (1u << bit);
+      c[r] = 0;
+#pragma unroll
+      for (int j = 0; j < V; ++j) c[r] += uk[r][j] >= cand;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) c[r] = row_sum16i(c[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (bit <= hb[r] && c[r] >= K) th[r] |= 1u << bit;
+  }
+  // ties at the threshold: the lowest ids first
+  int xid[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      gt += uk[r][j] > th[r];
+      eq += uk[r][j] == th[r];
+    }
+    gt = row_sum16i(gt);
+    eq = row_sum16i(eq);
+    const int need = K - gt;
+    int x = 255;                               // every tie taken (the usual case)
+    if (need < eq) {
+      x = 0;
+      for (int bit = 7; bit >= 0; --bit) {
+        const int cand = x | (1 << bit);
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < V; ++j) c += (uk[r][j] == th[r]) && (i + 16 * j < cand);
+        if (row_sum16i(c) < need) x = cand;
+      }
+    }
+    xid[r] = x;
+  }
+  // compact the winners' keys into the token's row, positions in id order
+  int pos[R][V];
+  __builtin_amdgcn_wave_barrier();             // every lane has read its row entries
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int* row = reinterpret_cast<int*>(L + (4 * R * w + R * q + r) * S);
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const bool win = uk[r][j] > th[r] || (uk[r][j] == th[r] && i + 16 * j <= xid[r]);
+      const uint32_t m = (uint32_t)(__ballot(win) >> (16 * q)) & 0xFFFFu;
+      pos[r][j] = win ? base + __popc(m & ((1u << i) - 1u)) : -1;
+      if (win) row[pos[r][j]] = (int)(uk[r][j] ^ 0x80000000u);
+      base += __popc(m);
+    }
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  int rank[R][V];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int* row = reinterpret_cast<const int*>(L + (4 * R * w + R * q + r) * S);
+#pragma unroll
+    for (int j = 0; j < V; ++j) rank[r][j] = 0;
+    for (int c = 0; c < K; ++c) {
+      const int kc = row[c];
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const int mine = (int)(uk[r][j] ^ 0x80000000u);
+        rank[r][j] += (kc > mine) || (kc == mine && c < pos[r][j]);
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  // winners in rank order: ids out, scores back into the row for the gates
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int tl = 4 * R * w + R * q + r;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      if (pos[r][j] >= 0) {
+        L[tl * S + rank[r][j]] = val[r][j];
+        if (t0 + tl < T) {
+          ids[(t0 + tl) * K + rank[r][j]] = i + 16 * j;
+          if (cntl) atomicAdd(&cntl[i + 16 * j], 1);
+        }
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int tl = 4 * R * w + R * q + r;
+    const float m0 = key_value(top[r]);
+    float part = 0.f;
+    for (int c = i; c < K; c += 16) part += expf(L[tl * S + c] - m0);
+    const float sum = row_sum16(part);
+    if (t0 + tl < T) {
+      for (int c = i; c < K; c += 16)
+        gates[(t0 + tl) * K + c] = expf(L[tl * S + c] - m0) / sum;
+    }
+  }
+}
+
+// Top-K by the selection the call asked for (sel: 0 sorted lanes and K
+// rounds of row maxima, 1 threshold bisection); the results are the same.
+template <int V, int R = 4>
+__device__ __forceinline__ void select_topk(int sel, float* L, int S, int64_t t0, int64_t T, int E,
+                                            int K, int32_t* __restrict__ ids,
+                                            float* __restrict__ gates, int* cntl) {
+  if (sel) topk_threshold_from_lds<V, R>(L, S, t0, T, E, K, ids, gates, cntl);
+  else topk_from_lds<V, R>(L, S, t0, T, E, K, ids, gates, cntl);
+}
+
 // Shared tail: bias, optional export, selection.
 // PREPPED: the caller already added the bias and wrote -inf into the padding.
 template <int V, bool PREPPED = false>
 __device__ __forceinline__ void route_tail(float* L, int S, int64_t t0, int64_t T, int E, int K, int Epad,
                            const float* __restrict__ bias, float* __restrict__ logits,
-                           int32_t* __restrict__ ids, float* __restrict__ gates, int* cntl) {
+                           int32_t* __restrict__ ids, float* __restrict__ gates, int* cntl,
+                           int sel) {
   if (!PREPPED) {
     for (int idx = threadIdx.x; idx < kTok * Epad; idx += kThreads) {
       const int r = idx / Epad, e = idx - (idx / Epad) * Epad;
@@ -229,7 +413,7 @@ __device__ __forceinline__ void route_tail(float* L, int S, int64_t t0, int64_t 
     }
     __syncthreads();  // selection rewrites the rows being exported
   }
-  topk_from_lds<V>(L, S, t0, T, E, K, ids, gates, cntl);
+  select_topk<V>(sel, L, S, t0, T, E, K, ids, gates, cntl);
 }
 
 // Per-block expert counts for the permutation: the selection above adds each
@@ -253,7 +437,7 @@ template <int NBW, bool VEC>
 __global__ __launch_bounds__(kThreads, (NBW >= 8) ? 1 : 2) void route_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
-    int d, int E, int K, int32_t* __restrict__ blockcnt, int64_t ldc) {
+    int d, int E, int K, int32_t* __restrict__ blockcnt, int64_t ldc, int sel) {
   constexpr int Epad = 32 * NBW;
   __shared__ int cntl[256];
   // X stages held in registers (prefetch depth); fewer when the weight tile is wide
@@ -395,7 +579,8 @@ __global__ __launch_bounds__(kThreads, (NBW >= 8) ? 1 : 2) void route_bf16_kerne
       }
   if (blockcnt) count_zero(cntl, kThreads);
   __syncthreads();
-  route_tail<2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates, blockcnt ? cntl : nullptr);
+  route_tail<2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates, blockcnt ? cntl : nullptr,
+                      sel);
   if (blockcnt) count_store(cntl, blockcnt, ldc, blockIdx.x, E, kThreads);
 }
 
@@ -486,7 +671,7 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
     int d, int E, int K, int ksplit, float* __restrict__ partial, RouteJobs jobs,
-    int32_t* __restrict__ blockcnt, int64_t ldc) {
+    int32_t* __restrict__ blockcnt, int64_t ldc, int sel) {
   using G = RouteGeo<NBW>;
   constexpr int Epad = G::Epad, NST = G::NST, CPR = G::CPR;
   constexpr int XI = G::kXInstr, WI = G::kWInstr, CBW = G::CBW;
@@ -670,7 +855,7 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
     }
     __syncthreads();  // selection rewrites the rows being exported
   }
-  if (ids) topk_from_lds<2 * NBW, kTok / (4 * G::NW)>(L, G::S, t0, T, E, K, ids, gates,
+  if (ids) select_topk<2 * NBW, kTok / (4 * G::NW)>(sel, L, G::S, t0, T, E, K, ids, gates,
                                                        blockcnt ? cntl : nullptr);
   if (blockcnt) count_store(cntl, blockcnt, ldc, bx, E, G::kThreads);
 }
@@ -716,7 +901,7 @@ template <int NBW>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const float* __restrict__ scores, const float* __restrict__ bias, float* __restrict__ logits,
     int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T, int E, int K,
-    int32_t* __restrict__ blockcnt, int64_t ldc) {
+    int32_t* __restrict__ blockcnt, int64_t ldc, int sel) {
   using G = SelGeo<NBW>;
   constexpr int Epad = G::Epad, S = G::S, TW = G::TW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -761,7 +946,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
     }
     __syncthreads();  // selection rewrites the rows being exported
   }
-  topk_from_lds<2 * NBW, G::R>(L, S, t0, T, E, K, ids, gates, blockcnt ? cntl : nullptr);
+  select_topk<2 * NBW, G::R>(sel, L, S, t0, T, E, K, ids, gates, blockcnt ? cntl : nullptr);
   if (blockcnt) count_store(cntl, blockcnt, ldc, blockIdx.x, E, kThreads);
 }
 
@@ -770,7 +955,7 @@ template <int NBW>
 __global__ __launch_bounds__(kThreads) void route_f32_kernel(
     const float* __restrict__ X, const float* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
-    int d, int E, int K, int32_t* __restrict__ blockcnt, int64_t ldc) {
+    int d, int E, int K, int32_t* __restrict__ blockcnt, int64_t ldc, int sel) {
   constexpr int Epad = 32 * NBW;
   constexpr int S = Epad + 16;
   __shared__ float L[kTok * S];
@@ -787,7 +972,8 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
     L[r * S + e] = s;
   }
   __syncthreads();
-  route_tail<2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates, blockcnt ? cntl : nullptr);
+  route_tail<2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates, blockcnt ? cntl : nullptr,
+                      sel);
   if (blockcnt) count_store(cntl, blockcnt, ldc, blockIdx.x, E, kThreads);
 }
 
@@ -808,7 +994,7 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
       hipLaunchKernelGGL(kern, dim3(grid.x, (unsigned)ksplit), dim3(RouteGeo<NBW>::kThreads),
                          (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)W_r,
                          bias, logits, ids, gates, p.T, p.d, p.E, p.K, ksplit, partial,
-                         RouteJobs{}, ksplit > 1 ? nullptr : blockcnt, ldc);
+                         RouteJobs{}, ksplit > 1 ? nullptr : blockcnt, ldc, p.sel);
       if (ksplit > 1) {
         err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -824,16 +1010,16 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(sel, dim3((unsigned)((p.T + TW - 1) / TW)), dim3(kThreads),
                            (size_t)kSelLds, s, partial, bias, logits, ids, gates, p.T, p.E, p.K,
-                           blockcnt, ldc);
+                           blockcnt, ldc, p.sel);
       }
     } else
       hipLaunchKernelGGL((route_bf16_kernel<NBW, false>), grid, dim3(kThreads), 0, s,
                          (const uint16_t*)X, (const uint16_t*)W_r, bias, logits, ids, gates, p.T,
-                         p.d, p.E, p.K, blockcnt, ldc);
+                         p.d, p.E, p.K, blockcnt, ldc, p.sel);
   } else {
     hipLaunchKernelGGL((route_f32_kernel<NBW>), grid, dim3(kThreads), 0, s, (const float*)X,
                        (const float*)W_r, bias, logits, ids, gates, p.T, p.d, p.E, p.K, blockcnt,
-                       ldc);
+                       ldc, p.sel);
   }
   return hipGetLastError();
 }
@@ -851,7 +1037,7 @@ hipError_t launch_jobs_nbw(int64_t T, int d, const RouteJobs& jobs, const void* 
   hipLaunchKernelGGL(kern, dim3((unsigned)(jobs.n * jobs.nblk), 1), dim3(RouteGeo<NBW>::kThreads),
                      (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)nullptr,
                      (const float*)nullptr, (float*)nullptr, (int32_t*)nullptr, (float*)nullptr, T,
-                     d, 0, 1, 1, (float*)nullptr, jobs, (int32_t*)nullptr, (int64_t)0);
+                     d, 0, 1, 1, (float*)nullptr, jobs, (int32_t*)nullptr, (int64_t)0, 0);
   return hipGetLastError();
 }
 
