@@ -482,20 +482,26 @@ hipError_t launch_bf16(const uint16_t* A, const int32_t* perm, const int32_t* ta
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- fp32 (plain FMA)
-// 32-row x 64-column tiles, LDS-tiled over k; only for the fp32 element type.
-constexpr int kF32Rows = 32;
+// ---------------------------------------------------------------- fp32 (MFMA)
+// 64-row x 64-column tiles of 4 waves, each 32 x 32 with
+// v_mfma_f32_32x32x2_f32 over 32-deep k slices staged in LDS; only for the
+// fp32 element type (a correctness-sized layer).  A lane supplies
+// A[row lane%32][k lane/32] and B[k lane/32][col lane%32] and ends with
+// columns lane%32 of rows 8*(v/4) + 4*(lane/32) + v%4 of its wave's block.
+constexpr int kF32Rows = 64, kF32Cols = 64, kF32K = 32;
 constexpr int kF32Sub = kGemmBM / kF32Rows;   // sub-tiles per table tile
+using f32x16v = float __attribute__((ext_vector_type(16)));
+
 template <bool UP>
 __global__ __launch_bounds__(256) void grouped_gemm_f32(
     const float* __restrict__ A, const int32_t* __restrict__ perm, const int32_t* __restrict__ table,
     const float* __restrict__ B0, const float* __restrict__ B1, float* __restrict__ C, int64_t T,
     int Kd, int N, int NT) {
-  constexpr int TM = kF32Rows, TN = 64, TK = 16;
+  constexpr int TM = kF32Rows, TN = kF32Cols, TK = kF32K;
   __shared__ float As[TM][TK + 1];
   __shared__ float Bg[TK][TN];
-  __shared__ float Bu[TK][TN];
-  // each 128-row table tile is covered by BM/TM sub-tiles of TM rows
+  __shared__ float Bu[UP ? TK : 1][TN];
+  // each 256-row table tile is covered by kF32Sub sub-tiles of TM rows
   constexpr int kSub = kF32Sub;
   const int total = table[0] * kSub * NT;
   const int bid = blockIdx.x;
@@ -507,13 +513,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
   const int e = tile_expert((uint32_t)ent[0]), row0 = ent[1] + sub * TM;
   const int nrows = (ent[2] - row0 < TM) ? ent[2] - row0 : TM;
   if (nrows <= 0) return;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  float ag[2][4] = {}, au[2][4] = {};
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
   const float* Wg = B0 + (int64_t)e * Kd * N;
   const float* Wu = UP ? B1 + (int64_t)e * Kd * N : nullptr;
+  f32x16v ag, au;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) ag[v] = au[v] = 0.f;
   for (int k0 = 0; k0 < Kd; k0 += TK) {
     for (int idx = tid; idx < TM * TK; idx += 256) {
-      const int r = idx / TK, c = idx % TK;
+      const int r = idx / TK, c = idx - (idx / TK) * TK;
       const int rr = r < nrows ? r : nrows - 1;
       int64_t row;
       if (UP) {
@@ -522,40 +531,34 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
       } else {
         row = row0 + rr;
       }
-      As[r][c] = A[row * Kd + k0 + c];
+      As[r][c] = (k0 + c < Kd) ? A[row * Kd + k0 + c] : 0.f;
     }
     for (int idx = tid; idx < TK * TN; idx += 256) {
-      const int r = idx / TN, c = idx % TN;
+      const int r = idx / TN, c = idx - (idx / TN) * TN;
       const int col = nt * TN + c;
-      Bg[r][c] = col < N ? Wg[(int64_t)(k0 + r) * N + col] : 0.f;
-      if (UP) Bu[r][c] = col < N ? Wu[(int64_t)(k0 + r) * N + col] : 0.f;
+      const bool ok = col < N && k0 + r < Kd;
+      Bg[r][c] = ok ? Wg[(int64_t)(k0 + r) * N + col] : 0.f;
+      if (UP) Bu[r][c] = ok ? Wu[(int64_t)(k0 + r) * N + col] : 0.f;
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < TK; ++kk)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const float a = As[ty * 2 + i][kk];
-#pragma unroll
-        for (int jx = 0; jx < 4; ++jx) {
-          ag[i][jx] = fmaf(a, Bg[kk][tx * 4 + jx], ag[i][jx]);
-          if (UP) au[i][jx] = fmaf(a, Bu[kk][tx * 4 + jx], au[i][jx]);
-        }
-      }
+    for (int kk = 0; kk < TK; kk += 2) {
+      const float a = As[wm * 32 + (lane & 31)][kk + (lane >> 5)];
+      ag = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Bg[kk + (lane >> 5)][wn * 32 + (lane & 31)], ag, 0, 0, 0);
+      if (UP)
+        au = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Bu[kk + (lane >> 5)][wn * 32 + (lane & 31)], au, 0, 0, 0);
+    }
     __syncthreads();
   }
+  const int col = nt * TN + wn * 32 + (lane & 31);
+  if (col >= N) return;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = ty * 2 + i;
+  for (int v = 0; v < 16; ++v) {
+    const int r = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
     if (r >= nrows) continue;
-#pragma unroll
-    for (int jx = 0; jx < 4; ++jx) {
-      const int col = nt * TN + tx * 4 + jx;
-      if (col >= N) continue;
-      float v = ag[i][jx];
-      if (UP) v = v / (1.0f + expf(-v)) * au[i][jx];
-      C[(int64_t)(row0 + r) * N + col] = v;
-    }
+    float out = ag[v];
+    if (UP) out = out / (1.0f + expf(-out)) * au[v];
+    C[(int64_t)(row0 + r) * N + col] = out;
   }
 }
 
@@ -572,7 +575,7 @@ hipError_t launch_gemm_up(const Problem& p, const void* X, const int32_t* perm,
                              mtiles, p.E, offsets, p.rows_max, stream_rows, s);
   }
   if (Hpre) return hipErrorNotSupported;      // the training path is bf16 only
-  const int NT = (p.n + 63) / 64;
+  const int NT = (p.n + kF32Cols - 1) / kF32Cols;
   hipLaunchKernelGGL(grouped_gemm_f32<true>, dim3((unsigned)(mtiles * kF32Sub * NT)), dim3(256), 0, s,
                      (const float*)X, perm, table, (const float*)W_gate, (const float*)W_up,
                      (float*)H, p.T, p.d, p.n, NT);
@@ -587,7 +590,7 @@ hipError_t launch_gemm_down(const Problem& p, const void* H, const int32_t* tabl
     return launch_bf16<false>((const uint16_t*)H, nullptr, table, (const uint16_t*)W_down,
                               nullptr, (uint16_t*)O, nullptr, p.T, p.n, p.d, mtiles, p.E, offsets,
                               p.rows_max, stream_rows, s);
-  const int NT = (p.d + 63) / 64;
+  const int NT = (p.d + kF32Cols - 1) / kF32Cols;
   hipLaunchKernelGGL(grouped_gemm_f32<false>, dim3((unsigned)(mtiles * kF32Sub * NT)), dim3(256), 0, s,
                      (const float*)H, nullptr, table, (const float*)W_down, nullptr, (float*)O,
                      p.T, p.n, p.d, NT);

@@ -27,6 +27,7 @@ namespace {
 using bf16x8 = __bf16 __attribute__((ext_vector_type(8)));
 using i16x4 = short __attribute__((ext_vector_type(4)));
 using f32x4 = float __attribute__((ext_vector_type(4)));
+using f32x16 = float __attribute__((ext_vector_type(16)));
 using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTok = 64;       // tokens per workgroup
@@ -376,23 +377,24 @@ __device__ __forceinline__ void topk_threshold_from_lds(float* L, int S, int64_t
   }
 }
 
-// Top-K by the selection the call asked for (sel: 0 sorted lanes and K
-// rounds of row maxima, 1 threshold bisection); the results are the same.
-template <int V, int R = 4>
-__device__ __forceinline__ void select_topk(int sel, float* L, int S, int64_t t0, int64_t T, int E,
-                                            int K, int32_t* __restrict__ ids,
-                                            float* __restrict__ gates, int* cntl) {
-  if (sel) topk_threshold_from_lds<V, R>(L, S, t0, T, E, K, ids, gates, cntl);
+// Top-K by the selection the kernel was built for (SEL: 0 sorted lanes and
+// K rounds of row maxima, 1 threshold bisection); the results are the same.
+// A template parameter, not a run-time branch: compiled into one kernel, the
+// bisection's registers made the default selection spill scalar registers.
+template <int SEL, int V, int R = 4>
+__device__ __forceinline__ void select_topk(float* L, int S, int64_t t0, int64_t T, int E, int K,
+                                            int32_t* __restrict__ ids, float* __restrict__ gates,
+                                            int* cntl) {
+  if constexpr (SEL == 1) topk_threshold_from_lds<V, R>(L, S, t0, T, E, K, ids, gates, cntl);
   else topk_from_lds<V, R>(L, S, t0, T, E, K, ids, gates, cntl);
 }
 
 // Shared tail: bias, optional export, selection.
 // PREPPED: the caller already added the bias and wrote -inf into the padding.
-template <int V, bool PREPPED = false>
+template <int SEL, int V, bool PREPPED = false>
 __device__ __forceinline__ void route_tail(float* L, int S, int64_t t0, int64_t T, int E, int K, int Epad,
                            const float* __restrict__ bias, float* __restrict__ logits,
-                           int32_t* __restrict__ ids, float* __restrict__ gates, int* cntl,
-                           int sel) {
+                           int32_t* __restrict__ ids, float* __restrict__ gates, int* cntl) {
   if (!PREPPED) {
     for (int idx = threadIdx.x; idx < kTok * Epad; idx += kThreads) {
       const int r = idx / Epad, e = idx - (idx / Epad) * Epad;
@@ -413,7 +415,7 @@ __device__ __forceinline__ void route_tail(float* L, int S, int64_t t0, int64_t 
     }
     __syncthreads();  // selection rewrites the rows being exported
   }
-  select_topk<V>(sel, L, S, t0, T, E, K, ids, gates, cntl);
+  select_topk<SEL, V>(L, S, t0, T, E, K, ids, gates, cntl);
 }
 
 // Per-block expert counts for the permutation: the selection above adds each
@@ -433,11 +435,11 @@ __device__ __forceinline__ void count_store(const int* cntl, int32_t* __restrict
 // NBW: 16-column blocks per wave; the padded expert range is 32*NBW.
 // The widest expert range (NBW = 8) needs the whole register file: one
 // workgroup per CU; narrower ones fit two.
-template <int NBW, bool VEC>
+template <int NBW, bool VEC, int SEL>
 __global__ __launch_bounds__(kThreads, (NBW >= 8) ? 1 : 2) void route_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
-    int d, int E, int K, int32_t* __restrict__ blockcnt, int64_t ldc, int sel) {
+    int d, int E, int K, int32_t* __restrict__ blockcnt, int64_t ldc) {
   constexpr int Epad = 32 * NBW;
   __shared__ int cntl[256];
   // X stages held in registers (prefetch depth); fewer when the weight tile is wide
@@ -579,8 +581,8 @@ __global__ __launch_bounds__(kThreads, (NBW >= 8) ? 1 : 2) void route_bf16_kerne
       }
   if (blockcnt) count_zero(cntl, kThreads);
   __syncthreads();
-  route_tail<2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates, blockcnt ? cntl : nullptr,
-                      sel);
+  route_tail<SEL, 2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates,
+                           blockcnt ? cntl : nullptr);
   if (blockcnt) count_store(cntl, blockcnt, ldc, blockIdx.x, E, kThreads);
 }
 
@@ -666,12 +668,12 @@ __device__ __forceinline__ V pick4(const V (&a)[4], int j) {
   return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
 }
 
-template <int NBW>
+template <int NBW, int SEL>
 __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
     int d, int E, int K, int ksplit, float* __restrict__ partial, RouteJobs jobs,
-    int32_t* __restrict__ blockcnt, int64_t ldc, int sel) {
+    int32_t* __restrict__ blockcnt, int64_t ldc) {
   using G = RouteGeo<NBW>;
   constexpr int Epad = G::Epad, NST = G::NST, CPR = G::CPR;
   constexpr int XI = G::kXInstr, WI = G::kWInstr, CBW = G::CBW;
@@ -855,7 +857,7 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
     }
     __syncthreads();  // selection rewrites the rows being exported
   }
-  if (ids) select_topk<2 * NBW, kTok / (4 * G::NW)>(sel, L, G::S, t0, T, E, K, ids, gates,
+  if (ids) select_topk<SEL, 2 * NBW, kTok / (4 * G::NW)>(L, G::S, t0, T, E, K, ids, gates,
                                                        blockcnt ? cntl : nullptr);
   if (blockcnt) count_store(cntl, blockcnt, ldc, bx, E, G::kThreads);
 }
@@ -897,11 +899,11 @@ struct SelGeo {
   static constexpr int kCnt = TW * S * 4;            // per-block expert counts after the rows
   static constexpr int kLds = kCnt + 1024;
 };
-template <int NBW>
+template <int NBW, int SEL>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const float* __restrict__ scores, const float* __restrict__ bias, float* __restrict__ logits,
     int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T, int E, int K,
-    int32_t* __restrict__ blockcnt, int64_t ldc, int sel) {
+    int32_t* __restrict__ blockcnt, int64_t ldc) {
   using G = SelGeo<NBW>;
   constexpr int Epad = G::Epad, S = G::S, TW = G::TW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -946,39 +948,90 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
     }
     __syncthreads();  // selection rewrites the rows being exported
   }
-  select_topk<2 * NBW, G::R>(sel, L, S, t0, T, E, K, ids, gates, blockcnt ? cntl : nullptr);
+  select_topk<SEL, 2 * NBW, G::R>(L, S, t0, T, E, K, ids, gates, blockcnt ? cntl : nullptr);
   if (blockcnt) count_store(cntl, blockcnt, ldc, blockIdx.x, E, kThreads);
 }
 
-// ---------------------------------------------------------------- fp32 router (plain FMA)
+// ---------------------------------------------------------------- fp32 router (MFMA)
+// 64 tokens x Epad scores per workgroup: 32 x 32 blocks (2 token halves x
+// Epad/32 expert blocks, dealt to the 4 waves) with v_mfma_f32_32x32x2_f32
+// over 32-deep k slices of X and W_r staged in LDS (in the space the score
+// rows take afterwards).  A lane supplies X[token lane%32][k lane/32] and
+// W_r[k lane/32][expert lane%32] and ends with expert lane%32 of tokens
+// 8*(v/4) + 4*(lane/32) + v%4 of its block.
 template <int NBW>
+struct F32RouteGeo {
+  static constexpr int Epad = 32 * NBW, S = Epad + 16, TK = 32;
+  static constexpr int kBlocks = 2 * NBW;                 // 32 x 32 score blocks
+  static constexpr int kPerWave = (kBlocks + 3) / 4;
+  static constexpr int kXs = kTok * (TK + 1);             // floats, padded rows
+  static constexpr int kWs = TK * Epad;
+  static constexpr int kFloats = (kTok * S > kXs + kWs) ? kTok * S : kXs + kWs;
+};
+template <int NBW, int SEL>
 __global__ __launch_bounds__(kThreads) void route_f32_kernel(
     const float* __restrict__ X, const float* __restrict__ Wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
-    int d, int E, int K, int32_t* __restrict__ blockcnt, int64_t ldc, int sel) {
-  constexpr int Epad = 32 * NBW;
-  constexpr int S = Epad + 16;
-  __shared__ float L[kTok * S];
+    int d, int E, int K, int32_t* __restrict__ blockcnt, int64_t ldc) {
+  using G = F32RouteGeo<NBW>;
+  constexpr int Epad = G::Epad, S = G::S, TK = G::TK;
+  __shared__ float L[G::kFloats];
   __shared__ int cntl[256];
+  float* Xs = L;                 // [kTok][TK + 1]
+  float* Ws = L + G::kXs;        // [TK][Epad]
   if (blockcnt) count_zero(cntl, kThreads);
   const int64_t t0 = (int64_t)blockIdx.x * kTok;
-  for (int idx = threadIdx.x; idx < kTok * Epad; idx += kThreads) {
-    const int r = idx / Epad, e = idx - (idx / Epad) * Epad;
-    float s = 0.f;
-    if (e < E && t0 + r < T) {
-      const float* x = X + (t0 + r) * (int64_t)d;
-      for (int i = 0; i < d; ++i) s = fmaf(x[i], Wr[(int64_t)i * E + e], s);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  f32x16 acc[G::kPerWave];
+#pragma unroll
+  for (int b = 0; b < G::kPerWave; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+  for (int k0 = 0; k0 < d; k0 += TK) {
+    for (int idx = tid; idx < kTok * TK; idx += kThreads) {
+      const int r = idx / TK, c = idx - (idx / TK) * TK;
+      Xs[r * (TK + 1) + c] = (t0 + r < T && k0 + c < d) ? X[(t0 + r) * (int64_t)d + k0 + c] : 0.f;
     }
-    L[r * S + e] = s;
+    for (int idx = tid; idx < TK * Epad; idx += kThreads) {
+      const int r = idx / Epad, e = idx - (idx / Epad) * Epad;
+      Ws[r * Epad + e] = (e < E && k0 + r < d) ? Wr[(int64_t)(k0 + r) * E + e] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < G::kPerWave; ++b) {
+      const int blk = w + 4 * b;                 // token half blk & 1, expert block blk >> 1
+      if (blk < G::kBlocks) {
+        const int tr = 32 * (blk & 1) + (lane & 31), ec = 32 * (blk >> 1) + (lane & 31);
+#pragma unroll
+        for (int kk = 0; kk < TK; kk += 2)
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(Xs[tr * (TK + 1) + kk + (lane >> 5)],
+                                                        Ws[(kk + (lane >> 5)) * Epad + ec], acc[b],
+                                                        0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // scores to the rows (the staging space is free after the last barrier)
+#pragma unroll
+  for (int b = 0; b < G::kPerWave; ++b) {
+    const int blk = w + 4 * b;
+    if (blk < G::kBlocks) {
+      const int ec = 32 * (blk >> 1) + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 32 * (blk & 1) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        L[r * S + ec] = acc[b][v];
+      }
+    }
   }
   __syncthreads();
-  route_tail<2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates, blockcnt ? cntl : nullptr,
-                      sel);
+  route_tail<SEL, 2 * NBW>(L, S, t0, T, E, K, Epad, bias, logits, ids, gates,
+                           blockcnt ? cntl : nullptr);
   if (blockcnt) count_store(cntl, blockcnt, ldc, blockIdx.x, E, kThreads);
 }
 
-template <int NBW>
-hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, const float* bias,
+template <int NBW, int SEL>
+hipError_t launch_route_sel(const Problem& p, const void* X, const void* W_r, const float* bias,
                             float* logits, int32_t* ids, float* gates, float* partial,
                             int32_t* blockcnt, hipStream_t s) {
   const int64_t ldc = blockcnt ? route_count_ld(p, partial != nullptr) : 0;
@@ -986,7 +1039,7 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
   if (p.bf16) {
     if (p.E % 8 == 0) {
       const int ksplit = partial ? route_ksplit(p) : 1;
-      auto* kern = route_staged_kernel<NBW>;
+      auto* kern = route_staged_kernel<NBW, SEL>;
       hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            RouteGeo<NBW>::kLds);
@@ -994,7 +1047,7 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
       hipLaunchKernelGGL(kern, dim3(grid.x, (unsigned)ksplit), dim3(RouteGeo<NBW>::kThreads),
                          (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)W_r,
                          bias, logits, ids, gates, p.T, p.d, p.E, p.K, ksplit, partial,
-                         RouteJobs{}, ksplit > 1 ? nullptr : blockcnt, ldc, p.sel);
+                         RouteJobs{}, ksplit > 1 ? nullptr : blockcnt, ldc);
       if (ksplit > 1) {
         err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -1004,24 +1057,32 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
         err = hipGetLastError();
         if (err != hipSuccess) return err;
         constexpr int kSelLds = SelGeo<NBW>::kLds, TW = SelGeo<NBW>::TW;
-        auto* sel = route_select_kernel<NBW>;
+        auto* sel = route_select_kernel<NBW, SEL>;
         err = hipFuncSetAttribute(reinterpret_cast<const void*>(sel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kSelLds);
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(sel, dim3((unsigned)((p.T + TW - 1) / TW)), dim3(kThreads),
                            (size_t)kSelLds, s, partial, bias, logits, ids, gates, p.T, p.E, p.K,
-                           blockcnt, ldc, p.sel);
+                           blockcnt, ldc);
       }
     } else
-      hipLaunchKernelGGL((route_bf16_kernel<NBW, false>), grid, dim3(kThreads), 0, s,
+      hipLaunchKernelGGL((route_bf16_kernel<NBW, false, SEL>), grid, dim3(kThreads), 0, s,
                          (const uint16_t*)X, (const uint16_t*)W_r, bias, logits, ids, gates, p.T,
-                         p.d, p.E, p.K, blockcnt, ldc, p.sel);
+                         p.d, p.E, p.K, blockcnt, ldc);
   } else {
-    hipLaunchKernelGGL((route_f32_kernel<NBW>), grid, dim3(kThreads), 0, s, (const float*)X,
+    hipLaunchKernelGGL((route_f32_kernel<NBW, SEL>), grid, dim3(kThreads), 0, s, (const float*)X,
                        (const float*)W_r, bias, logits, ids, gates, p.T, p.d, p.E, p.K, blockcnt,
-                       ldc, p.sel);
+                       ldc);
   }
   return hipGetLastError();
+}
+
+template <int NBW>
+hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, const float* bias,
+                            float* logits, int32_t* ids, float* gates, float* partial,
+                            int32_t* blockcnt, hipStream_t s) {
+  if (p.sel == 1) return launch_route_sel<NBW, 1>(p, X, W_r, bias, logits, ids, gates, partial, blockcnt, s);
+  return launch_route_sel<NBW, 0>(p, X, W_r, bias, logits, ids, gates, partial, blockcnt, s);
 }
 
 }  // namespace
@@ -1029,7 +1090,7 @@ hipError_t launch_route_nbw(const Problem& p, const void* X, const void* W_r, co
 namespace {
 template <int NBW>
 hipError_t launch_jobs_nbw(int64_t T, int d, const RouteJobs& jobs, const void* X, hipStream_t s) {
-  auto* kern = route_staged_kernel<NBW>;
+  auto* kern = route_staged_kernel<NBW, 0>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        RouteGeo<NBW>::kLds);
@@ -1037,7 +1098,7 @@ hipError_t launch_jobs_nbw(int64_t T, int d, const RouteJobs& jobs, const void* 
   hipLaunchKernelGGL(kern, dim3((unsigned)(jobs.n * jobs.nblk), 1), dim3(RouteGeo<NBW>::kThreads),
                      (size_t)RouteGeo<NBW>::kLds, s, (const uint16_t*)X, (const uint16_t*)nullptr,
                      (const float*)nullptr, (float*)nullptr, (int32_t*)nullptr, (float*)nullptr, T,
-                     d, 0, 1, 1, (float*)nullptr, jobs, (int32_t*)nullptr, (int64_t)0, 0);
+                     d, 0, 1, 1, (float*)nullptr, jobs, (int32_t*)nullptr, (int64_t)0);
   return hipGetLastError();
 }
 
