@@ -40,6 +40,12 @@
 //   it about 2% and 6% faster).
 // * Workgroup ids are remapped so that consecutive tiles (same expert, same
 //   token rows) run on the same XCD and share its L2.
+// * Optionally (stream_rows > 0) the grid also holds one weight-streaming
+//   block (gemm_stream.hpp) per expert and column block, after every tile:
+//   experts with at most stream_rows rows are computed there instead of by
+//   their single, mostly empty tile.
+//
+// fp32 kernel (correctness-sized layers): fp32 MFMA on 64 x 64 tiles.
 #include "gemm_stream.hpp"
 
 namespace moe {

@@ -7,27 +7,17 @@
 // moved is weight: the work is bound by reading each active expert's
 // weights once from HBM, so the kernel is organised around that stream.
 //
-// * One workgroup (4 waves) owns one expert and one block of 256 weight
-//   columns (up: 128 W_gate columns + the same 128 W_up columns, so SwiGLU is
-//   register-local; down: 256 W_down columns).  Experts without rows exit
-//   at once; only active experts' weights are read.  Measured at the decode
+// * The body (gemm_stream.hpp) runs here on 4 waves, one workgroup per
+//   expert and block of 256 weight columns; experts without rows exit at
+//   once, so only active experts' weights are read.  Measured at the decode
 //   size (T=64, d=4096, E=256, n=512) with cached copies: the weight stream
 //   ran at 4.7-4.9 TB/s whether or not the MFMAs ran and for 3 to 8 stages,
 //   i.e. bound by the memory system for these strided 512-byte row pieces
 //   (128-column blocks: 4.5-4.75 TB/s).  The weight copies carry the
 //   non-temporal hint (each weight is read once per launch): that lifted the
 //   up projection from 374 to 305 us at this size.
-// * The expert's rows are taken in passes of up to 64 (four 16-row MFMA
-//   blocks; 32 when the batch averages at most 16 rows per expert); a pass
-//   streams the column block over the whole k range through four LDS
-//   stages (64 k each), filled with global_load_lds_dwordx4 and counted with
-//   explicit vmcnt waits, three stages in flight.  Row blocks past the pass's
-//   last row skip their MFMAs.
-// * 16x16x32 bf16 MFMA.  Token rows (gathered through perm_token for up)
-//   sit in LDS with the 128-byte-row XOR swizzle and are read with
-//   ds_read_b128; weight rows keep the natural [k][n] order (256-byte rows,
-//   XOR-swizzled) and are read with ds_read_b64_tr_b16.  Both reads are
-//   bank-conflict free.
+// * Rows are taken in passes of 64, or 32 when the batch averages at most 16
+//   rows per expert (a smaller token tile leaves more LDS to weights).
 #include "gemm_stream.hpp"
 
 namespace moe {

@@ -22,9 +22,12 @@
 //                 uses a top-K row and a top-K column.
 //   omni_count / omni_scan / omni_scatter / omni_rank
 //                 (expert, token) permutation over N = N_r*N_c experts:
-//                 counts, exclusive scan, a scatter into each expert's segment
-//                 in arrival order, then one wave per expert ranks its entries
-//                 by token (distinct keys) so the order is deterministic;
+//                 counts (in the whole-layer call, omni_select counts its
+//                 winners itself into counts that the projection launch
+//                 cleared), exclusive scan in one launch, a scatter into each
+//                 expert's segment in arrival order, then one wave per expert
+//                 ranks its entries by token (distinct keys) so the order is
+//                 deterministic;
 //   omni_expert   one wave per active expert: w_in loaded once, then for each
 //                 of its tokens a[s] = silu(x_t . w_in) (fp32 dot, wave sum);
 //   omni_combine  one wave per token: y_t = sum_k g_k a[slot] w_out[id_k]

@@ -18,7 +18,10 @@
 // DPP row selects the top K of its tokens on order-preserving int32 keys:
 // integer max / min reductions need no NaN canonicalisation, and folding
 // -0.0 into +0.0 before keying makes the two zeros tie (then the lower id
-// wins, as the oracle rules).
+// wins, as the oracle rules).  The selection is either K rounds of row
+// maxima over lanes sorted once (default) or the threshold bisection of
+// [P4] §4.3 (MOE_FLAG_TOPK_THRESHOLD); both give the same ids, order and
+// gates.  The fp32 router uses fp32 MFMA (32x32x2) on LDS-staged slices.
 #include "moe_internal.hpp"
 
 namespace moe {
