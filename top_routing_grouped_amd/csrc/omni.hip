@@ -199,11 +199,17 @@ __device__ __forceinline__ void wave_top(const uint32_t* k, const int* id, int r
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const uint32_t mk = lane < r ? (uint32_t)lk[lane] : 0u;
   const int mi = lane < r ? li[lane] : 0x7FFFFFFF;
+  // each winner's rank: the winners before it in (key desc, id asc), read
+  // four at a time from LDS (every lane reads the same entries: broadcast)
   int rank = 0;
-  for (int q = 0; q < r; ++q) {
-    const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)mk, q);
-    const int iq = __builtin_amdgcn_readlane(mi, q);
-    rank += (kq > mk || (kq == mk && iq < mi)) ? 1 : 0;
+  for (int q = 0; q < r; q += 4) {
+    const int4 kq = *reinterpret_cast<const int4*>(lk + q);
+    const int4 iq = *reinterpret_cast<const int4*>(li + q);
+    const uint32_t kv[4] = {(uint32_t)kq.x, (uint32_t)kq.y, (uint32_t)kq.z, (uint32_t)kq.w};
+    const int iv[4] = {iq.x, iq.y, iq.z, iq.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      rank += (q + u < r && (kv[u] > mk || (kv[u] == mk && iv[u] < mi))) ? 1 : 0;
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -225,8 +231,8 @@ __global__ __launch_bounds__(kThreads) void omni_select_kernel(
     int Nr, int Nc, int K, int32_t* __restrict__ counts) {
   __shared__ int ckey[kWaves][kMaxCand];
   __shared__ int cid[kWaves][kMaxCand];
-  __shared__ int tk[kWaves][128];
-  __shared__ int ti[kWaves][128];
+  __shared__ __attribute__((aligned(16))) int tk[kWaves][128];   // 16-byte rank reads
+  __shared__ __attribute__((aligned(16))) int ti[kWaves][128];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * kWaves + wv;
   if (t >= T) return;                                  // wave-uniform; no block barrier below
