@@ -403,15 +403,16 @@ __global__ __launch_bounds__(kThreads) void omni_scatter_kernel(const int32_t* _
 
 // One wave per expert: each entry's final place is its rank among the
 // segment's (token*K + k) keys (distinct), i.e. ascending token order.
-// Segments of at most 64 entries: each lane counts the smaller keys directly
-// (c compares per lane).  Longer ones, when T fits the wave's LDS mask
+// Segments of at most 64 entries: each lane loads one entry and counts the
+// smaller keys across the lanes (readlane; one memory round trip per
+// segment).  Longer ones, when T fits the wave's LDS mask
 // (mask_words = ceil(T/32) > 0): an expert occurs at most once per token, so
 // the wave sets one bit per token in a T-bit mask, takes exclusive prefix
 // popcounts over the mask words, and an entry's rank is the prefix of its
 // token's word plus the popcount of the lower bits: O(T/32 + c) per expert
 // instead of O(c^2/64) (a hot expert chosen by most of 32768 tokens would
-// otherwise serialise ~16M loads on one wave).
-constexpr int kRankDirect = 64;
+// otherwise serialise ~16M loads on one wave).  Beyond that T, long
+// segments fall back to direct counting over global memory.
 __global__ __launch_bounds__(kThreads) void omni_rank_kernel(const int32_t* __restrict__ offsets,
                                                              const int32_t* __restrict__ tmp_tk,
                                                              int32_t* __restrict__ perm,
@@ -423,7 +424,18 @@ __global__ __launch_bounds__(kThreads) void omni_rank_kernel(const int32_t* __re
   const int e = blockIdx.x * kWaves + wv;
   if (e >= N) return;
   const int off = offsets[e], c = offsets[e + 1] - off;
-  if (c <= kRankDirect || mask_words == 0) {
+  if (c <= 64) {
+    // one load per entry, then the smaller keys counted across the lanes
+    const int mine = lane < c ? tmp_tk[off + lane] : 0x7FFFFFFF;
+    int rank = 0;
+    for (int j = 0; j < c; ++j) rank += __builtin_amdgcn_readlane(mine, j) < mine ? 1 : 0;
+    if (lane < c) {
+      perm[off + rank] = mine / K;
+      inv[mine] = off + rank;
+    }
+    return;
+  }
+  if (mask_words == 0) {
     for (int i0 = 0; i0 < c; i0 += 64) {
       const int i = i0 + lane;
       const int mine = i < c ? tmp_tk[off + i] : 0x7FFFFFFF;
