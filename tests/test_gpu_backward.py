@@ -105,6 +105,35 @@ def test_backward_repeats_bitwise():
         assert torch.equal(g1[name], g2[name]), name
 
 
+def test_threshold_selection_in_training():
+    """MOE_FLAG_TOPK_THRESHOLD in moe_forward_train: Y, the saved state and
+    every gradient bit-equal to the default flags' (the backward accepts the
+    same desc)."""
+    T, d, E, K, n = 700, 256, 16, 4, 128
+    print(f"case threshold training T={T} d={d} E={E} K={K} n={n}", flush=True)
+    inp = mi.draw(T, d, E, n, torch.bfloat16, seed=19, bias="zipf")
+    dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    dY = mi.draw_grad_output(T, d, torch.bfloat16, seed=20).cuda()
+    outs = []
+    for flags in (0, moe.MOE_FLAG_TOPK_THRESHOLD):
+        Y, saved, desc = moe.forward_train(dev["X"], dev["W_r"], dev["W_gate"], dev["W_up"],
+                                           dev["W_down"], K, 1.0, bias=dev["bias"], flags=flags)
+        g = moe.backward(desc, saved, dev["X"], dev["W_r"], dev["W_gate"], dev["W_up"],
+                         dev["W_down"], dY)
+        outs.append((Y, saved, g))
+    torch.cuda.synchronize()
+    (Y0, s0, g0), (Y1, s1, g1) = outs
+    assert torch.equal(Y1, Y0)
+    v0, v1 = moe.saved_view(desc, s0), moe.saved_view(desc, s1)
+    N = int(v0["offsets"][E].item())
+    for key in ("logits", "ids", "gates", "inv_slot", "counts", "offsets"):
+        assert torch.equal(v1[key], v0[key]), key
+    assert torch.equal(v1["perm_token"][:N], v0["perm_token"][:N])
+    assert torch.equal(v1["preact"][:N], v0["preact"][:N])
+    for key in g0:
+        assert torch.equal(g1[key], g0[key]), key
+
+
 def test_backward_of_an_empty_batch_zeroes_the_weight_gradients():
     d, E, K, n = 128, 8, 2, 128
     desc = moe.make_desc(0, d, E, K, n, "bf16")

@@ -418,11 +418,14 @@ def forward(X, W_r, W_gate, W_up, W_down, K, capacity_factor=0.0, bias=None, ws=
     return Y
 
 
-def forward_train(X, W_r, W_gate, W_up, W_down, K, capacity_factor=0.0, bias=None, ws=None):
+def forward_train(X, W_r, W_gate, W_up, W_down, K, capacity_factor=0.0, bias=None, ws=None,
+                  flags=0):
     """Training forward (bf16).  Returns (Y [T, d], saved, desc); pass saved and
-    desc unchanged to ``backward``."""
+    desc unchanged to ``backward``.  `flags` may carry MOE_FLAG_GEMM_TILED and
+    MOE_FLAG_TOPK_THRESHOLD."""
     import torch
     desc = _desc_for(X, W_gate, K, capacity_factor)
+    desc.flags = int(flags)
     if ws is None:
         ws = workspace(desc, MOE_WS_FORWARD, X.device)
     saved = workspace(desc, MOE_WS_SAVED, X.device)
