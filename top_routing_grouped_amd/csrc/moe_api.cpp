@@ -265,6 +265,16 @@ moe_status run_route_permute(const moe::Problem& p, const void* X, const void* W
                              int32_t* raw, int32_t* perm, int32_t* inv, int32_t* table,
                              hipStream_t s) {
   const bool split = partial != nullptr;
+  if (moe::permute_blocks(p.T) == 1) {
+    // one token block (decode-sized): the one-workgroup permutation counts
+    // for itself, so the router writes no per-block counts (5.7 instead of
+    // 14.6 us for the permutation at T = 64)
+    MOE_TRY(hip_status(moe::launch_route(p, X, W_r, bias, logits, ids, gates, partial, s),
+                       "route launch"));
+    return hip_status(moe::launch_permute_one_block(p, ids, raw, counts, offsets, table, perm, inv,
+                                                    s),
+                      "permutation launch");
+  }
   MOE_TRY(hip_status(moe::launch_route(p, X, W_r, bias, logits, ids, gates, partial, s, blockcnt),
                      "route launch"));
   return hip_status(moe::launch_permute_fused(p, ids, blockcnt, moe::route_count_block(p, split),
