@@ -649,8 +649,8 @@ __device__ __forceinline__ void wait_stages(int pending) {
 
 // With ksplit > 1 the k range is split over gridDim.y workgroups per token
 // block (for batches too small to fill the chip): each writes its raw fp32
-// partial scores to partial[ks][T][Epad]; route_sum_kernel and
-// route_select_kernel finish.
+// partial scores to partial[ks][T][Epad]; route_select_kernel adds them and
+// finishes.
 // Router matrices over the same tokens that share one launch (fp32 scores
 // only, no bias or selection): job j takes workgroups j*nblk .. (j+1)*nblk-1,
 // multiplying X by E[j] columns of a matrix whose rows (and score rows) are
@@ -869,28 +869,10 @@ __global__ __launch_bounds__(RouteGeo<NBW>::kThreads, 1) void route_staged_kerne
 // order (a fixed order: the result does not depend on which workgroup of the
 // router finished first).  One float4 of scores per thread, spread over as
 // many workgroups as the T x Epad scores need.
-__global__ __launch_bounds__(kThreads) void route_sum_kernel(float* __restrict__ partial,
-                                                             int ksplit, int64_t n4) {
-  using f4 = float __attribute__((ext_vector_type(4)));
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n4) return;
-  f4* P = reinterpret_cast<f4*>(partial);
-  f4 v = P[i];
-  int ks = 1;
-  for (; ks + 4 <= ksplit; ks += 4) {        // four loads in flight, summed in order
-    const f4 a = P[(int64_t)ks * n4 + i], b = P[(int64_t)(ks + 1) * n4 + i];
-    const f4 c = P[(int64_t)(ks + 2) * n4 + i], d = P[(int64_t)(ks + 3) * n4 + i];
-    v += a;
-    v += b;
-    v += c;
-    v += d;
-  }
-  for (; ks < ksplit; ++ks) v += P[(int64_t)ks * n4 + i];
-  P[i] = v;
-}
 
-// Split-k finish, part 2: the summed scores of TW tokens per workgroup, plus
-// bias (-inf in the padding), then the selection by 4 waves of 4R tokens.
+// Split-k finish: the partial scores of TW tokens per workgroup added in split
+// order (a separate summing launch took 4.7 us at the decode size), plus bias
+// (-inf in the padding), then the selection by 4 waves of 4R tokens.
 // Wide expert ranges (E > 64) take TW = 16 and one token per DPP row, so the
 // serial selection chains of a small batch spread over several CUs (decode,
 // T = 64, E = 256: the route 30 -> 21 us); narrower ones keep TW = 64, R = 4.
@@ -906,7 +888,7 @@ template <int NBW, int SEL>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const float* __restrict__ scores, const float* __restrict__ bias, float* __restrict__ logits,
     int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T, int E, int K,
-    int32_t* __restrict__ blockcnt, int64_t ldc) {
+    int32_t* __restrict__ blockcnt, int64_t ldc, int ksplit) {
   using G = SelGeo<NBW>;
   constexpr int Epad = G::Epad, S = G::S, TW = G::TW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -929,11 +911,29 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const int e = 4 * c4 + j;
     bv[j] = (bias && e < E) ? bias[e] : 0.f;
   }
+  // scores[ks][T][Epad] holds the ksplit partial sums; they are added in
+  // split order (split 0 first), up to four splits' loads in flight
   f4 v[kPer];
+  int64_t roff[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int64_t t = (t0 + r0 + kRowStep * i < T) ? t0 + r0 + kRowStep * i : T - 1;
-    v[i] = *reinterpret_cast<const f4*>(scores + t * Epad + 4 * c4);
+    roff[i] = t * Epad + 4 * c4;
+    v[i] = *reinterpret_cast<const f4*>(scores + roff[i]);
+  }
+  const int64_t plane = T * Epad;
+  for (int ks = 1; ks < ksplit; ks += 4) {
+    f4 a[4][kPer];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (ks + u < ksplit) a[u][i] = *reinterpret_cast<const f4*>(scores + (ks + u) * plane + roff[i]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (ks + u < ksplit) v[i] += a[u][i];
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -1054,11 +1054,6 @@ hipError_t launch_route_sel(const Problem& p, const void* X, const void* W_r, co
       if (ksplit > 1) {
         err = hipGetLastError();
         if (err != hipSuccess) return err;
-        const int64_t n4 = p.T * (int64_t)(32 * NBW) / 4;
-        hipLaunchKernelGGL(route_sum_kernel, dim3((unsigned)((n4 + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, s, partial, ksplit, n4);
-        err = hipGetLastError();
-        if (err != hipSuccess) return err;
         constexpr int kSelLds = SelGeo<NBW>::kLds, TW = SelGeo<NBW>::TW;
         auto* sel = route_select_kernel<NBW, SEL>;
         err = hipFuncSetAttribute(reinterpret_cast<const void*>(sel),
@@ -1066,7 +1061,7 @@ hipError_t launch_route_sel(const Problem& p, const void* X, const void* W_r, co
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(sel, dim3((unsigned)((p.T + TW - 1) / TW)), dim3(kThreads),
                            (size_t)kSelLds, s, partial, bias, logits, ids, gates, p.T, p.E, p.K,
-                           blockcnt, ldc);
+                           blockcnt, ldc, ksplit);
       }
     } else
       hipLaunchKernelGGL((route_bf16_kernel<NBW, false, SEL>), grid, dim3(kThreads), 0, s,
