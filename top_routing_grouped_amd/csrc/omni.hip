@@ -225,45 +225,64 @@ __device__ __forceinline__ void wave_top(const uint32_t* k, const int* id, int r
   *oi = lane < r ? li[64 + lane] : 0;
 }
 
+// Two waves per token: wave 2u of the workgroup takes token u's row axis and
+// wave 2u+1 its column axis (log-softmax, top min(K, axis)); the sorted lists
+// meet in LDS and the row wave goes on with the pairs.  One wave per token,
+// doing both axes in turn, took 45.3 instead of 43.7 us: little, because the
+// kernel is bound by the instructions all tokens issue, not by one token's
+// chain.
+constexpr int kSelTok = kWaves / 2;   // tokens per workgroup
 __global__ __launch_bounds__(kThreads) void omni_select_kernel(
     const float* __restrict__ p_r, const float* __restrict__ p_c, float* __restrict__ ls_r,
     float* __restrict__ ls_c, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
     int Nr, int Nc, int K, int32_t* __restrict__ counts) {
-  __shared__ int ckey[kWaves][kMaxCand];
-  __shared__ int cid[kWaves][kMaxCand];
+  __shared__ int ckey[kSelTok][kMaxCand];
+  __shared__ int cid[kSelTok][kMaxCand];
   __shared__ __attribute__((aligned(16))) int tk[kWaves][128];   // 16-byte rank reads
   __shared__ __attribute__((aligned(16))) int ti[kWaves][128];
+  __shared__ float lval[kSelTok][2][kMaxK];                       // sorted axis lists
+  __shared__ int lid[kSelTok][2][kMaxK];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * kWaves + wv;
-  if (t >= T) return;                                  // wave-uniform; no block barrier below
-  float vr[4], vc[4];
-  axis_log_softmax(p_r + t * Nr, Nr, ls_r ? ls_r + t * Nr : nullptr, vr);
-  axis_log_softmax(p_c + t * Nc, Nc, ls_c ? ls_c + t * Nc : nullptr, vc);
+  const int u = wv >> 1, axis = wv & 1;
+  const int64_t t = (int64_t)blockIdx.x * kSelTok + u;
+  const bool live = t < T;                             // wave-uniform
   const int R = K < Nr ? K : Nr, C = K < Nc ? K : Nc;
-  uint32_t kr[4], kc[4];
-  int ir[4], ic[4];
+  if (live) {
+    const int n = axis ? Nc : Nr, r = axis ? C : R;
+    const float* p = axis ? p_c + t * Nc : p_r + t * Nr;
+    float* ls = axis ? (ls_c ? ls_c + t * Nc : nullptr) : (ls_r ? ls_r + t * Nr : nullptr);
+    float v[4];
+    axis_log_softmax(p, n, ls, v);
+    uint32_t key[4];
+    int id[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = lane + 64 * j;
-    kr[j] = i < Nr ? ukey(vr[j]) : 0u;
-    kc[j] = i < Nc ? ukey(vc[j]) : 0u;
-    ir[j] = ic[j] = i;
+    for (int j = 0; j < 4; ++j) {
+      const int i = lane + 64 * j;
+      key[j] = i < n ? ukey(v[j]) : 0u;
+      id[j] = i;
+    }
+    uint32_t wk;
+    int wi;
+    wave_top<4>(key, id, r, &wk, &wi, tk[wv], ti[wv]);
+    if (lane < r) {
+      lval[u][axis][lane] = unukey(wk);
+      lid[u][axis][lane] = wi;
+    }
   }
-  uint32_t rk, ck;
-  int ri, ci;
-  wave_top<4>(kr, ir, R, &rk, &ri, tk[wv], ti[wv]);
-  wave_top<4>(kc, ic, C, &ck, &ci, tk[wv], ti[wv]);
-  const float rv = unukey(rk), cv = unukey(ck);
+  __syncthreads();                                     // both axes' lists of every token
+  if (!live || axis == 1) return;
+  const float cv = lane < C ? lval[u][1][lane] : 0.f;
+  const int ci = lane < C ? lid[u][1][lane] : 0;
   // candidate pairs (i, j) of axis ranks with (i+1)(j+1) <= K; lane j holds
   // column rank j, row rank i is broadcast
-  int* cks = ckey[wv];
-  int* cis = cid[wv];
+  int* cks = ckey[u];
+  int* cis = cid[u];
   int nc = 0;
   for (int i = 0; i < R; ++i) {
     int jmax = K / (i + 1);
     jmax = jmax < C ? jmax : C;
-    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rv), i));
-    const int ar = __builtin_amdgcn_readlane(ri, i);
+    const float a = lval[u][0][i];                     // LDS broadcast
+    const int ar = lid[u][0][i];
     if (lane < jmax) {
       cks[nc + lane] = (int)ukey(a + cv);
       cis[nc + lane] = ar * Nc + ci;
@@ -277,10 +296,10 @@ __global__ __launch_bounds__(kThreads) void omni_select_kernel(
   uint32_t mk[kPer];
   int mi[kPer];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int c = lane + 64 * u;
-    mk[u] = c < nc ? (uint32_t)cks[c] : 0u;
-    mi[u] = c < nc ? cis[c] : (1 << 17);
+  for (int q = 0; q < kPer; ++q) {
+    const int c = lane + 64 * q;
+    mk[q] = c < nc ? (uint32_t)cks[c] : 0u;
+    mi[q] = c < nc ? cis[c] : (1 << 17);
   }
   uint32_t sk;
   int sid;
@@ -695,7 +714,7 @@ hipError_t launch_omni_route(const OmniProblem& p, const void* X, const void* W_
     err = launch_route(axis_problem(p, p.Nc), X, W_c, nullptr, w.p_c, w.ids1, w.gates1, nullptr, s);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(omni_select_kernel, dim3((unsigned)((p.T + kWaves - 1) / kWaves)),
+  hipLaunchKernelGGL(omni_select_kernel, dim3((unsigned)((p.T + kSelTok - 1) / kSelTok)),
                      dim3(kThreads), 0, s, w.p_r, w.p_c, ls_r, ls_c, ids, gates, p.T, p.Nr, p.Nc,
                      p.K, counts);
   return hipGetLastError();
