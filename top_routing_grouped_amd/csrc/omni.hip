@@ -88,6 +88,8 @@ __device__ __forceinline__ float wave_maxf(float x) {
   return unskey(wave_max_i(skey(x)));
 }
 
+static_assert(kMaxAxis == 4 * 64, "an axis row is held as 4 scores per lane");
+
 // Log-softmax of one axis row (n <= 256 scores, lane holds entries lane + 64 j);
 // exports it when `out` is given; returns the lane's values (-inf padding).
 __device__ __forceinline__ void axis_log_softmax(const float* p, int n, float* out, float v[4]) {
