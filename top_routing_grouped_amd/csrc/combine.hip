@@ -22,19 +22,21 @@ constexpr int kTokPerBlock = kThreads / 64;
 // group of 8 slots and gates is read with one vector load and broadcast with
 // readlane, so they live in scalar registers.  A lane owns CB chunks of the row
 // (64 lanes x CB x 16 bytes = 2048 bf16 with CB = 4) and issues the loads of
-// all of them for 8 experts at once -- one memory round trip per token row
-// block -- then accumulates in k order.  Dropped assignments point their
-// load at a kept row of the same token (no extra HBM traffic) and are left
-// out of the sum by a select, so the load sequence has no branches.  O is
-// read once and Y written once, both with the non-temporal hint (9% faster
-// than cached accesses at the Qwen3 shape: the stream does not fill L2).
-template <int CB>
+// all of them for KG experts at once (KG = 4 for K <= 4, else 8) -- one
+// memory round trip per token row block -- then accumulates in k order.
+// Dropped assignments point their load at a kept row of the same token (no
+// extra HBM traffic) and are left out of the sum by a select, so the load
+// sequence has no branches.  A group with no kept entry at all issues no
+// loads (a wave-uniform branch): pointing them at row 0 of O made that row
+// one hot spot in L2 for every token without a kept row.  O is read once
+// and Y written once, both with the non-temporal hint (9% faster than cached
+// accesses at the Qwen3 shape: the stream does not fill L2).
+template <int CB, int KG>
 __global__ __launch_bounds__(kThreads) void combine_bf16(const uint16_t* __restrict__ O,
                                                         const float* __restrict__ gates,
                                                         const int32_t* __restrict__ inv,
                                                         uint16_t* __restrict__ Y, int64_t T, int d,
                                                         int K) {
-  constexpr int KG = 8;                       // experts per load group
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)__builtin_amdgcn_readfirstlane(
       (int)(blockIdx.x * kTokPerBlock + (threadIdx.x >> 6)));
@@ -72,6 +74,10 @@ __global__ __launch_bounds__(kThreads) void combine_bf16(const uint16_t* __restr
           ok[u] = (k0 + u < K) && sl[u] >= 0;
         }
       }
+      bool any = false;
+#pragma unroll
+      for (int u = 0; u < KG; ++u) any = any || ok[u];
+      if (!any) continue;                     // nothing kept in this group: no loads
 #pragma unroll
       for (int u = KG - 1; u >= 0; --u) fallback = ok[u] ? sl[u] : fallback;
 #pragma unroll
@@ -135,8 +141,11 @@ __global__ __launch_bounds__(kThreads) void combine_f32(const float* __restrict_
 hipError_t launch_combine(const Problem& p, const void* O, const float* gates,
                           const int32_t* inv_slot, void* Y, hipStream_t s) {
   const dim3 grid((unsigned)((p.T + kTokPerBlock - 1) / kTokPerBlock));
-  if (p.bf16)
-    hipLaunchKernelGGL(combine_bf16<4>, grid, dim3(kThreads), 0, s, (const uint16_t*)O, gates,
+  if (p.bf16 && p.K <= 4)
+    hipLaunchKernelGGL((combine_bf16<4, 4>), grid, dim3(kThreads), 0, s, (const uint16_t*)O, gates,
+                       inv_slot, (uint16_t*)Y, p.T, p.d, p.K);
+  else if (p.bf16)
+    hipLaunchKernelGGL((combine_bf16<4, 8>), grid, dim3(kThreads), 0, s, (const uint16_t*)O, gates,
                        inv_slot, (uint16_t*)Y, p.T, p.d, p.K);
   else
     hipLaunchKernelGGL(combine_f32, grid, dim3(kThreads), 0, s, (const float*)O, gates, inv_slot,
