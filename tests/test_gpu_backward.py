@@ -55,17 +55,18 @@ def _check_saved_routing(sv, rec, N):
 
 
 SMALL = [
-    # T, d, E, K, n, capacity factor, Zipf bias
-    (300, 128, 4, 2, 192, 0.0, False),    # ragged row tiles; n below one column tile
-    (517, 256, 8, 3, 320, 0.6, True),     # capacity drops; n spans a ragged second tile
-    (64, 128, 5, 5, 64, 0.0, False),      # K = E; E not a multiple of 8
-    (1000, 512, 16, 4, 256, 1.0, False),
-    (3, 64, 2, 1, 64, 0.0, False),        # fewer tokens than one row block
+    # T, d, E, K, n, capacity factor, Zipf bias, some token loses every assignment
+    (300, 128, 4, 2, 192, 0.0, False, False),    # ragged row tiles; n below one column tile
+    (517, 256, 8, 3, 320, 0.6, True, False),     # capacity drops; n spans a ragged second tile
+    (64, 128, 5, 5, 64, 0.0, False, False),      # K = E; E not a multiple of 8
+    (1000, 512, 16, 4, 256, 1.0, False, False),
+    (3, 64, 2, 1, 64, 0.0, False, False),        # fewer tokens than one row block
+    (400, 128, 16, 2, 128, 0.25, True, True),    # heavy drops: tokens with no kept slot
 ]
 
 
-@pytest.mark.parametrize("T,d,E,K,n,cf,bias", SMALL)
-def test_small_training_layer_parity(T, d, E, K, n, cf, bias):
+@pytest.mark.parametrize("T,d,E,K,n,cf,bias,full_drop", SMALL)
+def test_small_training_layer_parity(T, d, E, K, n, cf, bias, full_drop):
     print(f"backward parity T={T} d={d} E={E} K={K} n={n} cf={cf} bias={bias}", flush=True)
     inp = mi.draw(T, d, E, n, torch.bfloat16, seed=T, bias="zipf" if bias else None)
     dY = mi.draw_grad_output(T, d, torch.bfloat16, seed=T)
@@ -83,6 +84,8 @@ def test_small_training_layer_parity(T, d, E, K, n, cf, bias):
                           bias=a["bias"], logits=L_gpu)
     N = int(fw["offsets"][-1])
     _check_saved_routing(sv, fw, N)
+    if full_drop:
+        assert bool((fw["inv_slot"] < 0).all(axis=1).any())
     pre = f32np(sv["preact"])[:N]
     assert mo.rel_l2(pre[:, :n], fw["Hg"]) <= TOL["bf16"]
     assert mo.rel_l2(pre[:, n:], fw["Hu"]) <= TOL["bf16"]

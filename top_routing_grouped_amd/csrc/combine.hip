@@ -22,7 +22,7 @@ constexpr int kTokPerBlock = kThreads / 64;
 // group of 8 slots and gates is read with one vector load and broadcast with
 // readlane, so they live in scalar registers.  A lane owns CB chunks of the row
 // (64 lanes x CB x 16 bytes = 2048 bf16 with CB = 4) and issues the loads of
-// all of them for KG experts at once (KG = 4 for K <= 4, else 8) -- one
+// all of them for KG experts at once (KG = 2, 4 or 8: the least >= K) -- one
 // memory round trip per token row block -- then accumulates in k order.
 // Dropped assignments point their load at a kept row of the same token (no
 // extra HBM traffic) and are left out of the sum by a select, so the load
@@ -141,7 +141,10 @@ __global__ __launch_bounds__(kThreads) void combine_f32(const float* __restrict_
 hipError_t launch_combine(const Problem& p, const void* O, const float* gates,
                           const int32_t* inv_slot, void* Y, hipStream_t s) {
   const dim3 grid((unsigned)((p.T + kTokPerBlock - 1) / kTokPerBlock));
-  if (p.bf16 && p.K <= 4)
+  if (p.bf16 && p.K <= 2)
+    hipLaunchKernelGGL((combine_bf16<4, 2>), grid, dim3(kThreads), 0, s, (const uint16_t*)O, gates,
+                       inv_slot, (uint16_t*)Y, p.T, p.d, p.K);
+  else if (p.bf16 && p.K <= 4)
     hipLaunchKernelGGL((combine_bf16<4, 4>), grid, dim3(kThreads), 0, s, (const uint16_t*)O, gates,
                        inv_slot, (uint16_t*)Y, p.T, p.d, p.K);
   else if (p.bf16)

@@ -754,16 +754,27 @@ __global__ __launch_bounds__(64 * kTokWaves) void token_backward_kernel(
 #pragma unroll
     for (int v = 0; v < 8; ++v) acc[v] = 0.f;
     for (int k0 = 0; k0 < K; k0 += KG) {
-      u32x4 o[KG];
+      // Entries that are dropped, or past K, load a kept row of the token
+      // (one already being read) and are left out of the sum; a group with
+      // no kept row loads nothing.  Sending them all to row 0 made that row
+      // a hot spot in L2 for every token that lost its assignments.
+      int sl[KG];
       bool ok[KG];
+      int fb = -1;
 #pragma unroll
       for (int u = 0; u < KG; ++u) {
         const int k = k0 + u < K ? k0 + u : K - 1;
-        const int s = s_slot[wv][k];
-        ok[u] = (k0 + u < K) && s >= 0;
-        o[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(dXs + (int64_t)(ok[u] ? s : 0) * d + c * 8));
+        sl[u] = s_slot[wv][k];
+        ok[u] = (k0 + u < K) && sl[u] >= 0;
       }
+#pragma unroll
+      for (int u = KG - 1; u >= 0; --u) fb = ok[u] ? sl[u] : fb;
+      if (fb < 0) continue;
+      u32x4 o[KG];
+#pragma unroll
+      for (int u = 0; u < KG; ++u)
+        o[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(dXs + (int64_t)(ok[u] ? sl[u] : fb) * d + c * 8));
 #pragma unroll
       for (int u = 0; u < KG; ++u)
 #pragma unroll
