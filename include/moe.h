@@ -22,6 +22,11 @@
  *   default stream).  They never synchronise, never copy to the host and
  *   never allocate: buffers and workspaces are the caller's.  Device faults
  *   therefore surface at the caller's next synchronisation.
+ * - Debugging: with MOE_DEBUG_SYNC=1 in the environment (read at every
+ *   call), each launch step synchronises `stream` and a kernel that failed
+ *   is reported by that call as MOE_ERR_HIP, the message naming the step.
+ *   Outputs are unchanged.  A stream being captured into a graph is not
+ *   synchronised.
  * - Argument checks happen on the host before anything is enqueued; a failed
  *   check enqueues nothing.  A failed kernel launch gives MOE_ERR_HIP.
  * - Layouts are row-major and contiguous.  X, W_r, W_gate, W_up, W_down, H,

@@ -6,6 +6,7 @@
 #include "moe.h"
 
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
 #include <cstring>
 #include <string>
@@ -229,7 +230,38 @@ moe_status check_ptrs(std::initializer_list<std::pair<const void*, const char*>>
   return MOE_OK;
 }
 
+// MOE_DEBUG_SYNC=1 in the environment (read at every step): each launch
+// step synchronises the entry point's stream and reports a kernel that
+// failed as MOE_ERR_HIP naming that step, instead of leaving the error to
+// the caller's next synchronisation.  Debug only; a stream that is being
+// captured into a graph is not synchronised.
+thread_local hipStream_t g_stream = nullptr;
+thread_local bool g_in_call = false;
+
+struct StreamScope {   // the entry point's stream, for the debug synchronisation
+  hipStream_t prev;
+  bool prev_in;
+  explicit StreamScope(void* s) : prev(g_stream), prev_in(g_in_call) {
+    g_stream = (hipStream_t)s;
+    g_in_call = true;
+  }
+  ~StreamScope() {
+    g_stream = prev;
+    g_in_call = prev_in;
+  }
+};
+
+bool debug_sync() {
+  const char* v = std::getenv("MOE_DEBUG_SYNC");
+  return v != nullptr && std::strcmp(v, "1") == 0;
+}
+
 moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess && g_in_call && debug_sync()) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(g_stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone)
+      e = hipStreamSynchronize(g_stream);
+  }
   if (e == hipSuccess) return MOE_OK;
   return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -368,6 +400,7 @@ moe_status moe_omni_workspace_size(const moe_omni_desc* desc, int32_t entry, siz
 moe_status moe_omni_route(const moe_omni_desc* desc, const void* X, const void* W_r,
                           const void* W_c, float* ls_r, float* ls_c, int32_t* ids, float* gates,
                           void* ws, size_t ws_bytes, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_omni(desc));
   if (desc->T == 0) return MOE_OK;
@@ -387,6 +420,7 @@ moe_status moe_omni_route(const moe_omni_desc* desc, const void* X, const void* 
 moe_status moe_omni_permute(const moe_omni_desc* desc, const int32_t* ids, int32_t* counts,
                             int32_t* offsets, int32_t* perm_token, int32_t* inv_slot, void* ws,
                             size_t ws_bytes, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_omni(desc));
   if (desc->T == 0) return MOE_OK;
@@ -406,6 +440,7 @@ moe_status moe_omni_permute(const moe_omni_desc* desc, const int32_t* ids, int32
 moe_status moe_omni_forward(const moe_omni_desc* desc, const void* X, const void* W_r,
                             const void* W_c, const void* W_in, const void* W_out, void* Y,
                             void* ws, size_t ws_bytes, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_omni(desc));
   if (desc->T == 0) return MOE_OK;
@@ -510,6 +545,7 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 moe_status moe_route(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
                      float* logits, int32_t* topk_ids, float* topk_gates, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, MOE_FLAG_TOPK_THRESHOLD));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
@@ -524,6 +560,7 @@ moe_status moe_route(const moe_desc* desc, const void* X, const void* W_r, const
 moe_status moe_route_ws(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
                         float* logits, int32_t* topk_ids, float* topk_gates, void* ws,
                         size_t ws_bytes, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, MOE_FLAG_TOPK_THRESHOLD));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
@@ -542,6 +579,7 @@ moe_status moe_route_ws(const moe_desc* desc, const void* X, const void* W_r, co
 moe_status moe_permute(const moe_desc* desc, const int32_t* topk_ids, int32_t* counts,
                        int32_t* offsets, int32_t* raw_counts, int32_t* perm_token,
                        int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
@@ -560,6 +598,7 @@ moe_status moe_route_permute(const moe_desc* desc, const void* X, const void* W_
                              float* topk_gates, int32_t* counts, int32_t* offsets,
                              int32_t* raw_counts, int32_t* perm_token, int32_t* inv_slot,
                              void* ws, size_t ws_bytes, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, MOE_FLAG_TOPK_THRESHOLD));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
@@ -581,6 +620,7 @@ static_assert(moe::kNoallocScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "scratch s
 moe_status moe_permute_noalloc(const moe_desc* desc, const int32_t* topk_ids, int32_t* counts,
                                int32_t* offsets, int32_t* raw_counts, int32_t* perm_token,
                                int32_t* inv_slot, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
@@ -602,6 +642,7 @@ moe_status moe_permute_noalloc(const moe_desc* desc, const int32_t* topk_ids, in
 moe_status moe_round_tokens(const moe_desc* desc, const int32_t* topk_ids, const float* topk_gates,
                             int32_t* counts, int32_t* offsets, int32_t* perm_token,
                             int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
@@ -622,6 +663,7 @@ moe_status moe_round_tokens(const moe_desc* desc, const int32_t* topk_ids, const
 moe_status moe_grouped_gemm_up(const moe_desc* desc, const void* X, const int32_t* offsets,
                                const int32_t* perm_token, const void* W_gate, const void* W_up,
                                void* H, void* ws, size_t ws_bytes, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, kGemmFlags));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
@@ -646,6 +688,7 @@ moe_status moe_grouped_gemm_up(const moe_desc* desc, const void* X, const int32_
 moe_status moe_grouped_gemm_down(const moe_desc* desc, const void* H, const int32_t* offsets,
                                  const void* W_down, void* O, void* ws, size_t ws_bytes,
                                  void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, kGemmFlags));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
@@ -668,6 +711,7 @@ moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* o
                            const int32_t* perm_token, const void* W_gate, const void* W_up,
                            const void* W_down, void* H, void* O, void* ws, size_t ws_bytes,
                            void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, kGemmFlags));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
@@ -697,6 +741,7 @@ moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* o
 
 moe_status moe_combine(const moe_desc* desc, const void* O, const float* topk_gates,
                        const int32_t* inv_slot, void* Y, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc));
   if (desc->T == 0) return MOE_OK;  // no-op; empty tensors may carry NULL
@@ -709,6 +754,7 @@ moe_status moe_combine(const moe_desc* desc, const void* O, const float* topk_ga
 moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
                        const void* W_gate, const void* W_up, const void* W_down, void* Y,
                        void* ws, size_t ws_bytes, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_GEMM_SKINNY | MOE_FLAG_TOKEN_ROUNDING |
                                MOE_FLAG_TOPK_THRESHOLD));
@@ -755,6 +801,7 @@ moe_status moe_forward_train(const moe_desc* desc, const void* X, const void* W_
                              const float* bias, const void* W_gate, const void* W_up,
                              const void* W_down, void* Y, void* saved, size_t saved_bytes,
                              void* ws, size_t ws_bytes, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_TOPK_THRESHOLD));
   if (desc->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the training path is bf16 only");
@@ -784,6 +831,7 @@ moe_status moe_backward(const moe_desc* desc, const void* X, const void* W_r, co
                         const void* W_up, const void* W_down, const void* dY, const void* saved,
                         size_t saved_bytes, void* dX, float* dW_r, float* dW_gate, float* dW_up,
                         float* dW_down, void* ws, size_t ws_bytes, void* stream) {
+  const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_TOPK_THRESHOLD));  // the latter: no effect here
   if (desc->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the training path is bf16 only");
