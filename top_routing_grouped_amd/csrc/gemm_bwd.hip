@@ -96,6 +96,18 @@ __device__ __forceinline__ TileInfo decode_tile(const int32_t* table, int NT) {
 // ---------------------------------------------------------------- alpha GEMM
 enum { kEpiStore = 0, kEpiDSwiGLU = 1 };
 
+// Column order of the dSwiGLU alpha GEMM's 32-column MFMA blocks (the
+// store-epilogue instance keeps the natural order, col(i) = i): lane l feeds
+// the MFMA the column-operand row sig(l % 32), sig swapping bits 2 and 3.  The
+// accumulator a lane holds for block column i (i = 8*(v/4) + 4*(lane/32) +
+// v%4) is then output column sig(i), so each lane ends with two runs of 8
+// adjacent columns (16p + 8*(lane/32) + 0..7, p = 0, 1) instead of four
+// runs of 4, and the dSwiGLU epilogue reads the matching pre-activations
+// with 16-byte loads (half as many requests as 8-byte ones).
+__device__ __forceinline__ int sig(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+template <int EPI>
+__device__ __forceinline__ int block_col(int i) { return EPI == kEpiDSwiGLU ? sig(i) : i; }
+
 // C[s][j] = sum_k A[row(s)][k] * B[e][j][k] for the slots s of each tile.
 //   A: [.][Kd] (rows gathered through perm when GATHER, else the slot rows)
 //   B: B0[e][N][Kb] for k < Kb and B1[e][N][Kb] for k >= Kb (Kd = Kb or 2 Kb)
@@ -177,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 1) void alpha_gemm(
 #pragma unroll
     for (int tb = 0; tb < kWTB; ++tb) a_off[tb][ks] = kmaj_off(wm * 128 + tb * 32 + (lane & 31), c);
 #pragma unroll
-    for (int cb = 0; cb < kWCB; ++cb) b_off[cb][ks] = kHalf + kmaj_off(wn * 64 + cb * 32 + (lane & 31), c);
+    for (int cb = 0; cb < kWCB; ++cb) b_off[cb][ks] = kHalf + kmaj_off(wn * 64 + cb * 32 + block_col<EPI>(lane & 31), c);
   }
   auto read_frags = [&](Frags<kWTB, kWCB>& f, int kt, int ks) {
     const unsigned char* S = smem + (kt & 1) * kStage;
@@ -236,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 1) void alpha_gemm(
   }
 
   // ---- epilogue.  A lane holds, for row lane%32 of block tb, columns
-  // 8*(v/4) + 4*(lane/32) + v%4 of block cb.  Output tiles go through the
+  // block_col(8*(v/4) + 4*(lane/32)) + v%4 of block cb.  Output tiles go through the
   // stage buffers (row-major bf16, 16-byte chunks XOR-swizzled by row) and
   // leave as whole rows.
   constexpr int kRowBytes = kTile * 2, kChunks = kRowBytes / 16;
@@ -249,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void alpha_gemm(
   };
   auto stage_value = [&](int ln, int tb, int cb, int v4, const float* v) {
     const int rloc = wm * 128 + tb * 32 + (ln & 31);
-    const int col = wn * 64 + cb * 32 + 8 * v4 + 4 * (ln >> 5);
+    const int col = wn * 64 + cb * 32 + block_col<EPI>(8 * v4 + 4 * (ln >> 5));
     const u32x2 pk = {dev::pack_bf16x2(v[0], v[1]), dev::pack_bf16x2(v[2], v[3])};
     const int chunk = (col >> 3) ^ (rloc & (kChunks - 1));
     *reinterpret_cast<u32x2*>(smem + rloc * kRowBytes + chunk * 16 + ((col >> 2) & 1) * 8) = pk;
@@ -302,8 +314,9 @@ __global__ __launch_bounds__(kThreads, 1) void alpha_gemm(
     gsl[tb] = (rloc < nrows) ? gs[row0 + rloc] : 0.f;
   }
   // Pre-activations of the lane's values: row rloc, columns
-  // ncol0 + wn*64 + cb*32 + 8*v4 + 4*(lane/32) + 0..3 -- one row pointer per
-  // 32-row block and constant offsets.  N is a multiple of 64, so a wave's
+  // ncol0 + wn*64 + cb*32 + 16*p + 8*(lane/32) + 0..7 (the values of
+  // v4 = 2p and 2p+1) -- one row pointer per 32-row block and constant
+  // offsets, 16 bytes per load.  N is a multiple of 64, so a wave's
   // 64 columns are all inside or all outside the layer (a uniform branch);
   // rows past the tile's end read its first row and are zeroed.
   const bool colok = ncol0 + wn * 64 < N;
@@ -318,18 +331,22 @@ __global__ __launch_bounds__(kThreads, 1) void alpha_gemm(
     const int rloc = wm * 128 + tb * 32 + (lane & 31);
     const bool rok = rloc < nrows;
     const uint16_t* hrow =
-        Hpre + (int64_t)(row0 + (rok ? rloc : 0)) * (2 * N) + ncol0 + wn * 64 + 4 * (lane >> 5);
+        Hpre + (int64_t)(row0 + (rok ? rloc : 0)) * (2 * N) + ncol0 + wn * 64 + 8 * (lane >> 5);
     u32x2 ga[kWCB][4], ua[kWCB][4];
 #pragma unroll
     for (int cb = 0; cb < kWCB; ++cb)
 #pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
+      for (int p = 0; p < 2; ++p) {
         if (colok) {
-          ga[cb][v4] = *reinterpret_cast<const u32x2*>(hrow + cb * 32 + 8 * v4);
-          ua[cb][v4] = *reinterpret_cast<const u32x2*>(hrow + N + cb * 32 + 8 * v4);
+          const u32x4 g4 = *reinterpret_cast<const u32x4*>(hrow + cb * 32 + 16 * p);
+          const u32x4 u4 = *reinterpret_cast<const u32x4*>(hrow + N + cb * 32 + 16 * p);
+          ga[cb][2 * p] = u32x2{g4[0], g4[1]};
+          ga[cb][2 * p + 1] = u32x2{g4[2], g4[3]};
+          ua[cb][2 * p] = u32x2{u4[0], u4[1]};
+          ua[cb][2 * p + 1] = u32x2{u4[2], u4[3]};
         } else {
-          ga[cb][v4] = u32x2{0u, 0u};
-          ua[cb][v4] = u32x2{0u, 0u};
+          ga[cb][2 * p] = ga[cb][2 * p + 1] = u32x2{0u, 0u};
+          ua[cb][2 * p] = ua[cb][2 * p + 1] = u32x2{0u, 0u};
         }
       }
 #pragma unroll
