@@ -238,8 +238,7 @@ __global__ __launch_bounds__(kThreads) void omni_select_kernel(
     const float* __restrict__ p_r, const float* __restrict__ p_c, float* __restrict__ ls_r,
     float* __restrict__ ls_c, int32_t* __restrict__ ids, float* __restrict__ gates, int64_t T,
     int Nr, int Nc, int K, int32_t* __restrict__ counts) {
-  __shared__ int ckey[kSelTok][kMaxCand];
-  __shared__ int cid[kSelTok][kMaxCand];
+  __shared__ int rowstart[kSelTok][kMaxK + 1];                   // candidate numbering
   __shared__ __attribute__((aligned(16))) int tk[kWaves][128];   // 16-byte rank reads
   __shared__ __attribute__((aligned(16))) int ti[kWaves][128];
   __shared__ float lval[kSelTok][2][kMaxK];                       // sorted axis lists
@@ -273,24 +272,23 @@ __global__ __launch_bounds__(kThreads) void omni_select_kernel(
   }
   __syncthreads();                                     // both axes' lists of every token
   if (!live || axis == 1) return;
-  const float cv = lane < C ? lval[u][1][lane] : 0.f;
-  const int ci = lane < C ? lid[u][1][lane] : 0;
-  // candidate pairs (i, j) of axis ranks with (i+1)(j+1) <= K; lane j holds
-  // column rank j, row rank i is broadcast
-  int* cks = ckey[u];
-  int* cis = cid[u];
-  int nc = 0;
-  for (int i = 0; i < R; ++i) {
-    int jmax = K / (i + 1);
-    jmax = jmax < C ? jmax : C;
-    const float a = lval[u][0][i];                     // LDS broadcast
-    const int ar = lid[u][0][i];
-    if (lane < jmax) {
-      cks[nc + lane] = (int)ukey(a + cv);
-      cis[nc + lane] = ar * Nc + ci;
-    }
-    nc += jmax;
+  // Candidate pairs (i, j) of axis ranks with (i+1)(j+1) <= K, numbered row
+  // by row: row i holds jmax(i) = min(C, K/(i+1)) pairs, the first at
+  // rowstart[i] (a prefix sum over lanes).  Each lane builds its own slots
+  // c = lane + 64q directly: i by a binary search in rowstart, j = c -
+  // rowstart[i].  (Broadcasting row after row to all lanes took one LDS
+  // round trip and ~10 vector instructions for each of the R rows.)
+  int* rs = rowstart[u];
+  const int jm = lane < R ? min(C, K / (lane + 1)) : 0;
+  int incl = jm;                                       // inclusive prefix over lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
   }
+  rs[lane + 1] = incl;
+  if (lane == 0) rs[0] = 0;
+  const int nc = __builtin_amdgcn_readlane(incl, 63);
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -300,8 +298,17 @@ __global__ __launch_bounds__(kThreads) void omni_select_kernel(
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     const int c = lane + 64 * q;
-    mk[q] = c < nc ? (uint32_t)cks[c] : 0u;
-    mi[q] = c < nc ? cis[c] : (1 << 17);
+    mk[q] = 0u;
+    mi[q] = 1 << 17;
+    if (c < nc) {
+      int i = 0;                                       // the last row with rowstart <= c
+#pragma unroll
+      for (int step = 32; step >= 1; step >>= 1)
+        if (i + step < R && rs[i + step] <= c) i += step;
+      const int j = c - rs[i];
+      mk[q] = ukey(lval[u][0][i] + lval[u][1][j]);
+      mi[q] = lid[u][0][i] * Nc + lid[u][1][j];
+    }
   }
   uint32_t sk;
   int sid;
