@@ -125,7 +125,10 @@ __device__ __forceinline__ uint32_t ukey(float v) {
 __device__ __forceinline__ float unukey(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
-__device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
+// The lane mask of a compare goes straight to the scalar popcount (__ballot
+// takes an int and first turns the compare into a 0/1 value and back: two
+// more vector instructions per count).
+__device__ __forceinline__ int wave_count(bool p) { return __popcll(__builtin_amdgcn_ballot_w64(p)); }
 
 // Top r (1 <= r <= 64) of the wave's entries -- S slots per lane, entry
 // (u, lane) with key k[u] (0 = empty) and a distinct id i[u] < 2^17 -- by
@@ -188,11 +191,11 @@ __device__ __forceinline__ void wave_top(const uint32_t* k, const int* id, int r
 #pragma unroll
   for (int u = 0; u < S; ++u) {
     const bool sel = k[u] > th || (k[u] == th && id[u] <= x);
-    const uint64_t m = __ballot(sel);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(sel);
     if (sel) {
       const int pos = base + __popcll(m & below);
       lk[pos] = (int)k[u];
-      li[pos] = id[u];
+      li[pos] = ~id[u];                          // complemented: (key, ~id) orders as one u64
     }
     base += __popcll(m);
   }
@@ -200,25 +203,27 @@ __device__ __forceinline__ void wave_top(const uint32_t* k, const int* id, int r
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const uint32_t mk = lane < r ? (uint32_t)lk[lane] : 0u;
-  const int mi = lane < r ? li[lane] : 0x7FFFFFFF;
-  // each winner's rank: the winners before it in (key desc, id asc), read
-  // four at a time from LDS (every lane reads the same entries: broadcast)
+  const uint32_t mic = lane < r ? (uint32_t)li[lane] : 0u;
+  const uint64_t mine = ((uint64_t)mk << 32) | mic;
+  // each winner's rank: the winners before it in (key desc, id asc), i.e.
+  // with a larger (key, ~id) as one unsigned 64-bit value, read four at a
+  // time from LDS (every lane reads the same entries: broadcast)
   int rank = 0;
   for (int q = 0; q < r; q += 4) {
     const int4 kq = *reinterpret_cast<const int4*>(lk + q);
     const int4 iq = *reinterpret_cast<const int4*>(li + q);
     const uint32_t kv[4] = {(uint32_t)kq.x, (uint32_t)kq.y, (uint32_t)kq.z, (uint32_t)kq.w};
-    const int iv[4] = {iq.x, iq.y, iq.z, iq.w};
+    const uint32_t iv[4] = {(uint32_t)iq.x, (uint32_t)iq.y, (uint32_t)iq.z, (uint32_t)iq.w};
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      rank += (q + u < r && (kv[u] > mk || (kv[u] == mk && iv[u] < mi))) ? 1 : 0;
+      rank += (q + u < r && (((uint64_t)kv[u] << 32) | iv[u]) > mine) ? 1 : 0;
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (lane < r) {
     lk[64 + rank] = (int)mk;
-    li[64 + rank] = mi;
+    li[64 + rank] = (int)~mic;
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -243,7 +248,9 @@ __global__ __launch_bounds__(kThreads) void omni_select_kernel(
   __shared__ __attribute__((aligned(16))) int ti[kWaves][128];
   __shared__ float lval[kSelTok][2][kMaxK];                       // sorted axis lists
   __shared__ int lid[kSelTok][2][kMaxK];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // the wave index (and with it the axis, the list length and every search
+  // bound) is wave-uniform: scalar registers and scalar branches
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int u = wv >> 1, axis = wv & 1;
   const int64_t t = (int64_t)blockIdx.x * kSelTok + u;
   const bool live = t < T;                             // wave-uniform
