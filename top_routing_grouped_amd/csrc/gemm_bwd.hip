@@ -737,7 +737,7 @@ __global__ __launch_bounds__(64 * kTokWaves) void token_backward_kernel(
   __shared__ float s_dsel[kTokWaves][kMaxK];
   __shared__ int s_id[kTokWaves][kMaxK];
   __shared__ int s_slot[kTokWaves][kMaxK];
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * kTokWaves + wv;
   const bool live = t < T;
   float part = 0.f;

@@ -455,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void omni_rank_kernel(const int32_t* __re
                                                              int K, int mask_words) {
   extern __shared__ uint32_t rank_lds[];
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int e = blockIdx.x * kWaves + wv;
   if (e >= N) return;
   const int off = offsets[e], c = offsets[e + 1] - off;
@@ -568,7 +568,7 @@ __global__ __launch_bounds__(kThreads) void omni_expert_kernel(
     int N, int d) {
   constexpr int kTasks = 4;
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int e = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (e >= N) return;
   const int off = offsets[e], c = offsets[e + 1] - off;
   if (c == 0) return;
@@ -612,7 +612,7 @@ __global__ __launch_bounds__(kThreads) void omni_combine_kernel(
     uint16_t* __restrict__ Y, int64_t T, int d, int K) {
   constexpr int KG = NCH >= 4 ? 32 / NCH : 16;   // 16-byte loads in flight: 16..32 per lane
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= T) return;
   const int nchunk = d / 8;
   int myid = 0;
