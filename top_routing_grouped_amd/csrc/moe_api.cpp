@@ -454,14 +454,17 @@ moe_status moe_omni_forward(const moe_omni_desc* desc, const void* X, const void
   hipStream_t s = (hipStream_t)stream;
   moe::OmniRouteWs rw;
   moe::omni_route_ws_bytes(p, &rw, w.route);
-  // the selection counts the entries per expert, so the permutation does not
+  // the selection counts the entries per expert, so the permutation does
+  // not, and records each entry's place in its expert's arrival order in the
+  // buffer of the expert activations a (written only after the permutation)
+  int32_t* tpos = reinterpret_cast<int32_t*>(w.a);
   MOE_TRY(hip_status(moe::launch_omni_route(p, X, W_r, W_c, nullptr, nullptr, w.ids, w.gates, rw, s,
-                                            w.counts),
+                                            w.counts, tpos),
                      "atomic-expert router launch"));
   moe::OmniPermuteWs pw;
   moe::omni_permute_ws_bytes(p, &pw, w.permute);
   MOE_TRY(hip_status(moe::launch_omni_permute(p, w.ids, w.counts, w.offsets, w.perm, w.inv, pw, s,
-                                              true),
+                                              true, tpos),
                      "atomic-expert permutation launch"));
   return hip_status(moe::launch_omni_experts(p, X, W_in, W_out, w.ids, w.gates, w.offsets, w.perm,
                                              w.inv, w.a, Y, s),

@@ -198,13 +198,17 @@ size_t omni_route_ws_bytes(const OmniProblem& p, OmniRouteWs* w, unsigned char* 
 size_t omni_permute_ws_bytes(const OmniProblem& p, OmniPermuteWs* w, unsigned char* base);
 // counts (optional): the selection also counts each expert's entries into
 // it (cleared first), so that the permutation can skip its own count
-// (launch_omni_permute with counted = true).
+// (launch_omni_permute with counted = true).  tpos (optional, with counts):
+// [T*K], each entry's place in its expert's arrival order, which lets the
+// permutation place entries without atomics.
 hipError_t launch_omni_route(const OmniProblem& p, const void* X, const void* W_r, const void* W_c,
                              float* ls_r, float* ls_c, int32_t* ids, float* gates,
-                             const OmniRouteWs& w, hipStream_t s, int32_t* counts = nullptr);
+                             const OmniRouteWs& w, hipStream_t s, int32_t* counts = nullptr,
+                             int32_t* tpos = nullptr);
 hipError_t launch_omni_permute(const OmniProblem& p, const int32_t* ids, int32_t* counts,
                                int32_t* offsets, int32_t* perm, int32_t* inv,
-                               const OmniPermuteWs& w, hipStream_t s, bool counted = false);
+                               const OmniPermuteWs& w, hipStream_t s, bool counted = false,
+                               const int32_t* tpos = nullptr);
 hipError_t launch_omni_experts(const OmniProblem& p, const void* X, const void* W_in,
                                const void* W_out, const int32_t* ids, const float* gates,
                                const int32_t* offsets, const int32_t* perm, const int32_t* inv,
