@@ -451,8 +451,9 @@ __global__ __launch_bounds__(kThreads) void omni_scatter_kernel(const int32_t* _
   tmp_tk[s] = (int32_t)i;
 }
 
-// One wave per expert: each entry's final place is its rank among the
-// segment's (token*K + k) keys (distinct), i.e. ascending token order.
+// Ranking: each entry's final place is its rank among its expert's segment
+// of (token*K + k) keys (distinct), i.e. ascending token order.
+// rank_segment ranks one expert's segment with a whole wave (wv).
 // Segments of at most 64 entries: each lane loads one entry and counts the
 // smaller keys across the lanes (readlane; one memory round trip per
 // segment).  Longer ones, when T fits the wave's LDS mask
@@ -463,16 +464,11 @@ __global__ __launch_bounds__(kThreads) void omni_scatter_kernel(const int32_t* _
 // instead of O(c^2/64) (a hot expert chosen by most of 32768 tokens would
 // otherwise serialise ~16M loads on one wave).  Beyond that T, long
 // segments fall back to direct counting over global memory.
-__global__ __launch_bounds__(kThreads) void omni_rank_kernel(const int32_t* __restrict__ offsets,
-                                                             const int32_t* __restrict__ tmp_tk,
-                                                             int32_t* __restrict__ perm,
-                                                             int32_t* __restrict__ inv, int N,
-                                                             int K, int mask_words) {
-  extern __shared__ uint32_t rank_lds[];
+__device__ void rank_segment(int e, const int32_t* __restrict__ offsets,
+                             const int32_t* __restrict__ tmp_tk, int32_t* __restrict__ perm,
+                             int32_t* __restrict__ inv, int K, int mask_words, uint32_t* rank_lds,
+                             int wv) {
   const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  const int e = blockIdx.x * kWaves + wv;
-  if (e >= N) return;
   const int off = offsets[e], c = offsets[e + 1] - off;
   if (c <= 64) {
     // one load per entry, then the smaller keys counted across the lanes
@@ -535,6 +531,57 @@ __global__ __launch_bounds__(kThreads) void omni_rank_kernel(const int32_t* __re
     perm[off + rank] = t;
     inv[key] = off + rank;
   }
+}
+
+// Four experts per wave, 16 lanes each, when none of the four has more than
+// 16 entries (the usual case: 4 entries per expert on average at the 64k-
+// expert layer): a lane holds one entry, and its rank is the number of
+// smaller keys among the 15 others of its row, brought by DPP row rotations
+// (no memory round trip).  A wave whose group holds a longer segment ranks
+// the four experts one by one with the whole wave (rank_segment).  One
+// expert per wave took 11 us for 65536 experts.
+constexpr int kRankGroup = 4;
+template <int R>
+__device__ __forceinline__ int row_ror(int x) {
+  return __builtin_amdgcn_mov_dpp(x, 0x120 + R, 0xF, 0xF, false);   // row_ror:R
+}
+template <int R>
+__device__ __forceinline__ int count_smaller_in_row(int key) {
+  if constexpr (R == 16) {
+    return 0;
+  } else {
+    return (row_ror<R>(key) < key ? 1 : 0) + count_smaller_in_row<R + 1>(key);
+  }
+}
+__global__ __launch_bounds__(kThreads) void omni_rank_kernel(const int32_t* __restrict__ offsets,
+                                                             const int32_t* __restrict__ tmp_tk,
+                                                             int32_t* __restrict__ perm,
+                                                             int32_t* __restrict__ inv, int N,
+                                                             int K, int mask_words) {
+  extern __shared__ uint32_t rank_lds[];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int e0 = (blockIdx.x * kWaves + wv) * kRankGroup;
+  if (e0 >= N) return;
+  const int e = e0 + (lane >> 4), l16 = lane & 15;
+  int off = 0, c = 0;
+  if (e < N) {
+    off = offsets[e];
+    c = offsets[e + 1] - off;
+  }
+  const int cmax = max(max(__builtin_amdgcn_readlane(c, 0), __builtin_amdgcn_readlane(c, 16)),
+                       max(__builtin_amdgcn_readlane(c, 32), __builtin_amdgcn_readlane(c, 48)));
+  if (cmax <= 16) {
+    const int key = l16 < c ? tmp_tk[off + l16] : 0x7FFFFFFF;
+    const int rank = count_smaller_in_row<1>(key);
+    if (l16 < c && rank < c) {                 // rank < c always; kept as a bound
+      perm[off + rank] = key / K;
+      inv[key] = off + rank;
+    }
+    return;
+  }
+  for (int q = 0; q < kRankGroup; ++q)
+    if (e0 + q < N) rank_segment(e0 + q, offsets, tmp_tk, perm, inv, K, mask_words, rank_lds, wv);
 }
 
 // ---------------------------------------------------------------- experts
@@ -782,7 +829,8 @@ hipError_t launch_omni_permute(const OmniProblem& p, const int32_t* ids, int32_t
   // while it keeps a workgroup within 64 KB of LDS (T <= 65536)
   int mask_words = (int)((p.T + 31) / 32);
   if ((size_t)kWaves * 2 * mask_words * sizeof(uint32_t) > 64 * 1024) mask_words = 0;
-  hipLaunchKernelGGL(omni_rank_kernel, dim3((unsigned)((N + kWaves - 1) / kWaves)),
+  hipLaunchKernelGGL(omni_rank_kernel,
+                     dim3((unsigned)((N + kWaves * kRankGroup - 1) / (kWaves * kRankGroup))),
                      dim3(kThreads), (size_t)kWaves * 2 * mask_words * sizeof(uint32_t), s, offsets,
                      w.tmp_tk, perm, inv, N, p.K, mask_words);
   return hipGetLastError();
