@@ -185,7 +185,10 @@ __device__ __forceinline__ void wave_top(const uint32_t* k, const int* id, int r
       if (c < need) x = cand;
     }
   }
-  // compact the r winners to positions 0..r-1 (slot-major, lane order)
+  // compact the r winners to positions 0..r-1 (slot-major, lane order); the
+  // positions r..63 get key 0, which no winner's (key, ~id) is below, so the
+  // rank loop below can run over whole blocks of 16 without bounds
+  if (lane >= r) lk[lane] = 0;
   const uint64_t below = (1ull << lane) - 1ull;
   int base = 0;
 #pragma unroll
@@ -209,14 +212,20 @@ __device__ __forceinline__ void wave_top(const uint32_t* k, const int* id, int r
   // with a larger (key, ~id) as one unsigned 64-bit value, read four at a
   // time from LDS (every lane reads the same entries: broadcast)
   int rank = 0;
-  for (int q = 0; q < r; q += 4) {
-    const int4 kq = *reinterpret_cast<const int4*>(lk + q);
-    const int4 iq = *reinterpret_cast<const int4*>(li + q);
-    const uint32_t kv[4] = {(uint32_t)kq.x, (uint32_t)kq.y, (uint32_t)kq.z, (uint32_t)kq.w};
-    const uint32_t iv[4] = {(uint32_t)iq.x, (uint32_t)iq.y, (uint32_t)iq.z, (uint32_t)iq.w};
+  for (int q0 = 0; q0 < r; q0 += 16) {        // a block's 8 reads in flight together
+    int4 kq[4], iq[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      rank += (q + u < r && (((uint64_t)kv[u] << 32) | iv[u]) > mine) ? 1 : 0;
+    for (int b = 0; b < 4; ++b) {
+      kq[b] = *reinterpret_cast<const int4*>(lk + q0 + 4 * b);
+      iq[b] = *reinterpret_cast<const int4*>(li + q0 + 4 * b);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t kv[4] = {(uint32_t)kq[b].x, (uint32_t)kq[b].y, (uint32_t)kq[b].z, (uint32_t)kq[b].w};
+      const uint32_t iv[4] = {(uint32_t)iq[b].x, (uint32_t)iq[b].y, (uint32_t)iq[b].z, (uint32_t)iq[b].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rank += ((((uint64_t)kv[u] << 32) | iv[u]) > mine) ? 1 : 0;
+    }
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
