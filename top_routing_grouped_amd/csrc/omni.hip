@@ -384,13 +384,20 @@ __global__ __launch_bounds__(kScanThreads) void omni_scan_kernel(const int32_t* 
   __shared__ int part[kScanWaves], wtot[kScanWaves];
   const int q = threadIdx.x, lane = q & 63, w = q >> 6;
   const int b = blockIdx.x, i0 = b * kScanBlock;
-  // counts before this workgroup's range
+  // counts before this workgroup's range: those blocks are whole, so the
+  // loads need no bounds and go four blocks at a time (one block per round
+  // trip took 8 us for 65536 counts)
+  auto block_sum = [&](int j) {
+    const int4 c = *reinterpret_cast<const int4*>(counts + (size_t)j * kScanBlock + 4 * q);
+    return (c.x + c.y) + (c.z + c.w);
+  };
   int pre = 0;
-  for (int j = 0; j < b; ++j) {
-    int v[4];
-    load4(counts, j * kScanBlock + 4 * q, N, v);
-    pre += (v[0] + v[1]) + (v[2] + v[3]);
+  int j = 0;
+  for (; j + 4 <= b; j += 4) {
+    const int s0 = block_sum(j), s1 = block_sum(j + 1), s2 = block_sum(j + 2), s3 = block_sum(j + 3);
+    pre += (s0 + s1) + (s2 + s3);
   }
+  for (; j < b; ++j) pre += block_sum(j);
   pre = wave_sum_i(pre);
   // this range
   int v[4];
