@@ -682,14 +682,17 @@ __global__ __launch_bounds__(kThreads) void omni_expert_kernel(
 
 // One wave per token: lane k first loads the token's id and coefficient
 // g_k * a[slot] for entry k (so the row loads below depend on nothing but a
-// broadcast), then rows go in groups (16 for d <= 1024) with all their
+// broadcast), then rows go in groups (8 for 512 < d <= 1024) with all their
 // loads in flight.
 template <int NCH>
 __global__ __launch_bounds__(kThreads) void omni_combine_kernel(
     const uint16_t* __restrict__ W_out, const int32_t* __restrict__ ids,
     const float* __restrict__ gates, const int32_t* __restrict__ inv, const float* __restrict__ a,
     uint16_t* __restrict__ Y, int64_t T, int d, int K) {
-  constexpr int KG = NCH >= 4 ? 32 / NCH : 16;   // 16-byte loads in flight: 16..32 per lane
+  // rows in flight per group: 8 at d <= 1024 (NCH = 2) keeps 5 waves per
+  // SIMD, so all 4096 tokens' waves of the 64k-expert layer are resident at
+  // once (16 rows, 3 waves per SIMD: about 1 us slower)
+  constexpr int KG = NCH >= 4 ? 32 / NCH : (NCH == 2 ? 8 : 16);
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= T) return;
