@@ -60,6 +60,8 @@ SHAPES = [
     (3, 64, 5, 5, 7),            # K above each axis' length
     (200, 128, 16, 64, 12),      # both axes in one router launch, the first padded to 64
     (130, 192, 136, 8, 9),       # both axes in one router launch, the second padded to 256
+    (96, 1536, 12, 8, 16),       # d in (1024, 2048]: expert and combine kernels with 4 chunks per lane
+    (48, 4096, 4, 16, 8),        # d = 4096, the largest: 8 chunks per lane
 ]
 
 
