@@ -76,6 +76,25 @@ def test_rounding_matches_oracle(T, d, E, K, n, dtype, cf, bias, fires):
     check_outputs_streamed(inp, ref, f32np(res["gates"]), H, O, Y_fused, TOL[dtype])
 
 
+@pytest.mark.parametrize("T,d,E,K,n,cf,bias", [(3001, 128, 8, 3, 256, 0.0, True),
+                                               (1500, 128, 40, 4, 128, 1.0, True)])
+def test_rounding_composes_with_the_other_flags(T, d, E, K, n, cf, bias):
+    """Flags combined: the threshold selection gives the default selection's
+    outputs bit for bit, so with token rounding on as well Y must not change,
+    with the default GEMM launch and with the kernel forced to the tiled one."""
+    print(f"flags composed T={T} d={d} E={E} K={K} n={n} cf={cf}", flush=True)
+    inp = mi.draw(T, d, E, n, torch.bfloat16, seed=T + 1, bias="zipf" if bias else None)
+    dev = device_inputs(inp)
+    R, TH, TI = moe.MOE_FLAG_TOKEN_ROUNDING, moe.MOE_FLAG_TOPK_THRESHOLD, moe.MOE_FLAG_GEMM_TILED
+    out = {}
+    for flags in (R, R | TH, R | TI, R | TH | TI):
+        out[flags] = moe.forward(dev["X"], dev["W_r"], dev["W_gate"], dev["W_up"], dev["W_down"], K,
+                                 cf, bias=dev["bias"], flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(out[R | TH], out[R])
+    assert torch.equal(out[R | TH | TI], out[R | TI])
+
+
 def test_all_ties_drop_the_largest_tokens():
     """A zero router gives every token the same K experts and equal gates:
     each expert keeps its lowest token ids."""
