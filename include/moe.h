@@ -359,9 +359,9 @@ moe_status moe_backward(const moe_desc* desc, const void* X, const void* W_r, co
  * Expert id i = i_r*Nc + i_c; score S = ls_r[i_r] + ls_c[i_c] with ls the
  * fp32 log-softmax of x W over each axis; the K largest S by (S desc, id
  * asc); gates = softmax over the K selected S.  The search keeps the top
- * min(K, Nr) rows and min(K, Nc) columns (the released code's pruning,
- * which returns the full search's result) and then only pairs whose axis
- * ranks satisfy (i+1)(j+1) <= K.  No capacity: every task is kept.
+ * min(K, Nr) rows and min(K, Nc) columns and then only pairs whose axis
+ * ranks satisfy (i+1)(j+1) <= K, a pruning that returns the full search's
+ * result.  No capacity: every task is kept.
  * Supported: 1 <= Nr, Nc <= 256, 1 <= K <= min(64, Nr*Nc), d a multiple of
  * 64 up to 4096, T*K < 2^31, dtype MOE_BF16, flags 0. */
 typedef struct {
