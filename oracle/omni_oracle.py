@@ -12,7 +12,7 @@ Page cited: [P2] "MoE 的两个上游创新：Routing-Free 与 OmniMoE"
   a rank-1 FFN piece; the experts are stacked into two [N, d] tables;
 * §2.2 the Cartesian-product router: the id i splits into (i_r, i_c) with
   N = N_r * N_c; p_r = x W_r, p_c = x W_c; the score of (i_r, i_c) is the sum
-  of the two LogSoftmax values; the released code first keeps the top
+  of the two LogSoftmax values; the page's pruning first keeps the top
   k0 = min(sqrt(N), K) of each axis and searches the top-K in the k0 x k0
   candidates;
 * §2.3 expert-centric scheduling: the L*K (token, expert) tasks are ordered
