@@ -386,7 +386,8 @@ __global__ __launch_bounds__(kScanThreads) void omni_scan_kernel(const int32_t* 
   const int b = blockIdx.x, i0 = b * kScanBlock;
   // counts before this workgroup's range: those blocks are whole, so the
   // loads need no bounds and go four blocks at a time (one block per round
-  // trip took 8 us for 65536 counts)
+  // trip took 8 us for 65536 counts; sixteen at a time, each guarded by
+  // j + r < b, 7.2 us against 5.5)
   auto block_sum = [&](int j) {
     const int4 c = *reinterpret_cast<const int4*>(counts + (size_t)j * kScanBlock + 4 * q);
     return (c.x + c.y) + (c.z + c.w);
