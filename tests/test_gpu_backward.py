@@ -61,6 +61,7 @@ SMALL = [
     (64, 128, 5, 5, 64, 0.0, False, False),      # K = E; E not a multiple of 8
     (1000, 512, 16, 4, 256, 1.0, False, False),
     (3, 64, 2, 1, 64, 0.0, False, False),        # fewer tokens than one row block
+    (40, 64, 256, 256, 64, 0.0, False, False),   # K = E = 256: the token kernel's largest K
     (400, 128, 16, 2, 128, 0.25, True, True),    # heavy drops: tokens with no kept slot
 ]
 

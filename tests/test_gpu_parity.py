@@ -56,6 +56,8 @@ SMALL = [
     (300, 128, 64, 6, 256, "bf16", 0.3, "zipf"),     # heavy drops, fully dropped tokens
     (70, 64, 40, 20, 64, "bf16", 0.0, None),         # K above 16
     (60, 64, 64, 64, 64, "bf16", 0.0, None),         # K = E = 64: every token in every expert
+    (40, 64, 256, 256, 64, "bf16", 0.0, None),       # K = E = 256: the largest K and E
+    (120, 64, 200, 130, 64, "bf16", 0.5, "zipf"),    # K above 128 under a capacity cap
     (1, 128, 8, 2, 128, "bf16", 0.0, None),          # one token
     (600, 1024, 4, 2, 1152, "bf16", 0.0, None),      # column blocks: up 9 tiles (8 + 1), down 4 (3 + 1)
     (256, 128, 8, 2, 256, "fp32", 0.0, None),        # the tiny fp32 layer's shape, other seed
