@@ -81,3 +81,28 @@ def test_atomic_expert_forward_replays_from_a_graph():
         moe.moe_omni_forward(*args)            # eager call between replays
         torch.cuda.synchronize()
         assert torch.equal(Y, want)
+
+
+def test_explicit_stream_argument():
+    """The binding's stream argument takes a torch stream object or its raw
+    handle; either runs the layer on that stream with the same bits as torch's
+    current stream."""
+    T, d, E, K, n = 300, 256, 16, 4, 128
+    print(f"case explicit stream T={T} d={d} E={E} K={K} n={n}", flush=True)
+    inp = mi.draw(T, d, E, n, torch.bfloat16, seed=53)
+    dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    desc = moe.make_desc(T, d, E, K, n, "bf16", 0.0)
+    ws = moe.workspace(desc, moe.MOE_WS_FORWARD)
+    Y = torch.empty_like(dev["X"])
+    args = (desc, dev["X"], dev["W_r"], dev["bias"], dev["W_gate"], dev["W_up"], dev["W_down"], Y, ws)
+    moe.moe_forward(*args)
+    torch.cuda.synchronize()
+    want = Y.clone()
+    s = torch.cuda.Stream()
+    for handle in (s, s.cuda_stream):
+        Y.fill_(float("nan"))
+        s.wait_stream(torch.cuda.current_stream())
+        moe.moe_forward(*args, stream=handle)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, want), type(handle).__name__

@@ -177,10 +177,13 @@ def _p(t):
 
 
 def _stream(stream):
-    if stream is not None:
-        return ctypes.c_void_p(int(stream))
-    import torch
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    """The hipStream_t to enqueue on: a torch stream object (its handle), a raw
+    handle as an int, or None for torch's current stream."""
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    handle = getattr(stream, "cuda_stream", stream)
+    return ctypes.c_void_p(int(handle))
 
 
 # ---------------------------------------------------------------- host-only queries
