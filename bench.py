@@ -269,9 +269,8 @@ def main():
         pmc_summary(*args.pmc_summary, args.workload, args.pmc_kernel)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer would shard as described in DESIGN.md, but no multi-GPU path exists)",
-              file=sys.stderr)
+        print(f"bench.py: the layer runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(there is no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.calib_copy:
