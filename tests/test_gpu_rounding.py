@@ -49,6 +49,8 @@ CASES = [
     (2500, 128, 6, 2, 128, "fp32", 1.2, False, True),   # after a capacity cut
     (700, 64, 3, 1, 64, "bf16", 0.0, False, False),     # every expert below one tile: unchanged
     (100, 64, 8, 2, 64, "bf16", 0.0, False, False),
+    (1500, 64, 64, 16, 64, "bf16", 0.0, True, True),    # K = 16 under a skewed router
+    (1200, 64, 32, 32, 64, "bf16", 0.0, False, False),  # K = E: every expert already holds every token
 ]
 
 
