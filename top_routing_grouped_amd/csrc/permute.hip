@@ -89,22 +89,27 @@ __global__ __launch_bounds__(kB) void histogram_kernel(const int32_t* __restrict
 }
 
 // Exclusive scan over the first n (<= 256) threads' values; all threads of
-// the block must call it.  Returns the exclusive prefix; *total gets the sum.
+// the block (at least 256) must call it.  Returns the exclusive prefix (0 for threads from
+// 256 on); *total gets the sum.  Each of the first four waves scans its 64
+// values with lane shuffles, then adds the totals of the waves before it
+// (two barriers, where a scan through LDS in 8 rounds took 18).
 __device__ int block_exscan256(int v, int n, int* lds, int* total) {
-  const int tid = threadIdx.x;
-  if (tid < 256) lds[tid] = (tid < n) ? v : 0;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    int x = 0;
-    if (tid < 256 && tid >= off) x = lds[tid - off];
-    __syncthreads();
-    if (tid < 256) lds[tid] += x;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int own = (tid < n) ? v : 0;
+  int x = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  const int incl = (tid < 256) ? lds[tid] : 0;
-  *total = lds[255];
+  if (wv < 4 && lane == 63) lds[wv] = x;
   __syncthreads();
-  return incl - ((tid < n) ? v : 0);
+  int base = 0;
+  for (int j = 0; j < wv && j < 4; ++j) base += lds[j];
+  *total = ((lds[0] + lds[1]) + lds[2]) + lds[3];
+  __syncthreads();                      // the caller may reuse lds
+  return (wv < 4) ? x + base - own : 0;
 }
 
 // Row tiles of one expert: rows [off, off+cnt) cut into BM-row pieces.
