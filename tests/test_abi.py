@@ -52,9 +52,15 @@ def test_validate_cases():
         (moe.make_desc(16, 128, 8, 2, 256, capacity_factor=float("nan")), moe.MOE_ERR_INVALID_ARG),
         (moe.make_desc(16, 128, 8, 2, 256, capacity_factor=float("inf")), moe.MOE_ERR_INVALID_ARG),
         (moe.make_desc(2 ** 30, 128, 8, 2, 256), moe.MOE_ERR_UNSUPPORTED),     # T*K >= 2^31
+        (moe.make_desc(2 ** 28, 128, 8, 8, 256), moe.MOE_ERR_UNSUPPORTED),     # T*K == 2^31 exactly
+        # T*K would wrap a 64-bit product to 0 (2^62 * 8 = 2^65)
+        (moe.make_desc(2 ** 62, 128, 8, 8, 256), moe.MOE_ERR_UNSUPPORTED),
+        (moe.make_desc(2 ** 63 - 1, 128, 256, 256, 256), moe.MOE_ERR_UNSUPPORTED),
     ]
     for desc, want in bad:
         assert moe.moe_validate(desc) == want
+    # the largest T*K accepted: 2^31 - 1
+    assert moe.moe_validate(moe.make_desc(2 ** 31 - 1, 128, 8, 1, 256)) == moe.MOE_OK
     for f in (1, 2, 4, 5, 8, 10, 16, 26):                     # defined bits are valid
         assert moe.moe_validate(moe.make_desc(16, 128, 8, 2, 256, flags=f)) == moe.MOE_OK
     d = moe.make_desc(16, 128, 8, 2, 256)
@@ -264,6 +270,8 @@ def test_atomic_expert_descriptor_checks():
         (moe.make_omni_desc(16, 1024, 4, 4, 2, "fp32"), moe.MOE_ERR_UNSUPPORTED),
         (moe.make_omni_desc(16, 1024, 4, 4, 2, flags=1), moe.MOE_ERR_INVALID_ARG),
         (moe.make_omni_desc(-1, 1024, 4, 4, 2), moe.MOE_ERR_INVALID_ARG),
+        (moe.make_omni_desc(2 ** 25, 1024, 256, 256, 64), moe.MOE_ERR_UNSUPPORTED),  # T*K = 2^31
+        (moe.make_omni_desc(2 ** 62, 1024, 256, 256, 8), moe.MOE_ERR_UNSUPPORTED),   # would wrap
     ]
     for desc, want in bad:
         assert moe.moe_omni_validate(desc) == want

@@ -57,7 +57,8 @@ moe_status check_desc(const moe_desc* d, uint32_t allowed_flags = 0) {
   if (d->E > 256) return fail(MOE_ERR_UNSUPPORTED, "E above 256 is not supported");
   if (d->d < 64 || d->d % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "d must be a positive multiple of 64");
   if (d->n < 64 || d->n % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "n must be a positive multiple of 64");
-  if (d->T * (int64_t)d->K >= ((int64_t)1 << 31))
+  // T*K < 2^31, tested by division so that no product can overflow
+  if (d->T > (((int64_t)1 << 31) - 1) / d->K)
     return fail(MOE_ERR_UNSUPPORTED, "T*K must stay below 2^31 (int32 slots)");
   return MOE_OK;
 }
@@ -327,7 +328,8 @@ moe_status check_omni(const moe_omni_desc* d) {
   if (d->K > 64) return fail(MOE_ERR_UNSUPPORTED, "K above 64 is not supported");
   if (d->d < 64 || d->d % 64 != 0 || d->d > 4096)
     return fail(MOE_ERR_UNSUPPORTED, "d must be a multiple of 64 up to 4096");
-  if (d->T * (int64_t)d->K >= ((int64_t)1 << 31))
+  // T*K < 2^31, tested by division so that no product can overflow
+  if (d->T > (((int64_t)1 << 31) - 1) / d->K)
     return fail(MOE_ERR_UNSUPPORTED, "T*K must stay below 2^31 (int32 slots)");
   return MOE_OK;
 }
