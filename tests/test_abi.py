@@ -56,6 +56,9 @@ def test_validate_cases():
         # T*K would wrap a 64-bit product to 0 (2^62 * 8 = 2^65)
         (moe.make_desc(2 ** 62, 128, 8, 8, 256), moe.MOE_ERR_UNSUPPORTED),
         (moe.make_desc(2 ** 63 - 1, 128, 256, 256, 256), moe.MOE_ERR_UNSUPPORTED),
+        # grouped-GEMM grids beyond 32-bit tile numbering
+        (moe.make_desc(2 ** 20, 2 ** 30, 8, 1, 64), moe.MOE_ERR_UNSUPPORTED),
+        (moe.make_desc(2 ** 20, 64, 8, 1, 2 ** 29), moe.MOE_ERR_UNSUPPORTED),
     ]
     for desc, want in bad:
         assert moe.moe_validate(desc) == want

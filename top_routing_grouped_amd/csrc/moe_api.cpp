@@ -60,6 +60,14 @@ moe_status check_desc(const moe_desc* d, uint32_t allowed_flags = 0) {
   // T*K < 2^31, tested by division so that no product can overflow
   if (d->T > (((int64_t)1 << 31) - 1) / d->K)
     return fail(MOE_ERR_UNSUPPORTED, "T*K must stay below 2^31 (int32 slots)");
+  // every grouped-GEMM grid (forward and backward, at most one workgroup per
+  // 64 rows plus four per expert, times one per 64 columns of the widest
+  // operand) must fit the kernels' 32-bit tile numbering; a problem whose
+  // buffers fit in device memory is far below this
+  const int64_t row_blocks = d->T * (int64_t)d->K / 64 + 4 * (int64_t)d->E + 4;
+  const int64_t widest = d->d > 2 * (int64_t)d->n ? d->d : 2 * (int64_t)d->n;
+  if (row_blocks * ((widest + 63) / 64) >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "problem too large for one grouped-GEMM launch");
   return MOE_OK;
 }
 
