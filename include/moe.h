@@ -154,7 +154,10 @@ typedef struct {
 /* Checks the description (counts, supported shapes, capacity factor, and that
  * flags holds only defined bits, not both GEMM-path bits).  Each device entry
  * point further rejects the bits it does not take.  The host-only queries
- * below ignore the flags. */
+ * below ignore the flags.  MOE_ERR_UNSUPPORTED: E > 256, d or n not a
+ * positive multiple of 64, T*K >= 2^31, or a grouped-GEMM grid of 2^31 or
+ * more workgroups ((T*K/64 + 4E + 4) * ceil(max(d, 2n)/64) bounds it; no
+ * problem whose buffers fit in device memory comes near). */
 moe_status moe_validate(const moe_desc* desc);
 
 /* Per-expert cap C (see moe_desc.capacity_factor); exact integer arithmetic. */
