@@ -338,3 +338,44 @@ def test_route_permute_workspace_and_argument_checks():
     zero = moe.make_desc(0, 128, 8, 2, 128)
     assert lib.moe_route_permute(ctypes.byref(zero), None, None, None, None, None, None, None, None,
                                  None, None, None, None, 0, None) == moe.MOE_OK
+
+
+def test_binding_checks_shapes_and_dtypes_before_any_device_pointer():
+    # CPU tensors: every refusal below happens before a device pointer is taken
+    import torch
+    bf = torch.bfloat16
+    T, d, E, K, n = 32, 128, 8, 2, 256
+    X = torch.zeros(T, d, dtype=bf)
+    W_r = torch.zeros(d, E, dtype=bf)
+    Wg = torch.zeros(E, d, n, dtype=bf)
+    Wu = torch.zeros(E, d, n, dtype=bf)
+    Wd = torch.zeros(E, n, d, dtype=bf)
+    with pytest.raises(ValueError, match="bfloat16 or float32"):
+        moe.forward(X.half(), W_r, Wg, Wu, Wd, K)
+    with pytest.raises(ValueError, match="W_r"):                 # weights of another dtype
+        moe.forward(X.float(), W_r, Wg.float(), Wu.float(), Wd.float(), K)
+    with pytest.raises(ValueError, match="W_down"):              # W_down given as [E, d, n]
+        moe.forward(X, W_r, Wg, Wu, Wd.transpose(1, 2).contiguous().view(E, d, n), K)
+    with pytest.raises(ValueError, match="bias"):
+        moe.forward(X, W_r, Wg, Wu, Wd, K, bias=torch.zeros(E, dtype=bf))
+    with pytest.raises(ValueError, match="W_up"):
+        moe.forward_train(X, W_r, Wg, Wu[:, :, :128].contiguous(), Wd, K)
+    with pytest.raises(ValueError, match="W_r"):
+        moe.route(X, torch.zeros(d + 64, E, dtype=bf), K)
+    desc = moe.make_desc(T, d, E, K, n, "bf16")
+    with pytest.raises(ValueError, match="differs from desc.K"):
+        moe.route_permute(X, W_r, K + 1, desc)
+    rows = moe.moe_max_rows(desc)
+    with pytest.raises(ValueError, match="O: expected at least"):
+        moe.combine(desc, torch.zeros(rows - 1, d, dtype=bf), torch.zeros(T, K),
+                    torch.zeros(T, K, dtype=torch.int32))
+    with pytest.raises(ValueError, match="gates"):
+        moe.combine(desc, torch.zeros(rows, d, dtype=bf), torch.zeros(T, K, dtype=bf),
+                    torch.zeros(T, K, dtype=torch.int32))
+    with pytest.raises(ValueError, match="W_gate"):
+        moe.grouped_ffn(desc, X, None, None, Wg.float(), Wu, Wd)
+    with pytest.raises(ValueError, match="dY"):
+        moe.backward(desc, None, X, W_r, Wg, Wu, Wd, torch.zeros(T, d))
+    # consistent CPU tensors pass the checks and reach the device-pointer check
+    with pytest.raises(ValueError, match="device tensor"):
+        moe.forward(X, W_r, Wg, Wu, Wd, K)

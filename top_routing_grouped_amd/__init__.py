@@ -307,12 +307,52 @@ def moe_backward(desc, X, W_r, W_gate, W_up, W_down, dY, saved, dX, dW_r, dW_gat
 
 # ---------------------------------------------------------------- allocating helpers
 
-def _desc_for(X, W_gate, K, capacity_factor):
+def _dtype_name(t):
+    """The layer dtype of a tensor: bf16 or fp32 (anything else is refused,
+    since the kernels would read it with the wrong element size)."""
     import torch
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float32:
+        return "fp32"
+    raise ValueError(f"expected a bfloat16 or float32 tensor, got {t.dtype}")
+
+
+def _expect(name, t, shape, dtype):
+    """Shape and dtype of a tensor handed to the library, checked before any
+    pointer is taken: a mismatch would let a kernel read past a buffer."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected shape {tuple(shape)} and {dtype}, "
+                         f"got {tuple(t.shape)} and {t.dtype}")
+
+
+def _layer_dtype(desc):
+    import torch
+    return torch.bfloat16 if desc.dtype == MOE_BF16 else torch.float32
+
+
+def _check_router(desc, X, W_r, bias):
+    import torch
+    dt = _layer_dtype(desc)
+    _expect("X", X, (desc.T, desc.d), dt)
+    _expect("W_r", W_r, (desc.d, desc.E), dt)
+    if bias is not None:
+        _expect("bias", bias, (desc.E,), torch.float32)
+
+
+def _check_experts(desc, W_gate, W_up, W_down):
+    dt = _layer_dtype(desc)
+    _expect("W_gate", W_gate, (desc.E, desc.d, desc.n), dt)
+    _expect("W_up", W_up, (desc.E, desc.d, desc.n), dt)
+    _expect("W_down", W_down, (desc.E, desc.n, desc.d), dt)
+
+
+def _desc_for(X, W_gate, K, capacity_factor):
     T, d = X.shape
     E, _, n = W_gate.shape
-    dtype = "bf16" if X.dtype == torch.bfloat16 else "fp32"
-    return make_desc(T, d, E, K, n, dtype, capacity_factor)
+    return make_desc(T, d, E, K, n, _dtype_name(X), capacity_factor)
 
 
 def workspace(desc: MoeDesc, entry: int, device="cuda"):
@@ -329,7 +369,8 @@ def route(X, W_r, K, bias=None, want_logits=False, n=64, split=True, flags=0):
     import torch
     T, d = X.shape
     E = W_r.shape[1]
-    desc = make_desc(T, d, E, K, n, "bf16" if X.dtype == torch.bfloat16 else "fp32", flags=flags)
+    desc = make_desc(T, d, E, K, n, _dtype_name(X), flags=flags)
+    _check_router(desc, X, W_r, bias)
     ids = torch.empty((T, K), dtype=torch.int32, device=X.device)
     gates = torch.empty((T, K), dtype=torch.float32, device=X.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=X.device) if want_logits else None
@@ -344,6 +385,9 @@ def route_permute(X, W_r, K, desc: MoeDesc, bias=None, want_logits=False):
     """Steps 1-5 through moe_route_permute.  Returns dict(ids, gates, logits or
     None, counts, offsets, raw_counts, perm_token, inv_slot)."""
     import torch
+    if K != desc.K:
+        raise ValueError(f"K = {K} differs from desc.K = {desc.K}")
+    _check_router(desc, X, W_r, bias)
     dev = X.device
     T, E = desc.T, desc.E
     out = {
@@ -392,6 +436,8 @@ def round_tokens(desc: MoeDesc, ids, gates, meta):
 def grouped_ffn(desc: MoeDesc, X, offsets, perm_token, W_gate, W_up, W_down):
     """Steps 6-7.  Returns (H [rows_max, n], O [rows_max, d]); rows >= offsets[E] are unspecified."""
     import torch
+    _expect("X", X, (desc.T, desc.d), _layer_dtype(desc))
+    _check_experts(desc, W_gate, W_up, W_down)
     rows = max(1, moe_max_rows(desc))
     H = torch.empty((rows, desc.n), dtype=X.dtype, device=X.device)
     O = torch.empty((rows, desc.d), dtype=X.dtype, device=X.device)
@@ -403,6 +449,12 @@ def grouped_ffn(desc: MoeDesc, X, offsets, perm_token, W_gate, W_up, W_down):
 def combine(desc: MoeDesc, O, gates, inv_slot):
     """Step 8.  Returns Y [T, d]."""
     import torch
+    if O.dim() != 2 or O.shape[1] != desc.d or O.shape[0] < moe_max_rows(desc) \
+            or O.dtype != _layer_dtype(desc):
+        raise ValueError(f"O: expected at least {moe_max_rows(desc)} rows of {desc.d} "
+                         f"{_layer_dtype(desc)}, got {tuple(O.shape)} {O.dtype}")
+    _expect("gates", gates, (desc.T, desc.K), torch.float32)
+    _expect("inv_slot", inv_slot, (desc.T, desc.K), torch.int32)
     Y = torch.empty((desc.T, desc.d), dtype=O.dtype, device=O.device)
     moe_combine(desc, O, gates, inv_slot, Y)
     return Y
@@ -414,6 +466,8 @@ def forward(X, W_r, W_gate, W_up, W_down, K, capacity_factor=0.0, bias=None, ws=
     import torch
     desc = _desc_for(X, W_gate, K, capacity_factor)
     desc.flags = int(flags)
+    _check_router(desc, X, W_r, bias)
+    _check_experts(desc, W_gate, W_up, W_down)
     if ws is None:
         ws = workspace(desc, MOE_WS_FORWARD, X.device)
     Y = torch.empty_like(X)
@@ -429,6 +483,8 @@ def forward_train(X, W_r, W_gate, W_up, W_down, K, capacity_factor=0.0, bias=Non
     import torch
     desc = _desc_for(X, W_gate, K, capacity_factor)
     desc.flags = int(flags)
+    _check_router(desc, X, W_r, bias)
+    _check_experts(desc, W_gate, W_up, W_down)
     if ws is None:
         ws = workspace(desc, MOE_WS_FORWARD, X.device)
     saved = workspace(desc, MOE_WS_SAVED, X.device)
@@ -466,6 +522,9 @@ def backward(desc: MoeDesc, saved, X, W_r, W_gate, W_up, W_down, dY, ws=None):
     import torch
     dev = X.device
     T, d, E, n = desc.T, desc.d, desc.E, desc.n
+    _check_router(desc, X, W_r, None)
+    _check_experts(desc, W_gate, W_up, W_down)
+    _expect("dY", dY, (T, d), _layer_dtype(desc))
     if ws is None:
         ws = workspace(desc, MOE_WS_BACKWARD, dev)
     out = {
