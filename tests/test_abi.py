@@ -379,3 +379,23 @@ def test_binding_checks_shapes_and_dtypes_before_any_device_pointer():
     # consistent CPU tensors pass the checks and reach the device-pointer check
     with pytest.raises(ValueError, match="device tensor"):
         moe.forward(X, W_r, Wg, Wu, Wd, K)
+
+
+def test_atomic_expert_binding_checks_shapes_and_dtypes():
+    import torch
+    bf = torch.bfloat16
+    T, d, Nr, Nc, K = 16, 128, 8, 8, 4
+    X = torch.zeros(T, d, dtype=bf)
+    W_r, W_c = torch.zeros(d, Nr, dtype=bf), torch.zeros(d, Nc, dtype=bf)
+    W_in, W_out = torch.zeros(Nr * Nc, d, dtype=bf), torch.zeros(Nr * Nc, d, dtype=bf)
+    with pytest.raises(ValueError, match="X"):
+        moe.omni_forward(X.float(), W_r, W_c, W_in, W_out, K)
+    with pytest.raises(ValueError, match="W_c"):
+        moe.omni_route(X, W_r, torch.zeros(d + 64, Nc, dtype=bf), K)
+    with pytest.raises(ValueError, match="W_out"):
+        moe.omni_forward(X, W_r, W_c, W_in, W_out[:-1].contiguous(), K)
+    desc = moe.make_omni_desc(T, d, Nr, Nc, K)
+    with pytest.raises(ValueError, match="ids"):
+        moe.omni_permute(desc, torch.zeros(T, K + 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="device tensor"):      # consistent: reaches the pointers
+        moe.omni_forward(X, W_r, W_c, W_in, W_out, K)

@@ -570,8 +570,20 @@ def moe_omni_forward(desc, X, W_r, W_c, W_in, W_out, Y, ws, stream=None):
            "moe_omni_forward")
 
 
-def _omni_desc_for(X, W_r, W_c, K):
-    return make_omni_desc(X.shape[0], X.shape[1], W_r.shape[1], W_c.shape[1], K)
+def _omni_desc_for(X, W_r, W_c, K, W_in=None, W_out=None):
+    """The layer's description, with every tensor's shape and dtype checked
+    (bf16: X[T,d], W_r[d,Nr], W_c[d,Nc], W_in/W_out[Nr*Nc, d])."""
+    import torch
+    T, d = X.shape
+    Nr, Nc = W_r.shape[1], W_c.shape[1]
+    bf = torch.bfloat16
+    _expect("X", X, (T, d), bf)
+    _expect("W_r", W_r, (d, Nr), bf)
+    _expect("W_c", W_c, (d, Nc), bf)
+    if W_in is not None or W_out is not None:
+        _expect("W_in", W_in, (Nr * Nc, d), bf)
+        _expect("W_out", W_out, (Nr * Nc, d), bf)
+    return make_omni_desc(T, d, Nr, Nc, K)
 
 
 def _omni_ws(desc, entry, device):
@@ -596,6 +608,7 @@ def omni_route(X, W_r, W_c, K):
 def omni_permute(desc: MoeOmniDesc, ids):
     """(expert, token) order over the N experts: dict(counts, offsets, perm_token, inv_slot)."""
     import torch
+    _expect("ids", ids, (desc.T, desc.K), torch.int32)
     dev = ids.device
     N = desc.Nr * desc.Nc
     out = {
@@ -612,7 +625,7 @@ def omni_permute(desc: MoeOmniDesc, ids):
 def omni_forward(X, W_r, W_c, W_in, W_out, K, ws=None):
     """The atomic-expert layer in one library call.  Returns Y [T, d]."""
     import torch
-    desc = _omni_desc_for(X, W_r, W_c, K)
+    desc = _omni_desc_for(X, W_r, W_c, K, W_in, W_out)
     if ws is None:
         ws = _omni_ws(desc, MOE_OMNI_WS_FORWARD, X.device)
     Y = torch.empty_like(X)
