@@ -15,8 +15,10 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - Every call returns a moe_status; nothing throws across the ABI.  On
- *   failure moe_last_error() gives a message for the calling thread.
+ * - Every call returns a moe_status; nothing throws across the ABI (an
+ *   exception inside a call, such as a failed host allocation, returns
+ *   MOE_ERR_HOST).  On failure moe_last_error() gives a message for the
+ *   calling thread.
  * - Device entry points take device pointers owned by the caller and enqueue
  *   their kernels on `stream` (a hipStream_t passed as void*; NULL = the
  *   default stream).  They never synchronise, never copy to the host and
@@ -60,7 +62,8 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = -2,  /* shape outside the supported set */
   MOE_ERR_ALIGNMENT = -3,    /* a device pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = -4,    /* workspace missing or smaller than moe_workspace_size */
-  MOE_ERR_HIP = -5           /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_HIP = -5,          /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_HOST = -6          /* a host-side failure (an allocation on the host failed) */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;

@@ -33,6 +33,7 @@ def test_status_strings():
     lib = moe.lib()
     assert lib.moe_status_str(0) == b"MOE_OK"
     assert lib.moe_status_str(-4) == b"MOE_ERR_WORKSPACE"
+    assert lib.moe_status_str(-6) == b"MOE_ERR_HOST"
     assert lib.moe_status_str(7) == b"unknown moe_status"
 
 

@@ -27,6 +27,7 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_ALIGNMENT = -3
 MOE_ERR_WORKSPACE = -4
 MOE_ERR_HIP = -5
+MOE_ERR_HOST = -6
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_WS_PERMUTE = 0

@@ -22,6 +22,16 @@ moe_status fail(moe_status st, const std::string& msg) {
   return st;
 }
 
+// An exception that reached an entry point (a host allocation failed): it is
+// not let across the C ABI; the message is set without allocating when possible.
+moe_status caught() noexcept {
+  try {
+    g_last_error = "host-side failure (an allocation on the host failed)";
+  } catch (...) {
+  }
+  return MOE_ERR_HOST;
+}
+
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -390,12 +400,14 @@ OmniForwardWs carve_omni_forward(const moe::OmniProblem& p, unsigned char* base)
 
 extern "C" {
 
-moe_status moe_omni_validate(const moe_omni_desc* desc) {
+moe_status moe_omni_validate(const moe_omni_desc* desc) try {
   g_last_error.clear();
   return check_omni(desc);
+} catch (...) {
+  return caught();
 }
 
-moe_status moe_omni_workspace_size(const moe_omni_desc* desc, int32_t entry, size_t* bytes) {
+moe_status moe_omni_workspace_size(const moe_omni_desc* desc, int32_t entry, size_t* bytes) try {
   MOE_TRY(check_omni(desc));
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
   const moe::OmniProblem p = omni_problem(desc);
@@ -405,11 +417,13 @@ moe_status moe_omni_workspace_size(const moe_omni_desc* desc, int32_t entry, siz
     case MOE_OMNI_WS_FORWARD: *bytes = carve_omni_forward(p, nullptr).bytes; return MOE_OK;
     default: return fail(MOE_ERR_INVALID_ARG, "unknown workspace selector");
   }
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_omni_route(const moe_omni_desc* desc, const void* X, const void* W_r,
                           const void* W_c, float* ls_r, float* ls_c, int32_t* ids, float* gates,
-                          void* ws, size_t ws_bytes, void* stream) {
+                          void* ws, size_t ws_bytes, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_omni(desc));
@@ -425,11 +439,13 @@ moe_status moe_omni_route(const moe_omni_desc* desc, const void* X, const void* 
   return hip_status(moe::launch_omni_route(p, X, W_r, W_c, ls_r, ls_c, ids, gates, w,
                                            (hipStream_t)stream),
                     "atomic-expert router launch");
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_omni_permute(const moe_omni_desc* desc, const int32_t* ids, int32_t* counts,
                             int32_t* offsets, int32_t* perm_token, int32_t* inv_slot, void* ws,
-                            size_t ws_bytes, void* stream) {
+                            size_t ws_bytes, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_omni(desc));
@@ -445,11 +461,13 @@ moe_status moe_omni_permute(const moe_omni_desc* desc, const int32_t* ids, int32
   return hip_status(moe::launch_omni_permute(p, ids, counts, offsets, perm_token, inv_slot, w,
                                              (hipStream_t)stream),
                     "atomic-expert permutation launch");
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_omni_forward(const moe_omni_desc* desc, const void* X, const void* W_r,
                             const void* W_c, const void* W_in, const void* W_out, void* Y,
-                            void* ws, size_t ws_bytes, void* stream) {
+                            void* ws, size_t ws_bytes, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_omni(desc));
@@ -479,29 +497,37 @@ moe_status moe_omni_forward(const moe_omni_desc* desc, const void* X, const void
   return hip_status(moe::launch_omni_experts(p, X, W_in, W_out, w.ids, w.gates, w.offsets, w.perm,
                                              w.inv, w.a, Y, s),
                     "atomic-expert launch");
+} catch (...) {
+  return caught();
 }
 
 
-moe_status moe_validate(const moe_desc* desc) {
+moe_status moe_validate(const moe_desc* desc) try {
   g_last_error.clear();
   return check_desc(desc, kAllFlags);
+} catch (...) {
+  return caught();
 }
 
-moe_status moe_capacity(const moe_desc* desc, int64_t* C_out) {
+moe_status moe_capacity(const moe_desc* desc, int64_t* C_out) try {
   MOE_TRY(check_desc(desc, kAllFlags));
   if (!C_out) return fail(MOE_ERR_INVALID_ARG, "C_out is NULL");
   *C_out = make_problem(desc).C;
   return MOE_OK;
+} catch (...) {
+  return caught();
 }
 
-moe_status moe_max_rows(const moe_desc* desc, int64_t* rows_out) {
+moe_status moe_max_rows(const moe_desc* desc, int64_t* rows_out) try {
   MOE_TRY(check_desc(desc, kAllFlags));
   if (!rows_out) return fail(MOE_ERR_INVALID_ARG, "rows_out is NULL");
   *rows_out = make_problem(desc).rows_max;
   return MOE_OK;
+} catch (...) {
+  return caught();
 }
 
-moe_status moe_workspace_size(const moe_desc* desc, int32_t entry, size_t* bytes) {
+moe_status moe_workspace_size(const moe_desc* desc, int32_t entry, size_t* bytes) try {
   MOE_TRY(check_desc(desc, kAllFlags));
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
   const moe::Problem p = make_problem(desc);
@@ -533,13 +559,17 @@ moe_status moe_workspace_size(const moe_desc* desc, int32_t entry, size_t* bytes
     default:
       return fail(MOE_ERR_INVALID_ARG, "unknown workspace selector");
   }
+} catch (...) {
+  return caught();
 }
 
-moe_status moe_saved_layout_of(const moe_desc* desc, moe_saved_layout* out) {
+moe_status moe_saved_layout_of(const moe_desc* desc, moe_saved_layout* out) try {
   MOE_TRY(check_desc(desc, kAllFlags));
   if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
   *out = carve_saved(make_problem(desc), nullptr).layout;
   return MOE_OK;
+} catch (...) {
+  return caught();
 }
 
 const char* moe_status_str(moe_status status) {
@@ -550,6 +580,7 @@ const char* moe_status_str(moe_status status) {
     case MOE_ERR_ALIGNMENT: return "MOE_ERR_ALIGNMENT";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
     case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_HOST: return "MOE_ERR_HOST";
     default: return "unknown moe_status";
   }
 }
@@ -557,7 +588,7 @@ const char* moe_status_str(moe_status status) {
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 moe_status moe_route(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
-                     float* logits, int32_t* topk_ids, float* topk_gates, void* stream) {
+                     float* logits, int32_t* topk_ids, float* topk_gates, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, MOE_FLAG_TOPK_THRESHOLD));
@@ -568,11 +599,13 @@ moe_status moe_route(const moe_desc* desc, const void* X, const void* W_r, const
   return hip_status(moe::launch_route(p, X, W_r, bias, logits, topk_ids, topk_gates, nullptr,
                                       (hipStream_t)stream),
                     "route launch");
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_route_ws(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
                         float* logits, int32_t* topk_ids, float* topk_gates, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        size_t ws_bytes, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, MOE_FLAG_TOPK_THRESHOLD));
@@ -587,11 +620,13 @@ moe_status moe_route_ws(const moe_desc* desc, const void* X, const void* W_r, co
                                       need ? static_cast<float*>(ws) : nullptr,
                                       (hipStream_t)stream),
                     "route launch");
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_permute(const moe_desc* desc, const int32_t* topk_ids, int32_t* counts,
                        int32_t* offsets, int32_t* raw_counts, int32_t* perm_token,
-                       int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream) {
+                       int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc));
@@ -604,13 +639,15 @@ moe_status moe_permute(const moe_desc* desc, const int32_t* topk_ids, int32_t* c
     return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size(MOE_WS_PERMUTE)");
   return run_permute(p, topk_ids, counts, offsets, raw_counts, perm_token, inv_slot,
                      static_cast<unsigned char*>(ws), nullptr, (hipStream_t)stream);
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_route_permute(const moe_desc* desc, const void* X, const void* W_r,
                              const float* bias, float* logits, int32_t* topk_ids,
                              float* topk_gates, int32_t* counts, int32_t* offsets,
                              int32_t* raw_counts, int32_t* perm_token, int32_t* inv_slot,
-                             void* ws, size_t ws_bytes, void* stream) {
+                             void* ws, size_t ws_bytes, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, MOE_FLAG_TOPK_THRESHOLD));
@@ -626,13 +663,15 @@ moe_status moe_route_permute(const moe_desc* desc, const void* X, const void* W_
   return run_route_permute(p, X, W_r, bias, logits, topk_ids, topk_gates, w.route_partial,
                            w.blockcnt, counts, offsets, raw_counts ? raw_counts : w.raw,
                            perm_token, inv_slot, nullptr, (hipStream_t)stream);
+} catch (...) {
+  return caught();
 }
 
 static_assert(moe::kNoallocScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "scratch size in moe.h");
 
 moe_status moe_permute_noalloc(const moe_desc* desc, const int32_t* topk_ids, int32_t* counts,
                                int32_t* offsets, int32_t* raw_counts, int32_t* perm_token,
-                               int32_t* inv_slot, void* stream) {
+                               int32_t* inv_slot, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc));
@@ -650,11 +689,13 @@ moe_status moe_permute_noalloc(const moe_desc* desc, const int32_t* topk_ids, in
   MOE_TRY(hip_status(moe::noalloc_scratch(&scratch), "static scratch address"));
   return run_permute(p, topk_ids, counts, offsets, raw_counts, perm_token, inv_slot,
                      static_cast<unsigned char*>(scratch), nullptr, (hipStream_t)stream);
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_round_tokens(const moe_desc* desc, const int32_t* topk_ids, const float* topk_gates,
                             int32_t* counts, int32_t* offsets, int32_t* perm_token,
-                            int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream) {
+                            int32_t* inv_slot, void* ws, size_t ws_bytes, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc));
@@ -671,11 +712,13 @@ moe_status moe_round_tokens(const moe_desc* desc, const int32_t* topk_ids, const
   return hip_status(moe::launch_round(p, topk_ids, topk_gates, counts, offsets, perm_token,
                                       inv_slot, w, (hipStream_t)stream),
                     "token rounding launch");
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_grouped_gemm_up(const moe_desc* desc, const void* X, const int32_t* offsets,
                                const int32_t* perm_token, const void* W_gate, const void* W_up,
-                               void* H, void* ws, size_t ws_bytes, void* stream) {
+                               void* H, void* ws, size_t ws_bytes, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, kGemmFlags));
@@ -696,11 +739,13 @@ moe_status moe_grouped_gemm_up(const moe_desc* desc, const void* X, const int32_
   return hip_status(moe::launch_gemm_up(p, X, perm_token, table, W_gate, W_up, H, s, nullptr,
                                         offsets, stream_rows(p, desc)),
                     "grouped GEMM (up) launch");
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_grouped_gemm_down(const moe_desc* desc, const void* H, const int32_t* offsets,
                                  const void* W_down, void* O, void* ws, size_t ws_bytes,
-                                 void* stream) {
+                                 void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, kGemmFlags));
@@ -718,12 +763,14 @@ moe_status moe_grouped_gemm_down(const moe_desc* desc, const void* H, const int3
     MOE_TRY(hip_status(moe::launch_tile_table(p, offsets, table, s), "tile table launch"));
   return hip_status(moe::launch_gemm_down(p, H, table, W_down, O, s, offsets, stream_rows(p, desc)),
                     "grouped GEMM (down) launch");
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* offsets,
                            const int32_t* perm_token, const void* W_gate, const void* W_up,
                            const void* W_down, void* H, void* O, void* ws, size_t ws_bytes,
-                           void* stream) {
+                           void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, kGemmFlags));
@@ -750,10 +797,12 @@ moe_status moe_grouped_ffn(const moe_desc* desc, const void* X, const int32_t* o
                      "grouped GEMM (up) launch"));
   return hip_status(moe::launch_gemm_down(p, H, table, W_down, O, s, offsets, sr),
                     "grouped GEMM (down) launch");
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_combine(const moe_desc* desc, const void* O, const float* topk_gates,
-                       const int32_t* inv_slot, void* Y, void* stream) {
+                       const int32_t* inv_slot, void* Y, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc));
@@ -762,11 +811,13 @@ moe_status moe_combine(const moe_desc* desc, const void* O, const float* topk_ga
   const moe::Problem p = make_problem(desc);
   return hip_status(moe::launch_combine(p, O, topk_gates, inv_slot, Y, (hipStream_t)stream),
                     "combine launch");
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, const float* bias,
                        const void* W_gate, const void* W_up, const void* W_down, void* Y,
-                       void* ws, size_t ws_bytes, void* stream) {
+                       void* ws, size_t ws_bytes, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_GEMM_SKINNY | MOE_FLAG_TOKEN_ROUNDING |
@@ -808,12 +859,14 @@ moe_status moe_forward(const moe_desc* desc, const void* X, const void* W_r, con
                        "grouped GEMM (down) launch"));
   }
   return hip_status(moe::launch_combine(p, w.O, w.gates, w.inv, Y, s), "combine launch");
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_forward_train(const moe_desc* desc, const void* X, const void* W_r,
                              const float* bias, const void* W_gate, const void* W_up,
                              const void* W_down, void* Y, void* saved, size_t saved_bytes,
-                             void* ws, size_t ws_bytes, void* stream) {
+                             void* ws, size_t ws_bytes, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_TOPK_THRESHOLD));
@@ -838,12 +891,14 @@ moe_status moe_forward_train(const moe_desc* desc, const void* X, const void* W_
   MOE_TRY(hip_status(moe::launch_gemm_down(p, w.H, sv.table, W_down, w.O, s),
                      "grouped GEMM (down) launch"));
   return hip_status(moe::launch_combine(p, w.O, sv.gates, sv.inv, Y, s), "combine launch");
+} catch (...) {
+  return caught();
 }
 
 moe_status moe_backward(const moe_desc* desc, const void* X, const void* W_r, const void* W_gate,
                         const void* W_up, const void* W_down, const void* dY, const void* saved,
                         size_t saved_bytes, void* dX, float* dW_r, float* dW_gate, float* dW_up,
-                        float* dW_down, void* ws, size_t ws_bytes, void* stream) {
+                        float* dW_down, void* ws, size_t ws_bytes, void* stream) try {
   const StreamScope scope_(stream);
   g_last_error.clear();
   MOE_TRY(check_desc(desc, MOE_FLAG_GEMM_TILED | MOE_FLAG_TOPK_THRESHOLD));  // the latter: no effect here
@@ -869,6 +924,8 @@ moe_status moe_backward(const moe_desc* desc, const void* X, const void* W_r, co
                                          sv.inv, sv.perm, sv.offsets, sv.table, sv.Hpre, dX, dW_r,
                                          dW_gate, dW_up, dW_down, w, s),
                     "backward launch");
+} catch (...) {
+  return caught();
 }
 
 }  // extern "C"
